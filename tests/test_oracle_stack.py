@@ -1,0 +1,103 @@
+"""Pins for the oracle's layer stack, drivers and serialized state (CPU only)."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.state import HEADER
+import synth
+from model_inputs import TINY_DENSE, TINY_MOE, q8_layers
+
+
+def rel(a, b):
+    return float(np.max(np.abs(a - b)) / np.max(np.abs(b)))
+
+
+@pytest.mark.parametrize("base", [TINY_DENSE, TINY_MOE])
+@pytest.mark.parametrize("kv", ["f16", "q8_0"])
+def test_chunked_equals_layer_major_and_chunk_sizes_agree(base, kv):
+    w = base.with_(kv_type=kv)
+    m = oracle.OracleModel(w, q8_layers(w))
+    x = synth.prompt_inputs(w)
+    ref = m.prefill_layer_major(x)
+    for chunk in (1, 3, w.chunk, w.n_prompt):
+        got = m.prefill(x, chunk)
+        assert rel(got, ref) < 1e-12, chunk
+    assert np.all(np.isfinite(ref))
+
+
+def test_prefix_outputs_do_not_change_when_tokens_are_appended():
+    w = TINY_DENSE
+    m = oracle.OracleModel(w, q8_layers(w))
+    x = synth.prompt_inputs(w)
+    full = m.prefill_layer_major(x)
+    pre = m.prefill_layer_major(x[:11])
+    assert rel(pre, full[:11]) < 1e-12
+
+
+def test_layer_by_hand_matches_stack():
+    """One layer written out step by step from the dequantised weights."""
+    w = TINY_DENSE.with_(n_layer=1)
+    layers = q8_layers(w)
+    m = oracle.OracleModel(w, layers)
+    x = synth.prompt_inputs(w, 9).astype(np.float64)
+    out = m.prefill_layer_major(x)
+    W = oracle.dequant_layer(layers[0], m.K_of)
+    hd, Hq, Hkv = w.head_dim, w.n_head, w.n_kv_head
+    y = oracle.rmsnorm(x, W["attn_norm"], w.rms_eps)
+    q = (y @ W["wq"].T).reshape(9, Hq, hd)
+    k = (y @ W["wk"].T).reshape(9, Hkv, hd)
+    v = (y @ W["wv"].T).reshape(9, Hkv, hd)
+    pos = np.arange(9)
+    q = oracle.rope_apply(q, pos, hd, w.rope_theta)
+    k = oracle.rope_apply(k, pos, hd, w.rope_theta)
+    k = k.astype(np.float16).astype(np.float64)
+    v = v.astype(np.float16).astype(np.float64)
+    o = oracle.attention(q, k, v, pos).reshape(9, Hq * hd)
+    h = x + o @ W["wo"].T
+    y2 = oracle.rmsnorm(h, W["ffn_norm"], w.rms_eps)
+    g = y2 @ W["w_gate"].T
+    ref = h + ((g / (1 + np.exp(-g))) * (y2 @ W["w_up"].T)) @ W["w_down"].T
+    assert rel(out, ref) < 1e-5      # the float32 RoPE / cache rounding is the difference
+
+
+@pytest.mark.parametrize("kv", ["f16", "q8_0"])
+def test_state_round_trip_size_and_continuation(kv):
+    w = TINY_DENSE.with_(kv_type=kv)
+    m = oracle.OracleModel(w, q8_layers(w))
+    x = synth.prompt_inputs(w)
+    cache = m.new_cache(40)
+    m.prefill(x[:16], 7, cache=cache)
+    blob = oracle.state_bytes(cache, w.rope_theta)
+    assert len(blob) == oracle.state_size(w.n_layer, w.n_kv_head, w.head_dim, 16, kv)
+    assert blob[:4] == b"CPKV"
+    c2 = m.new_cache(40)
+    oracle.load_state(c2, blob)
+    assert oracle.state_bytes(c2, w.rope_theta) == blob
+    a = m.prefill(x[16:], 7, cache=cache)
+    b = m.prefill(x[16:], 7, cache=c2)
+    assert np.array_equal(a, b)
+
+
+def test_state_header_mutations_rejected():
+    w = TINY_DENSE
+    m = oracle.OracleModel(w, q8_layers(w))
+    cache = m.new_cache(16)
+    m.prefill(synth.prompt_inputs(w, 5), 5, cache=cache)
+    blob = bytearray(oracle.state_bytes(cache, w.rope_theta))
+    for off in (0, 4, 8, 20, 24):
+        bad = bytearray(blob)
+        bad[off] ^= 0x5A
+        with pytest.raises(ValueError):
+            oracle.parse_state(bytes(bad))
+    with pytest.raises(ValueError):
+        oracle.parse_state(bytes(blob[:-1]))
+    c3 = oracle.OracleCache(w.n_layer, 16, w.n_kv_head * 2, w.head_dim, "f16")
+    with pytest.raises(ValueError):
+        oracle.load_state(c3, bytes(blob))
+
+
+def test_state_sizes_at_workload_geometry():
+    # 16 layers x 8 kv heads x 128 dims, K and V
+    assert oracle.state_size(16, 8, 128, 17055, "f16") == 1_117_716_512
+    assert oracle.state_size(16, 8, 128, 58300, "q8_0") == 2_029_772_832
+    assert HEADER.size == 32
