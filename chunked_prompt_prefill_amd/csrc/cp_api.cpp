@@ -1,0 +1,830 @@
+// Host runtime and C ABI of the chunked prefill library.
+//
+// A context holds pointers into three caller-owned device arenas (repacked weights, KV
+// cache, workspace), the caller's stream and n_past.  prefill_chunk() validates on the
+// host, then enqueues, per layer: RMSNorm -> QKV GEMM -> RoPE + K append -> V append
+// -> attention -> O GEMM (+residual) -> RMSNorm -> SwiGLU FFN (dense, or router ->
+// permute -> grouped GEMMs -> unpermute) (+residual).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "cp_internal.h"
+
+using namespace cp;
+
+namespace {
+
+// --------------------------------------------------------------------------------------
+// Geometry
+// --------------------------------------------------------------------------------------
+struct Dims {
+  int L, d, Hq, Hkv, hd, G, F, E, k, Fe;
+  int Nqkv, Dq, Fp, Fep;
+  int n_ctx, Cm;
+  bool moe;
+  int kv_type;
+};
+
+int64_t round_up(int64_t v, int64_t g) { return (v + g - 1) / g * g; }
+
+std::string validate(const cp_config* c) {
+  if (!c) return "config is NULL";
+  if (c->n_layer < 1) return "n_layer must be >= 1";
+  if (c->d_model < 64 || c->d_model % 64) return "d_model must be a positive multiple of 64";
+  if (c->head_dim != 64 && c->head_dim != 128) return "head_dim must be 64 or 128";
+  if (c->n_kv_head < 1 || c->n_head < 1 || c->n_head % c->n_kv_head)
+    return "n_head must be a positive multiple of n_kv_head";
+  if (c->n_head / c->n_kv_head > 64) return "n_head / n_kv_head must be <= 64";
+  const bool moe = c->n_expert > 0;
+  if (!moe && c->ffn_dim < 1) return "dense FFN needs ffn_dim >= 1";
+  if (moe) {
+    if (c->ffn_dim != 0) return "routed experts need ffn_dim == 0";
+    if (c->n_expert > 256) return "n_expert must be <= 256";
+    if (c->n_expert_used < 1 || c->n_expert_used > c->n_expert || c->n_expert_used > 16)
+      return "n_expert_used must be in [1, min(n_expert, 16)]";
+    if (c->expert_ffn_dim < 1) return "expert_ffn_dim must be >= 1";
+  } else if (c->n_expert_used || c->expert_ffn_dim) {
+    return "dense FFN needs n_expert_used == expert_ffn_dim == 0";
+  }
+  if (!(c->rms_eps > 0.0f) || !std::isfinite(c->rms_eps)) return "rms_eps must be > 0";
+  if (!(c->rope_theta > 0.0f) || !std::isfinite(c->rope_theta)) return "rope_theta must be > 0";
+  if (c->kv_type != CP_KV_F16 && c->kv_type != CP_KV_Q8_0) return "kv_type must be 0 (f16) or 1 (q8_0)";
+  if (c->n_ctx_max < 1 || c->n_ctx_max > (1 << 24)) return "n_ctx_max must be in [1, 2^24]";
+  if (c->n_chunk_max < 1 || c->n_chunk_max > c->n_ctx_max) return "n_chunk_max must be in [1, n_ctx_max]";
+  if ((int64_t)c->n_chunk_max * c->n_head * c->head_dim > (1LL << 31)) return "n_chunk_max too large";
+  return "";
+}
+
+Dims dims_of(const cp_config* c) {
+  Dims D;
+  D.L = c->n_layer; D.d = c->d_model; D.Hq = c->n_head; D.Hkv = c->n_kv_head; D.hd = c->head_dim;
+  D.G = D.Hq / D.Hkv; D.F = c->ffn_dim; D.E = c->n_expert; D.k = c->n_expert_used;
+  D.Fe = c->expert_ffn_dim; D.moe = D.E > 0; D.kv_type = c->kv_type;
+  D.Nqkv = (D.Hq + 2 * D.Hkv) * D.hd; D.Dq = D.Hq * D.hd;
+  D.Fp = (int)round_up(D.F, 64); D.Fep = (int)round_up(D.Fe, 64);
+  D.n_ctx = (int)round_up(c->n_ctx_max, 64);
+  D.Cm = c->n_chunk_max;
+  return D;
+}
+
+// --------------------------------------------------------------------------------------
+// Launch policies
+// --------------------------------------------------------------------------------------
+int gemm_mt(int M) { return M <= 64 ? 64 : (M <= 128 ? 128 : 256); }
+
+int gemm_splits(int M, int N, int K) {
+  const int mt = gemm_mt(M);
+  const int64_t tiles = ceil_div(M, mt) * ceil_div(N, 256);
+  const int ks = K / 64;
+  if (tiles >= 192) return 1;
+  int s = (int)ceil_div(256, tiles);
+  s = std::min(s, std::max(1, ks / 4));
+  s = std::min(s, 16);
+  return std::max(s, 1);
+}
+
+int attn_splits(const Dims& D, int n, int start) {
+  const int64_t base = ceil_div((int64_t)n * D.G, 128) * D.Hkv;
+  const int kvt = (int)ceil_div(start + n, 64);
+  if (base >= 256) return 1;
+  int s = (int)ceil_div(512, base);
+  s = std::min(s, std::max(1, kvt / 4));
+  return std::max(1, std::min(s, 32));
+}
+
+// --------------------------------------------------------------------------------------
+// Arena layouts
+// --------------------------------------------------------------------------------------
+struct Bump {
+  size_t off = 0;
+  size_t take(size_t bytes) { size_t o = off; off += align_up(bytes); return o; }
+};
+
+struct QOff { size_t q = 0, d = 0; int N = 0, K = 0; };
+
+QOff qmat_off(Bump& b, int64_t N, int64_t K) {
+  QOff o;
+  o.N = (int)N; o.K = (int)K;
+  o.q = b.take(QMat::q_bytes(N, K));
+  o.d = b.take(QMat::d_bytes(N, K));
+  return o;
+}
+
+struct WLayout {
+  size_t attn_norm, ffn_norm, rq, rd;
+  QOff qkv, o, gu, dn;
+  std::vector<QOff> egu, edn;
+  size_t per_layer;
+};
+
+WLayout weights_layout(const Dims& D) {
+  WLayout W;
+  Bump b;
+  W.attn_norm = b.take((size_t)D.d * 4);
+  W.ffn_norm = b.take((size_t)D.d * 4);
+  W.qkv = qmat_off(b, D.Nqkv, D.d);
+  W.o = qmat_off(b, D.d, D.Dq);
+  if (!D.moe) {
+    W.gu = qmat_off(b, 2LL * D.Fp, D.d);
+    W.dn = qmat_off(b, D.d, D.Fp);
+    W.rq = W.rd = 0;
+  } else {
+    W.rq = b.take((size_t)D.E * D.d);
+    W.rd = b.take((size_t)D.E * (D.d / QK) * 2);
+    for (int e = 0; e < D.E; ++e) W.egu.push_back(qmat_off(b, 2LL * D.Fep, D.d));
+    for (int e = 0; e < D.E; ++e) W.edn.push_back(qmat_off(b, D.d, D.Fep));
+  }
+  W.per_layer = b.off;
+  return W;
+}
+
+struct WsLayout {
+  size_t cos, sin, stage;            // rope tables, then everything else (also state staging)
+  size_t xn, xn32, qkv, q, attn, h, yperm;
+  size_t logits, idx, w, rank, ccnt, offsets, perm, inv, tiles, ntiles;
+  size_t partial, partial_bytes;
+  size_t apo, apml;
+  int max_tiles;
+  size_t total;
+};
+
+size_t max_partial_bytes(const Dims& D) {
+  size_t best = 0;
+  const int Ns[4] = {D.Nqkv, D.d, D.moe ? 0 : 2 * D.Fp, D.d};
+  const int Ks[4] = {D.d, D.Dq, D.d, D.moe ? 0 : D.Fp};
+  for (int g = 0; g < 4; ++g) {
+    if (!Ns[g] || !Ks[g]) continue;
+    for (int M = 1; M <= D.Cm; ++M) {
+      const int s = gemm_splits(M, Ns[g], Ks[g]);
+      if (s > 1) best = std::max(best, (size_t)s * M * Ns[g] * 4);
+    }
+  }
+  return best;
+}
+
+size_t max_attn_partial_rows(const Dims& D) {
+  size_t best = 0;
+  for (int n = 1; n <= D.Cm; ++n) {
+    const int s = attn_splits(D, n, std::max(0, D.n_ctx - n));
+    if (s > 1) best = std::max(best, (size_t)s * D.Hkv * n * D.G);
+  }
+  return best;
+}
+
+WsLayout workspace_layout(const Dims& D) {
+  WsLayout S;
+  Bump b;
+  const size_t half = (size_t)D.hd / 2;
+  S.cos = b.take((size_t)D.n_ctx * half * 4);
+  S.sin = b.take((size_t)D.n_ctx * half * 4);
+  S.stage = b.off;
+  const size_t Cm = D.Cm;
+  S.xn = b.take(Cm * D.d * 2);
+  S.xn32 = D.moe ? b.take(Cm * D.d * 4) : 0;
+  S.qkv = b.take(Cm * D.Nqkv * 4);
+  S.q = b.take(Cm * D.Dq * 2);
+  S.attn = b.take(Cm * D.Dq * 2);
+  if (!D.moe) {
+    S.h = b.take(Cm * D.Fp * 2);
+    S.yperm = S.logits = S.idx = S.w = S.rank = S.ccnt = S.offsets = S.perm = S.inv = 0;
+    S.tiles = S.ntiles = 0;
+    S.max_tiles = 0;
+  } else {
+    const size_t slots = Cm * D.k;
+    S.h = b.take(slots * D.Fep * 2);
+    S.yperm = b.take(slots * D.d * 4);
+    S.logits = b.take(Cm * D.E * 4);
+    S.idx = b.take(slots * 4);
+    S.w = b.take(slots * 4);
+    S.rank = b.take(slots * 4);
+    S.ccnt = b.take((size_t)ceil_div(slots, kMoeChunk) * D.E * 4);
+    S.offsets = b.take((size_t)(D.E + 1) * 4);
+    S.perm = b.take(slots * 4);
+    S.inv = b.take(slots * 4);
+    S.max_tiles = (int)(ceil_div(slots, 128) + D.E);
+    S.tiles = b.take((size_t)S.max_tiles * 16);
+    S.ntiles = b.take(16);
+  }
+  S.partial_bytes = max_partial_bytes(D);
+  S.partial = S.partial_bytes ? b.take(S.partial_bytes) : 0;
+  const size_t arows = max_attn_partial_rows(D);
+  S.apo = arows ? b.take(arows * D.hd * 4) : 0;
+  S.apml = arows ? b.take(arows * 2 * 4) : 0;
+  S.total = b.off;
+  return S;
+}
+
+size_t kv_per_layer(const Dims& D) { return align_up(kv_layer_bytes(D.Hkv, D.hd, D.n_ctx, D.kv_type)); }
+
+size_t row_bytes(int hd, int kv_type) { return kv_type == CP_KV_F16 ? (size_t)hd * 2 : (size_t)(hd / QK) * 34; }
+
+size_t state_size(const Dims& D, int64_t n_tokens) {
+  return 32 + (size_t)D.L * 2 * n_tokens * D.Hkv * row_bytes(D.hd, D.kv_type);
+}
+
+struct StateHeader {
+  char magic[4];
+  uint32_t version, kv_type, n_layer, n_kv_head, head_dim, n_tokens;
+  float rope_theta;
+};
+static_assert(sizeof(StateHeader) == 32, "state header is 32 bytes");
+
+int check_state(const cp_config* c, const void* src, size_t n, std::string& err, uint32_t* n_tok) {
+  if (!src) { err = "state source is NULL"; return CP_E_INVALID; }
+  if (n < sizeof(StateHeader)) { err = "state shorter than its header"; return CP_E_STATE; }
+  StateHeader h;
+  std::memcpy(&h, src, sizeof h);
+  if (std::memcmp(h.magic, "CPKV", 4)) { err = "state magic mismatch"; return CP_E_STATE; }
+  if (h.version != 1) { err = "state version mismatch"; return CP_E_STATE; }
+  if ((int)h.kv_type != c->kv_type) { err = "state kv_type mismatch"; return CP_E_STATE; }
+  if ((int)h.n_layer != c->n_layer) { err = "state n_layer mismatch"; return CP_E_STATE; }
+  if ((int)h.n_kv_head != c->n_kv_head) { err = "state n_kv_head mismatch"; return CP_E_STATE; }
+  if ((int)h.head_dim != c->head_dim) { err = "state head_dim mismatch"; return CP_E_STATE; }
+  if (std::memcmp(&h.rope_theta, &c->rope_theta, 4)) { err = "state rope_theta mismatch"; return CP_E_STATE; }
+  if (h.n_tokens > (uint32_t)c->n_ctx_max) { err = "state longer than n_ctx_max"; return CP_E_STATE; }
+  const Dims D = dims_of(c);
+  if (n != state_size(D, h.n_tokens)) { err = "state length does not match its header"; return CP_E_STATE; }
+  if (n_tok) *n_tok = h.n_tokens;
+  return CP_OK;
+}
+
+struct LayerW {
+  float* attn_norm;
+  float* ffn_norm;
+  QMat qkv, o, gu, dn;
+  int8_t* rq;
+  uint16_t* rd;
+  int8_t* egu_q; uint32_t* egu_d; int64_t egu_qs, egu_ds;
+  int8_t* edn_q; uint32_t* edn_d; int64_t edn_qs, edn_ds;
+  KvLayer kv;
+};
+
+QMat qmat_at(uint8_t* base, const QOff& o) {
+  QMat m;
+  m.q = reinterpret_cast<int8_t*>(base + o.q);
+  m.d = reinterpret_cast<uint32_t*>(base + o.d);
+  m.N = o.N; m.K = o.K;
+  return m;
+}
+
+}  // namespace
+
+struct cp_ctx {
+  cp_config cfg;
+  Dims D;
+  WLayout WL;
+  WsLayout WS;
+  hipStream_t stream = nullptr;
+  uint8_t* warena = nullptr;
+  uint8_t* kv = nullptr;
+  uint8_t* ws = nullptr;
+  std::vector<LayerW> layers;
+  int32_t n_past = 0;
+  std::string err;
+  // timing
+  bool timing = false;
+  struct Rec { std::string cls; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  std::map<std::string, std::pair<double, int>> totals;
+
+  template <typename T> T* wsp(size_t off) { return reinterpret_cast<T*>(ws + off); }
+
+  hipEvent_t ev() {
+    if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+namespace {
+
+int fail(cp_ctx* c, int code, const std::string& msg) {
+  if (c) c->err = msg;
+  return code;
+}
+
+int hip_fail(cp_ctx* c, hipError_t e, const char* what) {
+  return fail(c, CP_E_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define CP_HIP(ctx, call, what)                          \
+  do {                                                   \
+    hipError_t _e = (call);                              \
+    if (_e != hipSuccess) return hip_fail(ctx, _e, what);\
+  } while (0)
+
+// Runs `launch` bracketed by timing events when timing is on for this context.
+template <typename F>
+hipError_t timed(cp_ctx* c, const char* cls, F&& launch) {
+  if (!c->timing) return launch();
+  hipEvent_t a = c->ev(), b = c->ev();
+  if (!a || !b) return launch();
+  hipEventRecord(a, c->stream);
+  hipError_t e = launch();
+  hipEventRecord(b, c->stream);
+  c->pending.push_back({cls, a, b});
+  return e;
+}
+
+hipError_t gemm(cp_ctx* c, const char* cls, const __bf16* A, int lda, int M, const QMat& W,
+                int mode, void* out, int ldo) {
+  GemmArgs g;
+  g.A = A; g.lda = lda; g.M = M; g.N = W.N; g.K = W.K;
+  g.wq = W.q; g.wd = W.d; g.mode = mode; g.out = out; g.ldo = ldo;
+  g.splits = gemm_splits(M, W.N, W.K);
+  g.partial = c->wsp<float>(c->WS.partial);
+  const int mt = gemm_mt(M);
+  return timed(c, cls, [&] { return launch_gemm(g, 0, mt, c->stream); });
+}
+
+int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int start) {
+  const Dims& D = c->D;
+  const LayerW& L = c->layers[li];
+  hipStream_t s = c->stream;
+  __bf16* xn = c->wsp<__bf16>(c->WS.xn);
+  float* qkv = c->wsp<float>(c->WS.qkv);
+  _Float16* q = c->wsp<_Float16>(c->WS.q);
+  __bf16* attn = c->wsp<__bf16>(c->WS.attn);
+  const float* cos_t = c->wsp<float>(c->WS.cos);
+  const float* sin_t = c->wsp<float>(c->WS.sin);
+
+  CP_HIP(c, timed(c, "rmsnorm", [&] { return launch_rmsnorm(x_res_in, L.attn_norm, n, D.d, c->cfg.rms_eps, xn, nullptr, s); }), "rmsnorm");
+  CP_HIP(c, gemm(c, "gemm_qkv", xn, D.d, n, L.qkv, GM_F32, qkv, D.Nqkv), "gemm_qkv");
+  CP_HIP(c, timed(c, "rope_kv_append", [&] {
+    hipError_t e = launch_rope_qk(qkv, cos_t, sin_t, n, start, D.Hq, D.Hkv, D.hd, D.kv_type, D.n_ctx, q, L.kv, s);
+    if (e != hipSuccess) return e;
+    return launch_v_append(qkv, n, start, D.Hq, D.Hkv, D.hd, D.kv_type, D.n_ctx, L.kv, s);
+  }), "rope_kv_append");
+  AttnArgs aa;
+  aa.q = q; aa.kv = L.kv; aa.n = n; aa.start = start; aa.n_head = D.Hq; aa.n_kv_head = D.Hkv;
+  aa.head_dim = D.hd; aa.kv_type = D.kv_type; aa.n_ctx = D.n_ctx; aa.out = attn;
+  aa.splits = attn_splits(D, n, start);
+  aa.part_o = c->wsp<float>(c->WS.apo);
+  aa.part_ml = c->wsp<float>(c->WS.apml);
+  CP_HIP(c, timed(c, "attention", [&] { return launch_attention(aa, s); }), "attention");
+  if (x != x_res_in)
+    CP_HIP(c, hipMemcpyAsync(x, x_res_in, (size_t)n * D.d * 4, hipMemcpyDeviceToDevice, s), "residual copy");
+  CP_HIP(c, gemm(c, "gemm_o", attn, D.Dq, n, L.o, GM_F32_ADD, x, D.d), "gemm_o");
+
+  if (!D.moe) {
+    CP_HIP(c, timed(c, "rmsnorm", [&] { return launch_rmsnorm(x, L.ffn_norm, n, D.d, c->cfg.rms_eps, xn, nullptr, s); }), "rmsnorm");
+    __bf16* hbuf = c->wsp<__bf16>(c->WS.h);
+    CP_HIP(c, gemm(c, "gemm_gate_up", xn, D.d, n, L.gu, GM_SWIGLU, hbuf, D.Fp), "gemm_gate_up");
+    CP_HIP(c, gemm(c, "gemm_down", hbuf, D.Fp, n, L.dn, GM_F32_ADD, x, D.d), "gemm_down");
+    return CP_OK;
+  }
+  float* xn32 = c->wsp<float>(c->WS.xn32);
+  CP_HIP(c, timed(c, "rmsnorm", [&] { return launch_rmsnorm(x, L.ffn_norm, n, D.d, c->cfg.rms_eps, xn, xn32, s); }), "rmsnorm");
+  MoeBuffers mb;
+  mb.logits = c->wsp<float>(c->WS.logits); mb.idx = c->wsp<int32_t>(c->WS.idx);
+  mb.w = c->wsp<float>(c->WS.w); mb.rank = c->wsp<int32_t>(c->WS.rank);
+  mb.chunk_cnt = c->wsp<int32_t>(c->WS.ccnt); mb.offsets = c->wsp<int32_t>(c->WS.offsets);
+  mb.perm = c->wsp<int32_t>(c->WS.perm); mb.inv = c->wsp<int32_t>(c->WS.inv);
+  mb.tiles = c->wsp<int32_t>(c->WS.tiles); mb.n_tiles = c->wsp<int32_t>(c->WS.ntiles);
+  CP_HIP(c, timed(c, "moe_route", [&] { return launch_router(xn32, L.rq, L.rd, n, D.d, D.E, D.k, mb.logits, mb.idx, mb.w, s); }), "moe_route");
+  const int mt = 128;
+  const int max_tiles = (int)(ceil_div((int64_t)n * D.k, mt) + D.E);
+  CP_HIP(c, timed(c, "moe_permute", [&] { return launch_moe_permute(mb, n, D.E, D.k, mt, max_tiles, s); }), "moe_permute");
+  __bf16* hperm = c->wsp<__bf16>(c->WS.h);
+  float* yperm = c->wsp<float>(c->WS.yperm);
+  GemmArgs g;
+  g.A = xn; g.lda = D.d; g.a_rows = mb.perm; g.a_row_div = D.k;
+  g.wq = L.egu_q; g.wd = L.egu_d; g.wq_estride = L.egu_qs; g.wd_estride = L.egu_ds;
+  g.M = n * D.k; g.N = 2 * D.Fep; g.K = D.d; g.tiles = mb.tiles; g.n_tiles = mb.n_tiles;
+  g.mode = GM_SWIGLU; g.out = hperm; g.ldo = D.Fep; g.splits = 1;
+  CP_HIP(c, timed(c, "moe_gemm_gate_up", [&] { return launch_gemm(g, max_tiles, mt, s); }), "moe_gemm_gate_up");
+  GemmArgs g2 = g;
+  g2.A = hperm; g2.lda = D.Fep; g2.a_rows = nullptr; g2.a_row_div = 1;
+  g2.wq = L.edn_q; g2.wd = L.edn_d; g2.wq_estride = L.edn_qs; g2.wd_estride = L.edn_ds;
+  g2.N = D.d; g2.K = D.Fep; g2.mode = GM_F32; g2.out = yperm; g2.ldo = D.d;
+  CP_HIP(c, timed(c, "moe_gemm_down", [&] { return launch_gemm(g2, max_tiles, mt, s); }), "moe_gemm_down");
+  CP_HIP(c, timed(c, "moe_unpermute", [&] { return launch_moe_unpermute(yperm, mb, n, D.d, D.k, x, x, s); }), "moe_unpermute");
+  return CP_OK;
+}
+
+bool aligned(const void* p) { return ((uintptr_t)p % kAlign) == 0; }
+
+}  // namespace
+
+// ======================================================================================
+// C ABI
+// ======================================================================================
+extern "C" {
+
+int cp_validate_config(const cp_config* cfg) { return validate(cfg).empty() ? CP_OK : CP_E_INVALID; }
+
+const char* cp_config_error(const cp_config* cfg) {
+  static thread_local std::string msg;
+  msg = validate(cfg);
+  return msg.c_str();
+}
+
+size_t cp_weights_arena_bytes(const cp_config* cfg) {
+  if (!validate(cfg).empty()) return 0;
+  const Dims D = dims_of(cfg);
+  return weights_layout(D).per_layer * D.L;
+}
+
+size_t cp_kv_bytes(const cp_config* cfg) {
+  if (!validate(cfg).empty()) return 0;
+  const Dims D = dims_of(cfg);
+  return kv_per_layer(D) * D.L;
+}
+
+size_t cp_workspace_bytes(const cp_config* cfg) {
+  if (!validate(cfg).empty()) return 0;
+  return workspace_layout(dims_of(cfg)).total;
+}
+
+size_t cp_state_bytes(const cp_config* cfg, int32_t n_tokens) {
+  if (!validate(cfg).empty() || n_tokens < 0) return 0;
+  return state_size(dims_of(cfg), n_tokens);
+}
+
+int cp_state_check(const cp_config* cfg, const void* src, size_t n_bytes) {
+  if (!validate(cfg).empty()) return CP_E_INVALID;
+  std::string err;
+  return check_state(cfg, src, n_bytes, err, nullptr);
+}
+
+int prefill_init(const cp_config* cfg, const cp_layer_weights* layers, void* weights_arena,
+                 void* kv_buf, void* workspace, void* hip_stream, cp_ctx** out) {
+  if (!out) return CP_E_INVALID;
+  *out = nullptr;
+  if (!validate(cfg).empty()) return CP_E_INVALID;
+  if (!layers || !weights_arena || !kv_buf || !workspace) return CP_E_INVALID;
+  if (!aligned(weights_arena) || !aligned(kv_buf) || !aligned(workspace)) return CP_E_ARENA;
+  cp_ctx* c = new cp_ctx();
+  c->cfg = *cfg;
+  c->D = dims_of(cfg);
+  c->WL = weights_layout(c->D);
+  c->WS = workspace_layout(c->D);
+  c->stream = (hipStream_t)hip_stream;
+  c->warena = (uint8_t*)weights_arena;
+  c->kv = (uint8_t*)kv_buf;
+  c->ws = (uint8_t*)workspace;
+  const Dims& D = c->D;
+  const WLayout& W = c->WL;
+  hipStream_t s = c->stream;
+  auto bail = [&](int code) { delete c; return code; };
+  for (int l = 0; l < D.L; ++l) {
+    const cp_layer_weights& src = layers[l];
+    if (!src.wq || !src.wk || !src.wv || !src.wo || !src.attn_norm || !src.ffn_norm || !src.w_gate ||
+        !src.w_up || !src.w_down || (D.moe && !src.w_router))
+      return bail(CP_E_INVALID);
+  }
+  for (int l = 0; l < D.L; ++l) {
+    const cp_layer_weights& src = layers[l];
+    uint8_t* base = c->warena + W.per_layer * l;
+    LayerW L{};
+    L.attn_norm = reinterpret_cast<float*>(base + W.attn_norm);
+    L.ffn_norm = reinterpret_cast<float*>(base + W.ffn_norm);
+    hipError_t e = hipMemcpyAsync(L.attn_norm, src.attn_norm, (size_t)D.d * 4, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(L.ffn_norm, src.ffn_norm, (size_t)D.d * 4, hipMemcpyDeviceToDevice, s);
+    L.qkv = qmat_at(base, W.qkv);
+    L.o = qmat_at(base, W.o);
+    const int64_t nq = (int64_t)D.Hq * D.hd, nk = (int64_t)D.Hkv * D.hd;
+    if (e == hipSuccess) e = launch_repack_q8_0(src.wq, nullptr, nq, D.d, 0, nq, 0, L.qkv, s);
+    if (e == hipSuccess) e = launch_repack_q8_0(src.wk, nullptr, nk, D.d, nq, nk, 0, L.qkv, s);
+    if (e == hipSuccess) e = launch_repack_q8_0(src.wv, nullptr, nk, D.d, nq + nk, nk, 0, L.qkv, s);
+    if (e == hipSuccess) e = launch_repack_q8_0(src.wo, nullptr, D.d, D.Dq, 0, D.d, 0, L.o, s);
+    if (!D.moe) {
+      L.gu = qmat_at(base, W.gu);
+      L.dn = qmat_at(base, W.dn);
+      if (e == hipSuccess)
+        e = launch_repack_q8_0(src.w_gate, src.w_up, D.F, D.d, 0, 2LL * D.Fp, 1, L.gu, s);
+      if (e == hipSuccess) e = launch_repack_q8_0(src.w_down, nullptr, D.d, D.F, 0, D.d, 0, L.dn, s);
+    } else {
+      L.rq = reinterpret_cast<int8_t*>(base + W.rq);
+      L.rd = reinterpret_cast<uint16_t*>(base + W.rd);
+      if (e == hipSuccess) e = launch_unpack_router(src.w_router, D.E, D.d, L.rq, L.rd, s);
+      const QMat g0 = qmat_at(base, W.egu[0]), d0 = qmat_at(base, W.edn[0]);
+      L.egu_q = g0.q; L.egu_d = g0.d; L.edn_q = d0.q; L.edn_d = d0.d;
+      L.egu_qs = D.E > 1 ? (int64_t)(W.egu[1].q - W.egu[0].q) : 0;
+      L.egu_ds = D.E > 1 ? (int64_t)(W.egu[1].d - W.egu[0].d) / 4 : 0;
+      L.edn_qs = D.E > 1 ? (int64_t)(W.edn[1].q - W.edn[0].q) : 0;
+      L.edn_ds = D.E > 1 ? (int64_t)(W.edn[1].d - W.edn[0].d) / 4 : 0;
+      const size_t gate_bytes = (size_t)D.Fe * ((D.d + QK - 1) / QK) * 34;
+      const size_t down_bytes = (size_t)D.d * ((D.Fe + QK - 1) / QK) * 34;
+      for (int x = 0; x < D.E && e == hipSuccess; ++x) {
+        const uint8_t* gsrc = (const uint8_t*)src.w_gate + gate_bytes * x;
+        const uint8_t* usrc = (const uint8_t*)src.w_up + gate_bytes * x;
+        e = launch_repack_q8_0(gsrc, usrc, D.Fe, D.d, 0, 2LL * D.Fep, 1, qmat_at(base, W.egu[x]), s);
+        if (e == hipSuccess)
+          e = launch_repack_q8_0((const uint8_t*)src.w_down + down_bytes * x, nullptr, D.d, D.Fe, 0, D.d, 0,
+                                 qmat_at(base, W.edn[x]), s);
+      }
+    }
+    L.kv = kv_layer_at(c->kv + kv_per_layer(D) * l, D.Hkv, D.hd, D.n_ctx, D.kv_type);
+    if (e != hipSuccess) { int r = hip_fail(c, e, "weight repack"); delete c; return r; }
+    c->layers.push_back(L);
+  }
+  // RoPE table: omega_i = theta^(-2i/hd), angle = p * omega_i in float64, cos/sin rounded
+  // to float32.
+  const int half = D.hd / 2;
+  std::vector<float> ct((size_t)D.n_ctx * half), st((size_t)D.n_ctx * half);
+  const double theta = (double)cfg->rope_theta;
+  for (int i = 0; i < half; ++i) {
+    const double w = std::pow(theta, -2.0 * i / D.hd);
+    for (int p = 0; p < D.n_ctx; ++p) {
+      const double a = (double)p * w;
+      ct[(size_t)p * half + i] = (float)std::cos(a);
+      st[(size_t)p * half + i] = (float)std::sin(a);
+    }
+  }
+  hipError_t e = hipMemcpyAsync(c->ws + c->WS.cos, ct.data(), ct.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(c->ws + c->WS.sin, st.data(), st.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) { int r = hip_fail(c, e, "init"); delete c; return r; }
+  *out = c;
+  return CP_OK;
+}
+
+int prefill_chunk(cp_ctx* c, const float* x_in, float* x_out, int32_t n) {
+  if (!c) return CP_E_INVALID;
+  if (!x_in || !x_out) return fail(c, CP_E_INVALID, "x_in / x_out is NULL");
+  if (n < 1 || n > c->cfg.n_chunk_max) return fail(c, CP_E_CAPACITY, "n_tokens outside [1, n_chunk_max]");
+  if ((int64_t)c->n_past + n > c->cfg.n_ctx_max) return fail(c, CP_E_CAPACITY, "n_past + n_tokens > n_ctx_max");
+  const int start = c->n_past;
+  for (int l = 0; l < c->D.L; ++l) {
+    const int r = run_layer(c, l, l == 0 ? x_in : x_out, x_out, n, start);
+    if (r != CP_OK) return r;
+  }
+  c->n_past = start + n;
+  return CP_OK;
+}
+
+int prefill_chunk_trace(cp_ctx* c, const float* x_in, float* x_out, int32_t n, float* layer_out,
+                        int64_t layer_stride, int32_t* route_idx, int64_t route_stride) {
+  if (!c) return CP_E_INVALID;
+  if (!x_in || !x_out) return fail(c, CP_E_INVALID, "x_in / x_out is NULL");
+  if (n < 1 || n > c->cfg.n_chunk_max) return fail(c, CP_E_CAPACITY, "n_tokens outside [1, n_chunk_max]");
+  if ((int64_t)c->n_past + n > c->cfg.n_ctx_max) return fail(c, CP_E_CAPACITY, "n_past + n_tokens > n_ctx_max");
+  if (layer_out && layer_stride < (int64_t)n * c->D.d) return fail(c, CP_E_INVALID, "layer_stride too small");
+  if (route_idx && (!c->D.moe || route_stride < (int64_t)n * c->D.k))
+    return fail(c, CP_E_INVALID, "route_idx needs routed experts and route_stride >= n * n_expert_used");
+  const int start = c->n_past;
+  for (int l = 0; l < c->D.L; ++l) {
+    const int r = run_layer(c, l, l == 0 ? x_in : x_out, x_out, n, start);
+    if (r != CP_OK) return r;
+    if (layer_out)
+      CP_HIP(c, hipMemcpyAsync(layer_out + layer_stride * l, x_out, (size_t)n * c->D.d * 4,
+                               hipMemcpyDeviceToDevice, c->stream), "trace copy");
+    if (route_idx)
+      CP_HIP(c, hipMemcpyAsync(route_idx + route_stride * l, c->wsp<int32_t>(c->WS.idx),
+                               (size_t)n * c->D.k * 4, hipMemcpyDeviceToDevice, c->stream), "trace copy");
+  }
+  c->n_past = start + n;
+  return CP_OK;
+}
+
+int prefill_chunk_timed(cp_ctx* c, const float* x_in, float* x_out, int32_t n, float* layer_ms) {
+  if (!c) return CP_E_INVALID;
+  if (!layer_ms) return fail(c, CP_E_INVALID, "layer_ms is NULL");
+  if (!x_in || !x_out) return fail(c, CP_E_INVALID, "x_in / x_out is NULL");
+  if (n < 1 || n > c->cfg.n_chunk_max) return fail(c, CP_E_CAPACITY, "n_tokens outside [1, n_chunk_max]");
+  if ((int64_t)c->n_past + n > c->cfg.n_ctx_max) return fail(c, CP_E_CAPACITY, "n_past + n_tokens > n_ctx_max");
+  const int L = c->D.L;
+  std::vector<hipEvent_t> ev(L + 1, nullptr);
+  for (auto& e : ev) CP_HIP(c, hipEventCreate(&e), "event create");
+  const int start = c->n_past;
+  int rc = CP_OK;
+  if (hipEventRecord(ev[0], c->stream) != hipSuccess) rc = fail(c, CP_E_DEVICE, "event record");
+  for (int l = 0; l < L && rc == CP_OK; ++l) {
+    rc = run_layer(c, l, l == 0 ? x_in : x_out, x_out, n, start);
+    if (rc == CP_OK && hipEventRecord(ev[l + 1], c->stream) != hipSuccess) rc = fail(c, CP_E_DEVICE, "event record");
+  }
+  if (rc == CP_OK) {
+    hipError_t e = hipEventSynchronize(ev[L]);
+    if (e != hipSuccess) rc = hip_fail(c, e, "event sync");
+    for (int l = 0; l < L && rc == CP_OK; ++l) hipEventElapsedTime(&layer_ms[l], ev[l], ev[l + 1]);
+  }
+  for (auto& e : ev) hipEventDestroy(e);
+  if (rc == CP_OK) c->n_past = start + n;
+  return rc;
+}
+
+int kv_cache_get_state(cp_ctx* c, void* dst, size_t cap, size_t* n_bytes) {
+  if (!c || !n_bytes) return CP_E_INVALID;
+  const Dims& D = c->D;
+  const size_t need = state_size(D, c->n_past);
+  *n_bytes = need;
+  if (!dst) return CP_OK;
+  if (cap < need) return fail(c, CP_E_ARENA, "destination smaller than the state");
+  CP_HIP(c, hipStreamSynchronize(c->stream), "stream sync");
+  StateHeader h;
+  std::memcpy(h.magic, "CPKV", 4);
+  h.version = 1; h.kv_type = (uint32_t)D.kv_type; h.n_layer = (uint32_t)D.L;
+  h.n_kv_head = (uint32_t)D.Hkv; h.head_dim = (uint32_t)D.hd; h.n_tokens = (uint32_t)c->n_past;
+  h.rope_theta = c->cfg.rope_theta;
+  std::memcpy(dst, &h, sizeof h);
+  uint8_t* o = (uint8_t*)dst + sizeof h;
+  const size_t rb = row_bytes(D.hd, D.kv_type) * D.Hkv;
+  uint8_t* stage = c->ws + c->WS.stage;
+  const size_t stage_cap = c->WS.total - c->WS.stage;
+  const int64_t slice = std::max<int64_t>(1, (int64_t)(stage_cap / rb));
+  for (int l = 0; l < D.L; ++l)
+    for (int which = 0; which < 2; ++which)
+      for (int64_t t0 = 0; t0 < c->n_past; t0 += slice) {
+        const int nt = (int)std::min<int64_t>(slice, c->n_past - t0);
+        CP_HIP(c, launch_kv_pack(c->layers[l].kv, (int)t0, nt, D.Hkv, D.hd, D.kv_type, D.n_ctx, which, stage, c->stream), "state pack");
+        CP_HIP(c, hipMemcpyAsync(o, stage, rb * nt, hipMemcpyDeviceToHost, c->stream), "state copy");
+        CP_HIP(c, hipStreamSynchronize(c->stream), "stream sync");
+        o += rb * nt;
+      }
+  return CP_OK;
+}
+
+int kv_cache_set_state(cp_ctx* c, const void* src, size_t n_bytes) {
+  if (!c) return CP_E_INVALID;
+  uint32_t nt_total = 0;
+  const int r = check_state(&c->cfg, src, n_bytes, c->err, &nt_total);
+  if (r != CP_OK) return r;
+  const Dims& D = c->D;
+  CP_HIP(c, hipStreamSynchronize(c->stream), "stream sync");
+  const uint8_t* p = (const uint8_t*)src + sizeof(StateHeader);
+  const size_t rb = row_bytes(D.hd, D.kv_type) * D.Hkv;
+  uint8_t* stage = c->ws + c->WS.stage;
+  const size_t stage_cap = c->WS.total - c->WS.stage;
+  const int64_t slice = std::max<int64_t>(1, (int64_t)(stage_cap / rb));
+  for (int l = 0; l < D.L; ++l)
+    for (int which = 0; which < 2; ++which)
+      for (int64_t t0 = 0; t0 < (int64_t)nt_total; t0 += slice) {
+        const int nt = (int)std::min<int64_t>(slice, nt_total - t0);
+        CP_HIP(c, hipMemcpyAsync(stage, p, rb * nt, hipMemcpyHostToDevice, c->stream), "state copy");
+        CP_HIP(c, launch_kv_unpack(c->layers[l].kv, (int)t0, nt, D.Hkv, D.hd, D.kv_type, D.n_ctx, which, stage, c->stream), "state unpack");
+        CP_HIP(c, hipStreamSynchronize(c->stream), "stream sync");
+        p += rb * nt;
+      }
+  c->n_past = (int32_t)nt_total;
+  return CP_OK;
+}
+
+int kv_cache_truncate(cp_ctx* c, int32_t n_keep) {
+  if (!c) return CP_E_INVALID;
+  if (n_keep < 0 || n_keep > c->n_past) return fail(c, CP_E_INVALID, "n_keep outside [0, n_past]");
+  c->n_past = n_keep;
+  return CP_OK;
+}
+
+int32_t prefill_n_past(const cp_ctx* c) { return c ? c->n_past : -1; }
+
+const char* prefill_last_error(const cp_ctx* c) { return c ? c->err.c_str() : "context is NULL"; }
+
+void prefill_free(cp_ctx* c) {
+  if (!c) return;
+  hipStreamSynchronize(c->stream);
+  for (auto& r : c->pending) { hipEventDestroy(r.a); hipEventDestroy(r.b); }
+  for (auto e : c->pool) hipEventDestroy(e);
+  delete c;
+}
+
+int cp_kernel_timing(cp_ctx* c, int enable) {
+  if (!c) return CP_E_INVALID;
+  CP_HIP(c, hipStreamSynchronize(c->stream), "stream sync");
+  for (auto& r : c->pending) { c->pool.push_back(r.a); c->pool.push_back(r.b); }
+  c->pending.clear();
+  c->totals.clear();
+  c->timing = enable != 0;
+  return CP_OK;
+}
+
+int cp_kernel_times(cp_ctx* c, const char* cls, float* total_ms, int32_t* launches) {
+  if (!c || !cls || !total_ms || !launches) return CP_E_INVALID;
+  CP_HIP(c, hipStreamSynchronize(c->stream), "stream sync");
+  for (auto& r : c->pending) {
+    float ms = 0.0f;
+    hipEventElapsedTime(&ms, r.a, r.b);
+    auto& t = c->totals[r.cls];
+    t.first += ms;
+    t.second += 1;
+    c->pool.push_back(r.a);
+    c->pool.push_back(r.b);
+  }
+  c->pending.clear();
+  auto it = c->totals.find(cls);
+  *total_ms = it == c->totals.end() ? 0.0f : (float)it->second.first;
+  *launches = it == c->totals.end() ? 0 : it->second.second;
+  return CP_OK;
+}
+
+int cp_quantize_q8_0(const float* x, int64_t rows, int32_t k, int64_t ldx, void* out, void* stream) {
+  if (!x || !out || rows < 0 || k < 1 || ldx < k) return CP_E_INVALID;
+  return launch_quantize_q8_0(x, rows, k, ldx, out, (hipStream_t)stream) == hipSuccess ? CP_OK : CP_E_DEVICE;
+}
+
+// ---------------------------------------------------------------------------------- tests
+size_t cp_test_kv_layer_bytes(int32_t n_kv_head, int32_t head_dim, int32_t n_ctx, int32_t kv_type) {
+  return kv_layer_bytes(n_kv_head, head_dim, (int32_t)round_up(n_ctx, 64), kv_type);
+}
+
+int cp_test_rope_kv_append(const float* qkv, const float* cos_t, const float* sin_t, int32_t n,
+                           int32_t start, int32_t n_head, int32_t n_kv_head, int32_t head_dim,
+                           int32_t kv_type, int32_t n_ctx, void* q_out, void* kv, void* stream) {
+  if (!qkv || !cos_t || !sin_t || !q_out || !kv || n < 1 || start < 0 || start + n > n_ctx) return CP_E_INVALID;
+  if ((head_dim != 64 && head_dim != 128) || n_kv_head < 1 || n_head % n_kv_head) return CP_E_INVALID;
+  const int nc = (int)round_up(n_ctx, 64);
+  KvLayer L = kv_layer_at(kv, n_kv_head, head_dim, nc, kv_type);
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_rope_qk(qkv, cos_t, sin_t, n, start, n_head, n_kv_head, head_dim, kv_type, nc, (_Float16*)q_out, L, s) != hipSuccess)
+    return CP_E_DEVICE;
+  return launch_v_append(qkv, n, start, n_head, n_kv_head, head_dim, kv_type, nc, L, s) == hipSuccess ? CP_OK : CP_E_DEVICE;
+}
+
+int cp_test_kv_rows(const void* kv, int32_t n_tokens, int32_t n_kv_head, int32_t head_dim,
+                    int32_t kv_type, int32_t n_ctx, void* out, void* stream) {
+  if (!kv || !out || n_tokens < 1 || n_tokens > n_ctx) return CP_E_INVALID;
+  const int nc = (int)round_up(n_ctx, 64);
+  KvLayer L = kv_layer_at(const_cast<void*>(kv), n_kv_head, head_dim, nc, kv_type);
+  const size_t rb = row_bytes(head_dim, kv_type) * n_kv_head;
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_kv_pack(L, 0, n_tokens, n_kv_head, head_dim, kv_type, nc, 0, (uint8_t*)out, s) != hipSuccess) return CP_E_DEVICE;
+  return launch_kv_pack(L, 0, n_tokens, n_kv_head, head_dim, kv_type, nc, 1, (uint8_t*)out + rb * n_tokens, s) == hipSuccess
+             ? CP_OK : CP_E_DEVICE;
+}
+
+size_t cp_test_router_scratch_bytes(int32_t n_expert, int32_t d) {
+  return align_up((size_t)n_expert * d) + align_up((size_t)n_expert * (d / QK) * 2);
+}
+
+int cp_test_router(const float* y, const void* w_router, int32_t n, int32_t d, int32_t E, int32_t k,
+                   float* logits, int32_t* idx, float* weight, void* scratch, void* stream) {
+  if (!y || !w_router || !logits || !idx || !weight || !scratch || n < 1 || d < 32 || d % 32 ||
+      E < 1 || E > 256 || k < 1 || k > E || k > 16)
+    return CP_E_INVALID;
+  int8_t* q = (int8_t*)scratch;
+  uint16_t* dd = (uint16_t*)((uint8_t*)scratch + align_up((size_t)E * d));
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_unpack_router(w_router, E, d, q, dd, s) != hipSuccess) return CP_E_DEVICE;
+  return launch_router(y, q, dd, n, d, E, k, logits, idx, weight, s) == hipSuccess ? CP_OK : CP_E_DEVICE;
+}
+
+size_t cp_test_gemm_scratch_bytes(int32_t M, int32_t N, int32_t K, int32_t splits) {
+  if (M < 1 || N < 32 || N % 32 || K < 64 || K % 64) return 0;
+  const int s = splits > 0 ? splits : gemm_splits(M, N, K);
+  return align_up(QMat::q_bytes(N, K)) + align_up(QMat::d_bytes(N, K)) + align_up((size_t)s * M * N * 4);
+}
+
+int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
+                 int32_t splits, void* out, void* scratch, void* stream) {
+  if (!A || !W || !out || !scratch || M < 1 || N < 32 || N % 32 || K < 64 || K % 64 || mode < 0 || mode > 2)
+    return CP_E_INVALID;
+  if (mode == GM_SWIGLU && N % 64) return CP_E_INVALID;
+  hipStream_t s = (hipStream_t)stream;
+  QMat q;
+  q.q = (int8_t*)scratch;
+  q.d = (uint32_t*)((uint8_t*)scratch + align_up(QMat::q_bytes(N, K)));
+  q.N = N; q.K = K;
+  float* partial = (float*)((uint8_t*)q.d + align_up(QMat::d_bytes(N, K)));
+  hipError_t e;
+  if (mode == GM_SWIGLU) {
+    const int F = N / 2;
+    const uint8_t* up = (const uint8_t*)W + (size_t)F * (K / QK) * 34;
+    e = launch_repack_q8_0(W, up, F, K, 0, N, 1, q, s);
+  } else {
+    e = launch_repack_q8_0(W, nullptr, N, K, 0, N, 0, q, s);
+  }
+  if (e != hipSuccess) return CP_E_DEVICE;
+  GemmArgs g;
+  g.A = (const __bf16*)A; g.lda = K; g.M = M; g.N = N; g.K = K; g.wq = q.q; g.wd = q.d;
+  g.mode = mode; g.out = out; g.ldo = mode == GM_SWIGLU ? N / 2 : N;
+  g.splits = splits > 0 ? splits : gemm_splits(M, N, K);
+  g.splits = std::min(g.splits, K / 64);
+  g.partial = partial;
+  return launch_gemm(g, 0, gemm_mt(M), s) == hipSuccess ? CP_OK : CP_E_DEVICE;
+}
+
+size_t cp_test_attention_scratch_bytes(int32_t n, int32_t n_head, int32_t head_dim, int32_t kv_splits) {
+  const int s = kv_splits > 0 ? kv_splits : 32;
+  return align_up((size_t)s * n * n_head * head_dim * 4) + align_up((size_t)s * n * n_head * 2 * 4);
+}
+
+int cp_test_attention(const void* q, const void* kv, int32_t n, int32_t start, int32_t n_head,
+                      int32_t n_kv_head, int32_t head_dim, int32_t kv_type, int32_t n_ctx,
+                      int32_t kv_splits, void* out, void* scratch, void* stream) {
+  if (!q || !kv || !out || !scratch || n < 1 || start < 0 || start + n > n_ctx) return CP_E_INVALID;
+  if ((head_dim != 64 && head_dim != 128) || n_kv_head < 1 || n_head % n_kv_head || kv_splits < 0 || kv_splits > 32)
+    return CP_E_INVALID;
+  Dims D{};
+  D.Hq = n_head; D.Hkv = n_kv_head; D.hd = head_dim; D.G = n_head / n_kv_head;
+  const int nc = (int)round_up(n_ctx, 64);
+  AttnArgs a;
+  a.q = (const _Float16*)q;
+  a.kv = kv_layer_at(const_cast<void*>(kv), n_kv_head, head_dim, nc, kv_type);
+  a.n = n; a.start = start; a.n_head = n_head; a.n_kv_head = n_kv_head; a.head_dim = head_dim;
+  a.kv_type = kv_type; a.n_ctx = nc; a.out = (__bf16*)out;
+  a.splits = kv_splits > 0 ? kv_splits : attn_splits(D, n, start);
+  a.part_o = (float*)scratch;
+  a.part_ml = (float*)((uint8_t*)scratch + align_up((size_t)a.splits * n * n_head * head_dim * 4));
+  return launch_attention(a, (hipStream_t)stream) == hipSuccess ? CP_OK : CP_E_DEVICE;
+}
+
+}  // extern "C"

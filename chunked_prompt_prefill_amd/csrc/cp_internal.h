@@ -1,0 +1,136 @@
+// Internal declarations shared by the host runtime and the kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "chunk_prefill.h"
+
+namespace cp {
+
+constexpr int QK = 32;              // q8_0 block length
+constexpr int kAlign = 256;         // every arena sub-buffer starts on 256 bytes
+
+__host__ __device__ inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// --------------------------------------------------------------------------------------
+// Repacked q8_0 matrix [N][K] (N % 32 == 0, K % 64 == 0).
+//   q: int8, for every 32-row group n32 and 32-column block kb, 1 KiB laid out in MFMA
+//      lane order: lane l (row n32*32 + l%32) holds bytes 16*(l/32) .. +15 of that
+//      row's block -> offset ((n32*KB + kb)*64 + l)*16.
+//   d: fp16 scales, two per u32: for 32-row group n32 and block pair kp (blocks 2kp and
+//      2kp+1) -> u32 index (n32*KP + kp)*32 + row%32.
+// --------------------------------------------------------------------------------------
+struct QMat {
+  int8_t* q = nullptr;
+  uint32_t* d = nullptr;
+  int32_t N = 0, K = 0;
+  static size_t q_bytes(int64_t N, int64_t K) { return (size_t)(N * K); }
+  static size_t d_bytes(int64_t N, int64_t K) { return (size_t)(N * (K / QK) * 2); }
+};
+
+enum GemmMode : int32_t { GM_F32 = 0, GM_F32_ADD = 1, GM_SWIGLU = 2, GM_PARTIAL = 3 };
+
+struct GemmArgs {
+  const __bf16* A = nullptr;    // [rows][lda]
+  int32_t lda = 0;
+  const int32_t* a_rows = nullptr;   // grouped: physical A row = a_rows[m] / a_row_div
+  int32_t a_row_div = 1;
+  const int8_t* wq = nullptr;
+  const uint32_t* wd = nullptr;
+  int64_t wq_estride = 0, wd_estride = 0;   // grouped: per-expert strides (elements)
+  int32_t M = 0, N = 0, K = 0;
+  const int32_t* tiles = nullptr;     // grouped: [max_tiles][4] {expert, m0, m1, 0}
+  const int32_t* n_tiles = nullptr;   // grouped: device count of valid tiles
+  int32_t mode = GM_F32;
+  void* out = nullptr;
+  int32_t ldo = 0;
+  float* partial = nullptr;           // split-K partial sums [splits][M][N]
+  int32_t splits = 1;
+};
+
+// Kernel launchers (return hipError_t of the launch).
+hipError_t launch_gemm(const GemmArgs& a, int grid_m_tiles, int mt, hipStream_t s);
+hipError_t launch_splitk_reduce(const float* partial, int32_t splits, int32_t M, int32_t N,
+                                int32_t mode, void* out, int32_t ldo, hipStream_t s);
+// Repack interchange q8_0 rows into a QMat.  mode 0: destination rows dst_row0 ..
+// dst_row0+dst_rows-1 take source rows 0 .. (rows >= src_rows are zero).  mode 1 (gate/up
+// interleave for the SwiGLU epilogue): destination row n = 64*g + 32*w + i takes row
+// 32*g + i of src0 (w = 0, gate) or src1 (w = 1, up); rows >= src_rows are zero.
+// Source blocks beyond ceil(k_src/32) are zero.
+hipError_t launch_repack_q8_0(const void* src0, const void* src1, int64_t src_rows, int32_t k_src,
+                              int64_t dst_row0, int64_t dst_rows, int32_t mode, QMat dst,
+                              hipStream_t s);
+hipError_t launch_quantize_q8_0(const float* x, int64_t rows, int32_t k, int64_t ldx,
+                                void* out, hipStream_t s);
+hipError_t launch_rmsnorm(const float* x, const float* gamma, int32_t n, int32_t d, float eps,
+                          __bf16* y, float* y32, hipStream_t s);
+
+struct KvLayer {          // one layer's cache (device pointers), capacity n_ctx
+  void* k = nullptr;      // f16 [Hkv][n_ctx][hd]  | int8 [Hkv][n_ctx][hd]
+  void* v = nullptr;      // f16 [Hkv][hd][n_ctx]  | int8 [Hkv][hd][n_ctx]
+  uint16_t* kd = nullptr; // q8_0: fp16 [Hkv][n_ctx][hd/32]
+  uint16_t* vd = nullptr; // q8_0: fp16 [Hkv][hd/32][n_ctx]
+};
+size_t kv_layer_bytes(int32_t n_kv_head, int32_t head_dim, int32_t n_ctx, int32_t kv_type);
+KvLayer kv_layer_at(void* base, int32_t n_kv_head, int32_t head_dim, int32_t n_ctx,
+                    int32_t kv_type);
+
+hipError_t launch_rope_qk(const float* qkv, const float* cos_t, const float* sin_t, int32_t n,
+                          int32_t start, int32_t n_head, int32_t n_kv_head, int32_t head_dim,
+                          int32_t kv_type, int32_t n_ctx, _Float16* q_out, KvLayer kv,
+                          hipStream_t s);
+hipError_t launch_v_append(const float* qkv, int32_t n, int32_t start, int32_t n_head,
+                           int32_t n_kv_head, int32_t head_dim, int32_t kv_type, int32_t n_ctx,
+                           KvLayer kv, hipStream_t s);
+
+struct AttnArgs {
+  const _Float16* q = nullptr;   // [n][Hq][hd]
+  KvLayer kv;
+  int32_t n = 0, start = 0, n_head = 0, n_kv_head = 0, head_dim = 0, kv_type = 0, n_ctx = 0;
+  __bf16* out = nullptr;         // [n][Hq*hd]
+  int32_t splits = 1;
+  float* part_o = nullptr;       // [splits][rows_total][hd]
+  float* part_ml = nullptr;      // [splits][rows_total][2]
+};
+int attention_rows_total(int32_t n, int32_t n_head);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+hipError_t launch_kv_pack(const KvLayer kv, int32_t t0, int32_t nt, int32_t n_kv_head,
+                          int32_t head_dim, int32_t kv_type, int32_t n_ctx, int which,
+                          uint8_t* out, hipStream_t s);
+hipError_t launch_kv_unpack(KvLayer kv, int32_t t0, int32_t nt, int32_t n_kv_head,
+                            int32_t head_dim, int32_t kv_type, int32_t n_ctx, int which,
+                            const uint8_t* in, hipStream_t s);
+
+// Routed experts.
+struct MoeBuffers {
+  float* logits = nullptr;     // [n][E]
+  int32_t* idx = nullptr;      // [n][k]
+  float* w = nullptr;          // [n][k]
+  int32_t* rank = nullptr;     // [n*k]   rank of a slot among equal experts in its chunk
+  int32_t* chunk_cnt = nullptr;// [n_chunks][E]
+  int32_t* offsets = nullptr;  // [E+1]
+  int32_t* perm = nullptr;     // [n*k]  permuted position -> slot (t*k + rank)
+  int32_t* inv = nullptr;      // [n*k]  slot -> permuted position
+  int32_t* tiles = nullptr;    // [max_tiles][4]
+  int32_t* n_tiles = nullptr;  // [1]
+};
+hipError_t launch_router(const float* y, const int8_t* rq, const uint16_t* rd, int32_t n, int32_t d,
+                         int32_t E, int32_t k, float* logits, int32_t* idx, float* w,
+                         hipStream_t s);
+hipError_t launch_moe_permute(const MoeBuffers& b, int32_t n, int32_t E, int32_t k, int32_t mt,
+                              int32_t max_tiles, hipStream_t s);
+hipError_t launch_moe_unpermute(const float* y_perm, const MoeBuffers& b, int32_t n, int32_t d,
+                                int32_t k, const float* x_res, float* x_out, hipStream_t s);
+
+// Router weights unpacked from the interchange layout: int8 [E][d] + fp16 [E][d/32].
+hipError_t launch_unpack_router(const void* src, int32_t E, int32_t d, int8_t* q, uint16_t* dd,
+                                hipStream_t s);
+
+constexpr int kMoeChunk = 256;   // slots per permute chunk
+
+}  // namespace cp

@@ -1,0 +1,612 @@
+// Non-GEMM kernels of the prefill path (gfx950): weight repack, q8_0 encode, RMSNorm,
+// RoPE + K/V cache append, state pack/unpack, and the routed-expert router / permute /
+// unpermute.  Every kernel that decides stored bytes or integers (q8_0 codes, cache rows,
+// expert indices) uses one float32 rounding per operation (explicit _rn intrinsics; the
+// library is also built without floating-point contraction).
+#include "cp_internal.h"
+#include "k_common.h"
+
+namespace cp {
+
+// ======================================================================================
+// Weight repack: interchange q8_0 rows -> QMat (lane-ordered quants, paired fp16 scales)
+// ======================================================================================
+__global__ void repack_kernel(const uint8_t* __restrict__ src0, const uint8_t* __restrict__ src1,
+                              int64_t src_rows, int32_t nb_src, int64_t dst_row0, int64_t dst_rows,
+                              int32_t mode, int8_t* __restrict__ dq, uint16_t* __restrict__ dd,
+                              int32_t K) {
+  const int KB = K / QK, KP = K / 64;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= dst_rows * KB) return;
+  const int64_t nl = i / KB;
+  const int kb = (int)(i % KB);
+  int64_t n, sr;
+  const uint8_t* src;
+  if (mode == 0) {
+    n = dst_row0 + nl;
+    sr = nl;
+    src = src0;
+  } else {
+    n = nl;
+    const int64_t grp = n / 64, w = (n % 64) / 32, ii = n % 32;
+    sr = grp * 32 + ii;
+    src = w ? src1 : src0;
+  }
+  uint32_t wds[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  uint16_t dbits = 0;
+  if (sr < src_rows && kb < nb_src) {
+    const uint8_t* p = src + (sr * nb_src + kb) * 34;
+    dbits = (uint16_t)(p[0] | (p[1] << 8));
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      wds[j] = (uint32_t)p[2 + 4 * j] | ((uint32_t)p[3 + 4 * j] << 8) |
+               ((uint32_t)p[4 + 4 * j] << 16) | ((uint32_t)p[5 + 4 * j] << 24);
+  }
+  const int64_t n32 = n / 32, r = n % 32;
+  uint4* q = reinterpret_cast<uint4*>(dq);
+  q[(n32 * KB + kb) * 64 + r] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+  q[(n32 * KB + kb) * 64 + 32 + r] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
+  dd[((n32 * KP + kb / 2) * 32 + r) * 2 + (kb & 1)] = dbits;
+}
+
+hipError_t launch_repack_q8_0(const void* src0, const void* src1, int64_t src_rows, int32_t k_src,
+                              int64_t dst_row0, int64_t dst_rows, int32_t mode, QMat dst,
+                              hipStream_t s) {
+  const int32_t nb_src = (k_src + QK - 1) / QK;
+  const int64_t work = dst_rows * (dst.K / QK);
+  if (work == 0) return hipSuccess;
+  hipLaunchKernelGGL(repack_kernel, dim3((unsigned)ceil_div(work, 256)), dim3(256), 0, s,
+                     (const uint8_t*)src0, (const uint8_t*)src1, src_rows, nb_src, dst_row0,
+                     dst_rows, mode, dst.q, reinterpret_cast<uint16_t*>(dst.d), dst.K);
+  return hipGetLastError();
+}
+
+// ======================================================================================
+// q8_0 encode of float32 rows (interchange layout).  32 lanes per block; the block amax
+// is a wavefront reduction; d = amax/127 and 1/d correctly rounded; q rounds half away.
+// ======================================================================================
+__device__ __forceinline__ void q8_encode_lane(float x, float& d, int& q) {
+  const float amax = warp_max32(fabsf(x));
+  d = __fdiv_rn(amax, 127.0f);
+  const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
+  int v = (int)roundf(__fmul_rn(x, id));
+  q = v > 127 ? 127 : (v < -127 ? -127 : v);
+}
+
+__global__ void quantize_kernel(const float* __restrict__ x, int64_t rows, int32_t k, int64_t ldx,
+                                uint8_t* __restrict__ out) {
+  const int nb = (k + QK - 1) / QK;
+  const int64_t bi = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (bi >= rows * nb) return;
+  const int64_t row = bi / nb;
+  const int blk = (int)(bi % nb);
+  const int l = threadIdx.x & 31;
+  const int col = blk * QK + l;
+  const float v = col < k ? x[row * ldx + col] : 0.0f;
+  float d;
+  int q;
+  q8_encode_lane(v, d, q);
+  uint8_t* o = out + (row * nb + blk) * 34;
+  if (l == 0) {
+    const uint16_t b = float_to_half_bits(d);
+    o[0] = (uint8_t)(b & 0xFF);
+    o[1] = (uint8_t)(b >> 8);
+  }
+  o[2 + l] = (uint8_t)(int8_t)q;
+}
+
+hipError_t launch_quantize_q8_0(const float* x, int64_t rows, int32_t k, int64_t ldx, void* out,
+                                hipStream_t s) {
+  const int64_t nb = (k + QK - 1) / QK;
+  const int64_t blocks = ceil_div(rows * nb, 8);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, k, ldx,
+                     (uint8_t*)out);
+  return hipGetLastError();
+}
+
+// ======================================================================================
+// RMSNorm: y = x / sqrt(mean(x^2) + eps) * gamma  -> bf16 (and optionally float32)
+// ======================================================================================
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
+                                                      const float* __restrict__ gamma, int32_t d,
+                                                      float eps, __bf16* __restrict__ y,
+                                                      float* __restrict__ y32) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * d;
+  float ss = 0.0f;
+  for (int i = threadIdx.x * 4; i < d; i += 1024) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + i);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  ss = red[0] + red[1] + red[2] + red[3];
+  const float scale = 1.0f / sqrtf(ss / (float)d + eps);
+  for (int i = threadIdx.x * 4; i < d; i += 1024) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + i);
+    const float4 gm = *reinterpret_cast<const float4*>(gamma + i);
+    const float a = v.x * scale * gm.x, b = v.y * scale * gm.y;
+    const float c = v.z * scale * gm.z, e = v.w * scale * gm.w;
+    uint2 pk = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, e));
+    *reinterpret_cast<uint2*>(y + row * d + i) = pk;
+    if (y32) *reinterpret_cast<float4*>(y32 + row * d + i) = make_float4(a, b, c, e);
+  }
+}
+
+hipError_t launch_rmsnorm(const float* x, const float* gamma, int32_t n, int32_t d, float eps,
+                          __bf16* y, float* y32, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(n), dim3(256), 0, s, x, gamma, d, eps, y, y32);
+  return hipGetLastError();
+}
+
+// ======================================================================================
+// KV cache layout of one layer (capacity n_ctx, a multiple of 64):
+//   f16 : K [Hkv][n_ctx][hd] f16, V transposed [Hkv][hd][n_ctx] f16
+//   q8_0: K int8 [Hkv][n_ctx][hd] + fp16 scales [Hkv][n_ctx][hd/32];
+//         V int8 [Hkv][hd][n_ctx] + fp16 scales [Hkv][hd/32][n_ctx]
+// ======================================================================================
+size_t kv_layer_bytes(int32_t Hkv, int32_t hd, int32_t n_ctx, int32_t kv_type) {
+  const size_t elems = (size_t)Hkv * hd * n_ctx;
+  if (kv_type == CP_KV_F16) return 2 * align_up(elems * 2);
+  return 2 * align_up(elems) + 2 * align_up(elems / QK * 2);
+}
+
+KvLayer kv_layer_at(void* base, int32_t Hkv, int32_t hd, int32_t n_ctx, int32_t kv_type) {
+  KvLayer L;
+  uint8_t* p = (uint8_t*)base;
+  const size_t elems = (size_t)Hkv * hd * n_ctx;
+  if (kv_type == CP_KV_F16) {
+    L.k = p;
+    L.v = p + align_up(elems * 2);
+  } else {
+    L.k = p;
+    L.v = p + align_up(elems);
+    L.kd = (uint16_t*)(p + 2 * align_up(elems));
+    L.vd = (uint16_t*)(p + 2 * align_up(elems) + align_up(elems / QK * 2));
+  }
+  return L;
+}
+
+// RoPE on q and k (rotate-half pairs (i, i+hd/2)), then q -> f16 output and k -> cache.
+// One workgroup per token; each wave handles 64 consecutive values of one head.
+__global__ __launch_bounds__(256) void rope_qk_kernel(const float* __restrict__ qkv,
+                                                      const float* __restrict__ cos_t,
+                                                      const float* __restrict__ sin_t,
+                                                      int32_t start, int32_t Hq, int32_t Hkv,
+                                                      int32_t hd, int32_t kv_type, int32_t n_ctx,
+                                                      _Float16* __restrict__ q_out, KvLayer kv) {
+  const int64_t t = blockIdx.x;
+  const int64_t p = start + t;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = hd / 2;
+  const int64_t Nqkv = (int64_t)(Hq + 2 * Hkv) * hd;
+  const float* row = qkv + t * Nqkv;
+  const int nseg = (Hq + Hkv) * hd / 64;
+  for (int seg = wave; seg < nseg; seg += 4) {
+    const int e = seg * 64 + lane;
+    const int head = e / hd, i = e % hd;
+    const int ic = i < half ? i : i - half;
+    const float c = cos_t[p * half + ic], s = sin_t[p * half + ic];
+    const float x = row[e];
+    float out;
+    if (i < half) {
+      const float y = row[head * hd + i + half];
+      out = __fsub_rn(__fmul_rn(x, c), __fmul_rn(y, s));
+    } else {
+      const float y = row[head * hd + i - half];
+      out = __fadd_rn(__fmul_rn(x, c), __fmul_rn(y, s));
+    }
+    if (head < Hq) {
+      q_out[(t * Hq + head) * hd + i] = (_Float16)out;
+    } else {
+      const int64_t gi = (int64_t)(head - Hq) * n_ctx + p;
+      if (kv_type == CP_KV_F16) {
+        reinterpret_cast<_Float16*>(kv.k)[gi * hd + i] = (_Float16)out;
+      } else {
+        float d;
+        int q;
+        q8_encode_lane(out, d, q);
+        reinterpret_cast<int8_t*>(kv.k)[gi * hd + i] = (int8_t)q;
+        if ((i & 31) == 0) kv.kd[gi * (hd / QK) + i / QK] = float_to_half_bits(d);
+      }
+    }
+  }
+}
+
+hipError_t launch_rope_qk(const float* qkv, const float* cos_t, const float* sin_t, int32_t n,
+                          int32_t start, int32_t n_head, int32_t n_kv_head, int32_t head_dim,
+                          int32_t kv_type, int32_t n_ctx, _Float16* q_out, KvLayer kv,
+                          hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_qk_kernel, dim3(n), dim3(256), 0, s, qkv, cos_t, sin_t, start, n_head,
+                     n_kv_head, head_dim, kv_type, n_ctx, q_out, kv);
+  return hipGetLastError();
+}
+
+// V rows -> transposed cache.  A workgroup takes 64 tokens of one kv head: each wave
+// converts 64 consecutive dims of a token row (q8_0: per-32 amax by wavefront
+// reduction), the codes are transposed through LDS, then written 64 positions at a time.
+__global__ __launch_bounds__(256) void v_append_kernel(const float* __restrict__ qkv, int32_t n,
+                                                       int32_t start, int32_t Hq, int32_t Hkv,
+                                                       int32_t hd, int32_t kv_type, int32_t n_ctx,
+                                                       KvLayer kv) {
+  __shared__ uint16_t sv[128][66];
+  __shared__ int8_t sq[128][68];
+  __shared__ uint16_t sd[4][64];
+  const int t0 = blockIdx.x * 64;
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t Nqkv = (int64_t)(Hq + 2 * Hkv) * hd;
+  const int64_t vcol = (int64_t)(Hq + Hkv + g) * hd;
+  const int parts = hd / 64;
+  for (int seg = wave; seg < 64 * parts; seg += 4) {
+    const int tl = seg / parts, i = (seg % parts) * 64 + lane;
+    const int t = t0 + tl;
+    const float v = t < n ? qkv[(int64_t)t * Nqkv + vcol + i] : 0.0f;
+    if (kv_type == CP_KV_F16) {
+      sv[i][tl] = float_to_half_bits(v);
+    } else {
+      float d;
+      int q;
+      q8_encode_lane(v, d, q);
+      sq[i][tl] = (int8_t)q;
+      if ((i & 31) == 0) sd[i / QK][tl] = float_to_half_bits(d);
+    }
+  }
+  __syncthreads();
+  const int nt = min(64, n - t0);
+  for (int e = threadIdx.x; e < hd * 64; e += 256) {
+    const int i = e / 64, tl = e % 64;
+    if (tl >= nt) continue;
+    const int64_t dst = ((int64_t)g * hd + i) * n_ctx + start + t0 + tl;
+    if (kv_type == CP_KV_F16) reinterpret_cast<uint16_t*>(kv.v)[dst] = sv[i][tl];
+    else reinterpret_cast<int8_t*>(kv.v)[dst] = sq[i][tl];
+  }
+  if (kv_type != CP_KV_F16) {
+    for (int e = threadIdx.x; e < (hd / QK) * 64; e += 256) {
+      const int b = e / 64, tl = e % 64;
+      if (tl >= nt) continue;
+      kv.vd[((int64_t)g * (hd / QK) + b) * n_ctx + start + t0 + tl] = sd[b][tl];
+    }
+  }
+}
+
+hipError_t launch_v_append(const float* qkv, int32_t n, int32_t start, int32_t n_head,
+                           int32_t n_kv_head, int32_t head_dim, int32_t kv_type, int32_t n_ctx,
+                           KvLayer kv, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(v_append_kernel, dim3((unsigned)ceil_div(n, 64), n_kv_head), dim3(256), 0, s,
+                     qkv, n, start, n_head, n_kv_head, head_dim, kv_type, n_ctx, kv);
+  return hipGetLastError();
+}
+
+// ======================================================================================
+// State pack / unpack: device cache <-> serialized rows (token-major (t, h); f16 rows of
+// hd binary16, or q8_0 rows of hd/32 blocks {fp16 d, int8 q[32]}).  which: 0 = K, 1 = V.
+// ======================================================================================
+__device__ __forceinline__ int64_t kv_units(int32_t nt, int32_t Hkv, int32_t hd, int32_t kv_type) {
+  return kv_type == CP_KV_F16 ? (int64_t)nt * Hkv * hd : (int64_t)nt * Hkv * (hd / QK) * 34;
+}
+
+template <bool PACK>
+__global__ void kv_pack_kernel(KvLayer kv, int32_t t0, int32_t nt, int32_t Hkv, int32_t hd,
+                               int32_t kv_type, int32_t n_ctx, int which, uint8_t* io) {
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= kv_units(nt, Hkv, hd, kv_type)) return;
+  if (kv_type == CP_KV_F16) {
+    const int64_t tl = u / ((int64_t)Hkv * hd);
+    const int h = (int)((u / hd) % Hkv), i = (int)(u % hd);
+    const int64_t t = t0 + tl;
+    uint16_t* base = reinterpret_cast<uint16_t*>(which ? kv.v : kv.k);
+    const int64_t off = which ? ((int64_t)h * hd + i) * n_ctx + t : ((int64_t)h * n_ctx + t) * hd + i;
+    uint16_t* o = reinterpret_cast<uint16_t*>(io) + u;
+    if (PACK) *o = base[off];
+    else base[off] = *o;
+    return;
+  }
+  const int nb = hd / QK;
+  const int bb = (int)(u % 34);
+  const int b = (int)((u / 34) % nb);
+  const int h = (int)((u / (34 * nb)) % Hkv);
+  const int64_t t = t0 + u / ((int64_t)34 * nb * Hkv);
+  uint8_t* p;
+  if (bb < 2) {
+    const int64_t si = which ? ((int64_t)h * nb + b) * n_ctx + t : ((int64_t)h * n_ctx + t) * nb + b;
+    p = reinterpret_cast<uint8_t*>(which ? kv.vd : kv.kd) + si * 2 + bb;
+  } else {
+    const int j = b * QK + bb - 2;
+    const int64_t qi = which ? ((int64_t)h * hd + j) * n_ctx + t : ((int64_t)h * n_ctx + t) * hd + j;
+    p = reinterpret_cast<uint8_t*>(which ? kv.v : kv.k) + qi;
+  }
+  if (PACK) io[u] = *p;
+  else *p = io[u];
+}
+
+hipError_t launch_kv_pack(const KvLayer kv, int32_t t0, int32_t nt, int32_t Hkv, int32_t hd,
+                          int32_t kv_type, int32_t n_ctx, int which, uint8_t* out, hipStream_t s) {
+  const int64_t units = (kv_type == CP_KV_F16) ? (int64_t)nt * Hkv * hd : (int64_t)nt * Hkv * (hd / QK) * 34;
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_pack_kernel<true>, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, s,
+                     kv, t0, nt, Hkv, hd, kv_type, n_ctx, which, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_unpack(KvLayer kv, int32_t t0, int32_t nt, int32_t Hkv, int32_t hd,
+                            int32_t kv_type, int32_t n_ctx, int which, const uint8_t* in,
+                            hipStream_t s) {
+  const int64_t units = (kv_type == CP_KV_F16) ? (int64_t)nt * Hkv * hd : (int64_t)nt * Hkv * (hd / QK) * 34;
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_pack_kernel<false>, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, s,
+                     kv, t0, nt, Hkv, hd, kv_type, n_ctx, which, const_cast<uint8_t*>(in));
+  return hipGetLastError();
+}
+
+// ======================================================================================
+// Routed experts
+// ======================================================================================
+__global__ void unpack_router_kernel(const uint8_t* __restrict__ src, int32_t E, int32_t d,
+                                     int8_t* __restrict__ q, uint16_t* __restrict__ dd) {
+  const int nb = d / QK;
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= (int64_t)E * nb * 34) return;
+  const int64_t blk = u / 34;
+  const int bb = (int)(u % 34);
+  const uint8_t* p = src + blk * 34;
+  if (bb == 0) dd[blk] = (uint16_t)(p[0] | (p[1] << 8));
+  else if (bb >= 2) q[blk * QK + bb - 2] = (int8_t)p[bb];
+}
+
+hipError_t launch_unpack_router(const void* src, int32_t E, int32_t d, int8_t* q, uint16_t* dd,
+                                hipStream_t s) {
+  const int64_t units = (int64_t)E * (d / QK) * 34;
+  hipLaunchKernelGGL(unpack_router_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, s,
+                     (const uint8_t*)src, E, d, q, dd);
+  return hipGetLastError();
+}
+
+// Router logits in the fixed float32 order (per block: products and sums ascending,
+// then acc += d_b * P_b over blocks ascending), then top-k (descending logit, ties to
+// the lower expert index) and softmax over the k selected logits.  A workgroup takes
+// RT tokens; thread e computes expert e for all of them; y is staged 256 columns at a time.
+constexpr int RT = 8;
+__global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ y,
+                                                     const int8_t* __restrict__ rq,
+                                                     const uint16_t* __restrict__ rd, int32_t n,
+                                                     int32_t d, int32_t E, int32_t k,
+                                                     float* __restrict__ logits,
+                                                     int32_t* __restrict__ idx,
+                                                     float* __restrict__ wout) {
+  __shared__ float sy[RT][256];
+  __shared__ float slog[RT][256];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * RT;
+  float acc[RT];
+#pragma unroll
+  for (int tt = 0; tt < RT; ++tt) acc[tt] = 0.0f;
+  for (int c0 = 0; c0 < d; c0 += 256) {
+    __syncthreads();
+    for (int e = tid; e < RT * 256; e += 256) {
+      const int tt = e / 256, j = e % 256;
+      const int t = t0 + tt;
+      sy[tt][j] = (t < n && c0 + j < d) ? y[(int64_t)t * d + c0 + j] : 0.0f;
+    }
+    __syncthreads();
+    if (tid < E) {
+      for (int b = 0; b < 8; ++b) {
+        const int col = c0 + b * QK;
+        if (col >= d) break;
+        const int blk = col / QK;
+        const uint4* qp = reinterpret_cast<const uint4*>(rq + (int64_t)tid * d + col);
+        const uint4 qa = qp[0], qb = qp[1];
+        const uint32_t w[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        const float ds = half_bits_to_float(rd[(int64_t)tid * (d / QK) + blk]);
+#pragma unroll
+        for (int tt = 0; tt < RT; ++tt) {
+          const float* ys = &sy[tt][b * QK];
+          float P = __fmul_rn((float)(int8_t)(w[0] & 0xFF), ys[0]);
+#pragma unroll
+          for (int j = 1; j < QK; ++j) {
+            const float qj = (float)(int8_t)((w[j >> 2] >> (8 * (j & 3))) & 0xFF);
+            P = __fadd_rn(P, __fmul_rn(qj, ys[j]));
+          }
+          const float term = __fmul_rn(ds, P);
+          acc[tt] = (blk == 0) ? term : __fadd_rn(acc[tt], term);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < E) {
+#pragma unroll
+    for (int tt = 0; tt < RT; ++tt) {
+      slog[tt][tid] = acc[tt];
+      if (t0 + tt < n) logits[(int64_t)(t0 + tt) * E + tid] = acc[tt];
+    }
+  }
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int tt = wave; tt < RT; tt += 4) {
+    const int t = t0 + tt;
+    if (t >= n) break;
+    float v[4];
+    bool used[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      v[j] = e < E ? slog[tt][e] : -INFINITY;
+      used[j] = e >= E;
+    }
+    float selv[16];
+    int sele[16];
+    for (int r = 0; r < k; ++r) {
+      float bv = -INFINITY;
+      int be = 0x7FFFFFFF;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        if (!used[j] && (v[j] > bv || (v[j] == bv && e < be))) { bv = v[j]; be = e; }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oe = __shfl_xor(be, o, 64);
+        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (lane + 64 * j == be) used[j] = true;
+      selv[r] = bv;
+      sele[r] = be;
+    }
+    if (lane == 0) {
+      float z = 0.0f;
+      float ex[16];
+      for (int r = 0; r < k; ++r) { ex[r] = expf(selv[r] - selv[0]); z += ex[r]; }
+      for (int r = 0; r < k; ++r) {
+        idx[(int64_t)t * k + r] = sele[r];
+        wout[(int64_t)t * k + r] = ex[r] / z;
+      }
+    }
+  }
+}
+
+hipError_t launch_router(const float* y, const int8_t* rq, const uint16_t* rd, int32_t n, int32_t d,
+                         int32_t E, int32_t k, float* logits, int32_t* idx, float* w,
+                         hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(router_kernel, dim3((unsigned)ceil_div(n, RT)), dim3(256), 0, s, y, rq, rd, n,
+                     d, E, k, logits, idx, w);
+  return hipGetLastError();
+}
+
+// Permute: slots s = t*k + rank are grouped by expert, stable in slot order.
+//  (1) per chunk of 256 slots: rank of each slot among earlier equal-expert slots in the
+//      chunk, and the chunk's per-expert counts;
+//  (2) one workgroup: per-expert exclusive sums over chunks, expert offsets, tile table;
+//  (3) per chunk: position = base(chunk, expert) + rank.
+__global__ __launch_bounds__(256) void moe_rank_kernel(const int32_t* __restrict__ idx, int32_t n_slots,
+                                                       int32_t E, int32_t* __restrict__ rank,
+                                                       int32_t* __restrict__ chunk_cnt) {
+  __shared__ int32_t se[kMoeChunk];
+  __shared__ int32_t scnt[256];
+  const int tid = threadIdx.x;
+  const int64_t s = (int64_t)blockIdx.x * kMoeChunk + tid;
+  const bool valid = s < n_slots;
+  se[tid] = valid ? idx[s] : -1;
+  for (int e = tid; e < E; e += 256) scnt[e] = 0;
+  __syncthreads();
+  if (valid) {
+    const int e = se[tid];
+    int r = 0;
+    for (int j = 0; j < tid; ++j) r += (se[j] == e);
+    rank[s] = r;
+    atomicAdd(&scnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) chunk_cnt[(int64_t)blockIdx.x * E + e] = scnt[e];
+}
+
+__global__ __launch_bounds__(256) void moe_scan_kernel(int32_t n_chunks, int32_t E, int32_t mt,
+                                                       int32_t max_tiles,
+                                                       int32_t* __restrict__ chunk_cnt,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ tiles,
+                                                       int32_t* __restrict__ n_tiles) {
+  __shared__ int32_t stot[256];
+  __shared__ int32_t soff[257];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) {
+    int total = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      const int v = chunk_cnt[(int64_t)c * E + e];
+      chunk_cnt[(int64_t)c * E + e] = total;
+      total += v;
+    }
+    stot[e] = total;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int off = 0, nt = 0;
+    for (int e = 0; e < E; ++e) {
+      soff[e] = off;
+      offsets[e] = off;
+      for (int m = 0; m < stot[e] && nt < max_tiles; m += mt) {
+        reinterpret_cast<int4*>(tiles)[nt++] = make_int4(e, off + m, off + min(m + mt, stot[e]), 0);
+      }
+      off += stot[e];
+    }
+    offsets[E] = off;
+    *n_tiles = nt;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256)
+    for (int c = 0; c < n_chunks; ++c) chunk_cnt[(int64_t)c * E + e] += soff[e];
+}
+
+__global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restrict__ idx, int32_t n_slots,
+                                                          int32_t E, const int32_t* __restrict__ rank,
+                                                          const int32_t* __restrict__ chunk_cnt,
+                                                          int32_t* __restrict__ perm,
+                                                          int32_t* __restrict__ inv) {
+  const int64_t s = (int64_t)blockIdx.x * kMoeChunk + threadIdx.x;
+  if (s >= n_slots) return;
+  const int e = idx[s];
+  const int pos = chunk_cnt[(int64_t)blockIdx.x * E + e] + rank[s];
+  perm[pos] = (int32_t)s;
+  inv[s] = pos;
+}
+
+hipError_t launch_moe_permute(const MoeBuffers& b, int32_t n, int32_t E, int32_t k, int32_t mt,
+                              int32_t max_tiles, hipStream_t s) {
+  const int32_t n_slots = n * k;
+  const int32_t n_chunks = (int32_t)ceil_div(n_slots, kMoeChunk);
+  hipLaunchKernelGGL(moe_rank_kernel, dim3(n_chunks), dim3(kMoeChunk), 0, s, b.idx, n_slots, E,
+                     b.rank, b.chunk_cnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(256), 0, s, n_chunks, E, mt, max_tiles,
+                     b.chunk_cnt, b.offsets, b.tiles, b.n_tiles);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(n_chunks), dim3(kMoeChunk), 0, s, b.idx, n_slots, E,
+                     b.rank, b.chunk_cnt, b.perm, b.inv);
+  return hipGetLastError();
+}
+
+// Unpermute: x_out[t] = x_res[t] + sum_{rank} w[t][rank] * y_perm[pos(t, rank)], summed in
+// rank order.  One thread per 4 columns of a token.
+__global__ __launch_bounds__(256) void moe_unpermute_kernel(const float* __restrict__ y_perm,
+                                                            const int32_t* __restrict__ inv,
+                                                            const float* __restrict__ w, int32_t n,
+                                                            int32_t d, int32_t k,
+                                                            const float* x_res, float* x_out) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t quads = d / 4;
+  if (q >= (int64_t)n * quads) return;
+  const int64_t t = q / quads, c = (q % quads) * 4;
+  float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int r = 0; r < k; ++r) {
+    const float wr = w[t * k + r];
+    const float4 yv = *reinterpret_cast<const float4*>(y_perm + (int64_t)inv[t * k + r] * d + c);
+    m.x += wr * yv.x; m.y += wr * yv.y; m.z += wr * yv.z; m.w += wr * yv.w;
+  }
+  const float4 xr = *reinterpret_cast<const float4*>(x_res + t * d + c);
+  *reinterpret_cast<float4*>(x_out + t * d + c) =
+      make_float4(xr.x + m.x, xr.y + m.y, xr.z + m.z, xr.w + m.w);
+}
+
+hipError_t launch_moe_unpermute(const float* y_perm, const MoeBuffers& b, int32_t n, int32_t d,
+                                int32_t k, const float* x_res, float* x_out, hipStream_t s) {
+  const int64_t work = (int64_t)n * (d / 4);
+  if (work == 0) return hipSuccess;
+  hipLaunchKernelGGL(moe_unpermute_kernel, dim3((unsigned)ceil_div(work, 256)), dim3(256), 0, s,
+                     y_perm, b.inv, b.w, n, d, k, x_res, x_out);
+  return hipGetLastError();
+}
+
+}  // namespace cp

@@ -1,0 +1,210 @@
+"""Python face of the C ABI: the same calls, with torch tensors for device buffers.
+
+The binding is the library's caller: it allocates the three device arenas with
+torch (PyTorch is used for device memory and streams only) and passes raw
+pointers.  Nothing here computes any part of the prefill path.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from ._lib import (CP_OK, KV_TYPES, PrefillError, cp_config, cp_layer_weights, lib, ptr,
+                   stream_ptr)
+
+MATRIX_KEYS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "w_router")
+
+
+def make_config(model, n_ctx_max: int, n_chunk_max: int) -> cp_config:
+    """cp_config from any object with the model's geometry attributes (n_layer, d_model,
+    n_head, n_kv_head, head_dim, ffn_dim, n_expert, n_expert_used, expert_ffn_dim,
+    rms_eps, rope_theta, kv_type as "f16"/"q8_0")."""
+    kv = model.kv_type
+    return cp_config(model.n_layer, model.d_model, model.n_head, model.n_kv_head, model.head_dim,
+                     model.ffn_dim, model.n_expert, model.n_expert_used, model.expert_ffn_dim,
+                     float(model.rms_eps), float(model.rope_theta),
+                     KV_TYPES[kv] if isinstance(kv, str) else int(kv), int(n_ctx_max),
+                     int(n_chunk_max))
+
+
+def arena_sizes(cfg: cp_config):
+    L = lib()
+    return (L.cp_weights_arena_bytes(ctypes.byref(cfg)), L.cp_kv_bytes(ctypes.byref(cfg)),
+            L.cp_workspace_bytes(ctypes.byref(cfg)))
+
+
+def validate_config(cfg: cp_config) -> str:
+    """Empty string when valid, else the library's message."""
+    L = lib()
+    if L.cp_validate_config(ctypes.byref(cfg)) == CP_OK:
+        return ""
+    return L.cp_config_error(ctypes.byref(cfg)).decode()
+
+
+def to_device(layer: Dict[str, np.ndarray], device="cuda") -> Dict[str, torch.Tensor]:
+    """Copy one layer's interchange bytes / gains to device memory."""
+    out = {}
+    for k, v in layer.items():
+        t = v if isinstance(v, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(v))
+        out[k] = t.to(device)
+    return out
+
+
+class PrefillContext:
+    """Owns the arenas of one cp_ctx and forwards every call to the library."""
+
+    def __init__(self, cfg: cp_config, layers: Sequence[Dict[str, torch.Tensor]],
+                 device="cuda", stream: Optional[torch.cuda.Stream] = None):
+        self.L = lib()
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.stream = stream
+        wb, kb, sb = arena_sizes(cfg)
+        if wb == 0:
+            raise PrefillError(-1, validate_config(cfg))
+        self.warena = torch.empty(wb, dtype=torch.uint8, device=self.device)
+        self.kv = torch.empty(kb, dtype=torch.uint8, device=self.device)
+        self.ws = torch.empty(sb, dtype=torch.uint8, device=self.device)
+        arr = (cp_layer_weights * cfg.n_layer)()
+        for i, lw in enumerate(layers):
+            arr[i] = cp_layer_weights(*(ptr(lw.get(k)) for k in
+                                        ("wq", "wk", "wv", "wo", "attn_norm", "ffn_norm",
+                                         "w_gate", "w_up", "w_down", "w_router")))
+        self._ctx = ctypes.c_void_p()
+        rc = self.L.prefill_init(ctypes.byref(cfg), arr, ptr(self.warena), ptr(self.kv),
+                                 ptr(self.ws), stream_ptr(stream), ctypes.byref(self._ctx))
+        if rc != CP_OK:
+            raise PrefillError(rc, "prefill_init failed")
+
+    # -- calls ---------------------------------------------------------------------------
+    def _check(self, rc: int):
+        if rc != CP_OK:
+            raise PrefillError(rc, self.L.prefill_last_error(self._ctx).decode())
+
+    def prefill_chunk(self, x_in: torch.Tensor, x_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        x_out = torch.empty_like(x_in) if x_out is None else x_out
+        self._check(self.L.prefill_chunk(self._ctx, ptr(x_in), ptr(x_out), x_in.shape[0]))
+        return x_out
+
+    def prefill_chunk_trace(self, x_in: torch.Tensor, x_out: torch.Tensor, layer_out=None,
+                            layer_stride: int = 0, route_idx=None, route_stride: int = 0):
+        """layer_out / route_idx: device tensors (or None); strides in elements."""
+        self._check(self.L.prefill_chunk_trace(self._ctx, ptr(x_in), ptr(x_out), x_in.shape[0],
+                                               ptr(layer_out), layer_stride, ptr(route_idx),
+                                               route_stride))
+        return x_out
+
+    def prefill_chunk_raw(self, x_in_ptr: int, x_out_ptr: int, n: int) -> int:
+        return self.L.prefill_chunk(self._ctx, x_in_ptr, x_out_ptr, n)
+
+    def prefill_chunk_timed(self, x_in: torch.Tensor, x_out: Optional[torch.Tensor] = None):
+        x_out = torch.empty_like(x_in) if x_out is None else x_out
+        ms = (ctypes.c_float * self.cfg.n_layer)()
+        self._check(self.L.prefill_chunk_timed(self._ctx, ptr(x_in), ptr(x_out), x_in.shape[0], ms))
+        return x_out, list(ms)
+
+    def kv_cache_get_state(self) -> bytes:
+        n = ctypes.c_size_t()
+        self._check(self.L.kv_cache_get_state(self._ctx, None, 0, ctypes.byref(n)))
+        buf = ctypes.create_string_buffer(n.value)
+        self._check(self.L.kv_cache_get_state(self._ctx, buf, n.value, ctypes.byref(n)))
+        return buf.raw[:n.value]
+
+    def kv_cache_set_state(self, blob: bytes) -> int:
+        """Returns the library's status code (CP_OK or an error) without raising."""
+        return self.L.kv_cache_set_state(self._ctx, blob, len(blob))
+
+    def kv_cache_truncate(self, n_keep: int) -> int:
+        return self.L.kv_cache_truncate(self._ctx, n_keep)
+
+    @property
+    def n_past(self) -> int:
+        return self.L.prefill_n_past(self._ctx)
+
+    def last_error(self) -> str:
+        return self.L.prefill_last_error(self._ctx).decode()
+
+    def cp_kernel_timing(self, enable: bool):
+        self._check(self.L.cp_kernel_timing(self._ctx, int(enable)))
+
+    def cp_kernel_times(self, cls: str):
+        ms, n = ctypes.c_float(), ctypes.c_int32()
+        self._check(self.L.cp_kernel_times(self._ctx, cls.encode(), ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
+
+    def close(self):
+        if self._ctx:
+            self.L.prefill_free(self._ctx)
+            self._ctx = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------------------------- helpers
+def cp_quantize_q8_0(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q8_0 interchange bytes of float32 device rows x [..., k] (encode on the GPU)."""
+    k = x.shape[-1]
+    rows = x.numel() // k
+    nb = (k + 31) // 32
+    if out is None:
+        out = torch.empty(x.shape[:-1] + (nb * 34,), dtype=torch.uint8, device=x.device)
+    rc = lib().cp_quantize_q8_0(ptr(x), rows, k, k, ptr(out), stream_ptr())
+    if rc != CP_OK:
+        raise PrefillError(rc, "cp_quantize_q8_0 failed")
+    return out
+
+
+def cp_test_kv_layer_bytes(n_kv_head, head_dim, n_ctx, kv_type) -> int:
+    return lib().cp_test_kv_layer_bytes(n_kv_head, head_dim, n_ctx, kv_type)
+
+
+def cp_test_rope_kv_append(qkv, cos_t, sin_t, n, start, n_head, n_kv_head, head_dim, kv_type,
+                           n_ctx, q_out, kv):
+    rc = lib().cp_test_rope_kv_append(ptr(qkv), ptr(cos_t), ptr(sin_t), n, start, n_head,
+                                      n_kv_head, head_dim, kv_type, n_ctx, ptr(q_out), ptr(kv),
+                                      stream_ptr())
+    if rc != CP_OK:
+        raise PrefillError(rc, "cp_test_rope_kv_append failed")
+
+
+def cp_test_kv_rows(kv, n_tokens, n_kv_head, head_dim, kv_type, n_ctx, out):
+    rc = lib().cp_test_kv_rows(ptr(kv), n_tokens, n_kv_head, head_dim, kv_type, n_ctx, ptr(out),
+                               stream_ptr())
+    if rc != CP_OK:
+        raise PrefillError(rc, "cp_test_kv_rows failed")
+
+
+def cp_test_router(y, w_router, n, d, n_expert, k, logits, idx, weight):
+    L = lib()
+    scratch = torch.empty(L.cp_test_router_scratch_bytes(n_expert, d), dtype=torch.uint8,
+                          device=y.device)
+    rc = L.cp_test_router(ptr(y), ptr(w_router), n, d, n_expert, k, ptr(logits), ptr(idx),
+                          ptr(weight), ptr(scratch), stream_ptr())
+    if rc != CP_OK:
+        raise PrefillError(rc, "cp_test_router failed")
+
+
+def cp_test_gemm(A, W, M, N, K, mode, splits, out):
+    L = lib()
+    scratch = torch.empty(max(1, L.cp_test_gemm_scratch_bytes(M, N, K, splits)), dtype=torch.uint8,
+                          device=A.device)
+    rc = L.cp_test_gemm(ptr(A), ptr(W), M, N, K, mode, splits, ptr(out), ptr(scratch), stream_ptr())
+    if rc != CP_OK:
+        raise PrefillError(rc, "cp_test_gemm failed")
+
+
+def cp_test_attention(q, kv, n, start, n_head, n_kv_head, head_dim, kv_type, n_ctx, kv_splits, out):
+    L = lib()
+    scratch = torch.empty(L.cp_test_attention_scratch_bytes(n, n_head, head_dim, kv_splits),
+                          dtype=torch.uint8, device=q.device)
+    rc = L.cp_test_attention(ptr(q), ptr(kv), n, start, n_head, n_kv_head, head_dim, kv_type, n_ctx,
+                             kv_splits, ptr(out), ptr(scratch), stream_ptr())
+    if rc != CP_OK:
+        raise PrefillError(rc, "cp_test_attention failed")

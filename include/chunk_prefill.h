@@ -1,0 +1,245 @@
+/*
+ * chunk_prefill.h - C ABI of the MI355X (gfx950) chunked prompt prefill library.
+ *
+ * What it computes.  Chunked prompt prefill of a decoder transformer, as measured
+ * throughout the pages "completion : allow the prompt to be processed under its own
+ * split mode", "llama : switch the split mode of a live context", the llama.cpp
+ * "--split-overlap" pull request, "refactor: one prefill planner and one pad-trim hook
+ * for CLI and server" and "Prompt chunks sized for a layer split's pipeline": a prompt
+ * is read in chunks of C tokens; each chunk runs through every layer of this GPU's
+ * share of the model, appends its K/V rows to a device-resident cache (f16 or q8_0),
+ * and attends causally to the whole cache so far.  Per layer:
+ *   RMSNorm -> q8_0 QKV projection -> RoPE -> K/V append -> causal GQA attention
+ *   -> q8_0 output projection + residual -> RMSNorm -> SwiGLU FFN (dense, or top-k
+ *   routed experts) + residual.
+ * There is no final norm and no LM head: the chunk's output is the residual stream
+ * after the last layer.
+ *
+ * Conventions shared by every call.
+ *   - "dev" pointers are device (HBM) addresses, "host" pointers are host memory.
+ *   - The caller owns every buffer: weights, arenas, cache, workspace, inputs and
+ *     outputs.  The library never allocates device memory.  A context borrows the
+ *     arenas and the stream until prefill_free().
+ *   - Work is enqueued on the caller's hipStream_t (passed as void*); calls that return
+ *     data to the host synchronise that stream.
+ *   - Every call returns CP_OK (0) or a negative CP_E_* code and never aborts on bad
+ *     input.  Validation happens on the host before anything is enqueued, so a rejected
+ *     call leaves the context (its cache and n_past) exactly as it was; the pages ask
+ *     that a failure leave a working context with its cache intact ("llama : switch the
+ *     split mode of a live context", section "What this adds"; "completion : allow the
+ *     prompt ...", section "Memory": an allocation failure is reported, not asserted).
+ *   - A context is thread-compatible, not thread-safe.
+ *
+ * q8_0 interchange layout (how weights are handed in).  A matrix [N_out][K_in] is
+ * row-major; each row is ceil(K_in/32) blocks of 34 bytes: a little-endian fp16 scale
+ * d, then 32 int8 values q; value = float(d) * q.  Rows with K_in % 32 != 0 are
+ * zero-padded to the next multiple of 32.  prefill_init() repacks these bytes into its
+ * own arena layout; the interchange copies may be freed after it returns.
+ */
+#ifndef CHUNK_PREFILL_H
+#define CHUNK_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum cp_status {
+  CP_OK = 0,
+  CP_E_INVALID = -1,   /* bad argument: NULL pointer, unsupported shape, bad size     */
+  CP_E_CAPACITY = -2,  /* n_tokens > n_chunk_max, or n_past + n_tokens > n_ctx_max     */
+  CP_E_STATE = -3,     /* serialized state does not match this context / is truncated */
+  CP_E_DEVICE = -4,    /* a HIP runtime call failed (message in prefill_last_error)    */
+  CP_E_ARENA = -5      /* caller buffer too small or misaligned (256-byte alignment)   */
+};
+
+enum cp_kv_type { CP_KV_F16 = 0, CP_KV_Q8_0 = 1 };
+
+/* Model geometry and capacities.  Supported shapes: head_dim in {64, 128};
+ * n_head % n_kv_head == 0; d_model % 64 == 0; (n_head * head_dim) % 64 == 0;
+ * dense ffn_dim > 0 with n_expert == 0, or routed experts with ffn_dim == 0,
+ * n_expert in [1, 256], 1 <= n_expert_used <= min(n_expert, 16), expert_ffn_dim > 0. */
+typedef struct cp_config {
+  int32_t n_layer, d_model, n_head, n_kv_head, head_dim;
+  int32_t ffn_dim;                                 /* dense FFN width; 0 for experts  */
+  int32_t n_expert, n_expert_used, expert_ffn_dim; /* 0, 0, 0 for a dense FFN          */
+  float rms_eps, rope_theta;                       /* RMSNorm epsilon, RoPE base       */
+  int32_t kv_type;                                 /* CP_KV_F16 or CP_KV_Q8_0          */
+  int32_t n_ctx_max;                               /* cache capacity in tokens         */
+  int32_t n_chunk_max;                             /* largest chunk prefill_chunk takes */
+} cp_config;
+
+/* One layer's weights, as device pointers in the q8_0 interchange layout (above).
+ *   wq [n_head*head_dim][d_model], wk/wv [n_kv_head*head_dim][d_model],
+ *   wo [d_model][n_head*head_dim]; attn_norm / ffn_norm: float32 [d_model] gains.
+ *   Dense:   w_gate, w_up [ffn_dim][d_model], w_down [d_model][ffn_dim].
+ *   Experts: w_router [n_expert][d_model]; w_gate, w_up [n_expert][expert_ffn_dim]
+ *            [d_model] and w_down [n_expert][d_model][expert_ffn_dim], experts stored
+ *            one after another, each in the interchange layout. */
+typedef struct cp_layer_weights {
+  const void *wq, *wk, *wv, *wo;
+  const float *attn_norm, *ffn_norm;
+  const void *w_gate, *w_up, *w_down;
+  const void *w_router;   /* NULL for a dense FFN */
+} cp_layer_weights;
+
+typedef struct cp_ctx cp_ctx;
+
+/* Sizes (bytes) of the three caller-owned device arenas for a configuration, or 0 when
+ * the configuration is invalid.  Host-only; no GPU needed. */
+size_t cp_weights_arena_bytes(const cp_config* cfg);  /* repacked weights of all layers */
+size_t cp_kv_bytes(const cp_config* cfg);             /* KV cache at n_ctx_max tokens   */
+size_t cp_workspace_bytes(const cp_config* cfg);      /* per-chunk scratch + RoPE table */
+
+/* Host-only check of a configuration: CP_OK or CP_E_INVALID (message via
+ * cp_config_error()). */
+int cp_validate_config(const cp_config* cfg);
+const char* cp_config_error(const cp_config* cfg);
+
+/* Create a context.  layers: host array of n_layer descriptors (device pointers inside).
+ * weights_arena / kv_buf / workspace: device buffers of at least the sizes above,
+ * 256-byte aligned.  hip_stream: the hipStream_t all work is enqueued on (NULL = the
+ * default stream).  Repacks the weights into the arena and builds the RoPE table
+ * (angles in float64, cos/sin rounded to float32) on that stream, then synchronises.
+ * On success *out holds the context and n_past = 0. */
+int prefill_init(const cp_config* cfg, const cp_layer_weights* layers, void* weights_arena,
+                 void* kv_buf, void* workspace, void* hip_stream, cp_ctx** out);
+
+/* Process one chunk of n_tokens rows at positions n_past .. n_past+n_tokens-1.
+ * x_in, x_out: dev float32 [n_tokens][d_model] row-major; x_out may equal x_in.
+ * Every layer appends the chunk's K/V (post-RoPE K) to its cache, then attends to cache
+ * rows 0 .. n_past+n_tokens-1 ("append, then attend").  Requires 1 <= n_tokens <=
+ * n_chunk_max and n_past + n_tokens <= n_ctx_max (else CP_E_CAPACITY, nothing
+ * enqueued).  Returns once the work is enqueued; n_past advances by n_tokens. */
+int prefill_chunk(cp_ctx* ctx, const float* x_in, float* x_out, int32_t n_tokens);
+
+/* Same as prefill_chunk, then synchronises and writes the time of each layer (ms,
+ * hipEvents recorded on the stream at every layer boundary) to host layer_ms[n_layer].
+ * This is the per-layer t(C, D) the b + a*C cost model is fitted to ("Prompt chunks
+ * sized for a layer split's pipeline", sections "Summary" and "What changed"). */
+int prefill_chunk_timed(cp_ctx* ctx, const float* x_in, float* x_out, int32_t n_tokens,
+                        float* layer_ms);
+
+/* Same as prefill_chunk, and also copies, after every layer l, the residual stream of the
+ * chunk to layer_out + l*layer_stride (dev float32 [n_tokens][d_model], NULL to skip) and,
+ * for routed experts, the selected expert indices to route_idx + l*route_stride (dev int32
+ * [n_tokens][n_expert_used], NULL to skip).  For checking each layer on its own. */
+int prefill_chunk_trace(cp_ctx* ctx, const float* x_in, float* x_out, int32_t n_tokens,
+                        float* layer_out, int64_t layer_stride, int32_t* route_idx,
+                        int64_t route_stride);
+
+/* Serialized, layout-independent KV state ("completion : allow the prompt to be
+ * processed under its own split mode", section "What this does"; "llama : switch the
+ * split mode of a live context", section "What this adds", step 1).  Little-endian:
+ *   magic "CPKV", u32 version 1, u32 kv_type, u32 n_layer, u32 n_kv_head, u32 head_dim,
+ *   u32 n_tokens, f32 rope_theta (32-byte header), then for every layer K then V, each
+ *   n_tokens x n_kv_head rows in token-major order; an f16 row is head_dim binary16
+ *   values, a q8_0 row is head_dim/32 blocks {fp16 d; int8 q[32]}.  K is post-RoPE.
+ * The form depends on none of n_ctx_max, n_chunk_max or the device layout.
+ *
+ * kv_cache_get_state: dst = host buffer of cap bytes, or NULL to query the size.  Writes
+ * the first n_past tokens; *n_bytes = blob size.  CP_E_ARENA if cap is too small.
+ * Synchronises the stream; stages through the workspace. */
+int kv_cache_get_state(cp_ctx* ctx, void* dst, size_t cap, size_t* n_bytes);
+
+/* Restore a blob from host memory.  The whole header (magic, version, kv_type, n_layer,
+ * n_kv_head, head_dim, rope_theta) and the exact length are validated against the
+ * context first; on any mismatch, or n_tokens > n_ctx_max, returns CP_E_STATE and the
+ * previous cache and n_past are untouched.  On success n_past = n_tokens.  The bytes a
+ * following kv_cache_get_state returns are identical to src.  Synchronises the stream. */
+int kv_cache_set_state(cp_ctx* ctx, const void* src, size_t n_bytes);
+
+/* Host-only header check of a blob against a configuration (the same validation
+ * kv_cache_set_state does before touching the cache). */
+int cp_state_check(const cp_config* cfg, const void* src, size_t n_bytes);
+size_t cp_state_bytes(const cp_config* cfg, int32_t n_tokens);
+
+/* Forget cache rows n_keep .. n_past-1 (0 <= n_keep <= n_past): n_past = n_keep.  Rows
+ * at or beyond n_past are scratch and are overwritten by the next chunk. */
+int kv_cache_truncate(cp_ctx* ctx, int32_t n_keep);
+
+int32_t prefill_n_past(const cp_ctx* ctx);
+const char* prefill_last_error(const cp_ctx* ctx);
+void prefill_free(cp_ctx* ctx);   /* releases host-side state only; buffers stay the caller's */
+
+/* Per-kernel timing.  With timing on, every launch of the named kernel class is
+ * bracketed by hipEvents on the context's stream; cp_kernel_times() synchronises and
+ * returns the summed duration (ms) and launch count since the last reset.  Classes:
+ * "gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attention", "rope_kv_append",
+ * "rmsnorm", "moe_route", "moe_permute", "moe_gemm_gate_up", "moe_gemm_down",
+ * "moe_unpermute", "splitk_reduce". */
+int cp_kernel_timing(cp_ctx* ctx, int enable);
+int cp_kernel_times(cp_ctx* ctx, const char* kernel_class, float* total_ms, int32_t* launches);
+
+/* q8_0 encode of float32 rows into the interchange layout, on the GPU (used to build
+ * seeded weights in device memory).  x: dev float32 [rows][ldx], first k columns used;
+ * out: dev bytes [rows][ceil(k/32)*34].  Per block of 32: d = amax/127 (float32,
+ * correctly rounded), q = round-half-away-from-zero(x * (1/d)), stored d = fp16 (RNE);
+ * values beyond k count as 0.  The amax is a wavefront reduction over the block. */
+int cp_quantize_q8_0(const float* x, int64_t rows, int32_t k, int64_t ldx, void* out,
+                     void* hip_stream);
+
+/* ----------------------------------------------------------------------------------
+ * Test exports: each runs one kernel of the path on caller buffers, so that a test can
+ * feed it the oracle's inputs and compare the outputs bit for bit or to tolerance.
+ * All pointers are device pointers unless stated; all are enqueued on hip_stream.
+ * ---------------------------------------------------------------------------------- */
+
+/* RoPE + K/V append for one chunk, exactly as prefill_chunk runs it.
+ * qkv: float32 [n][(n_head + 2*n_kv_head)*head_dim] (q, then k, then v columns);
+ * cos/sin: float32 [n_pos][head_dim/2] tables (rows = absolute positions);
+ * q_out: f16 [n][n_head][head_dim] (RoPE applied); the rows are written at positions
+ * start .. start+n-1 of a one-layer cache kv (layout as in cp_kv_bytes for n_layer = 1,
+ * capacity n_ctx).  Read them back with cp_test_kv_rows. */
+/* Bytes of a one-layer cache of capacity n_ctx (rounded up to 64 positions internally). */
+size_t cp_test_kv_layer_bytes(int32_t n_kv_head, int32_t head_dim, int32_t n_ctx, int32_t kv_type);
+
+int cp_test_rope_kv_append(const float* qkv, const float* cos_t, const float* sin_t,
+                           int32_t n, int32_t start, int32_t n_head, int32_t n_kv_head,
+                           int32_t head_dim, int32_t kv_type, int32_t n_ctx, void* q_out,
+                           void* kv, void* hip_stream);
+
+/* Copy rows [0, n_tokens) of a one-layer cache into the serialized row form (K rows then
+ * V rows, token-major, as in the state blob).  out: dev bytes. */
+int cp_test_kv_rows(const void* kv, int32_t n_tokens, int32_t n_kv_head, int32_t head_dim,
+                    int32_t kv_type, int32_t n_ctx, void* out, void* hip_stream);
+
+/* Router logits (float32, fixed order: per 32-block ascending products and sums, then
+ * scale-times-partial accumulated over blocks ascending, no fused multiply-add), top-k
+ * (descending logit, ties to the lower expert index) and softmax weights over the k.
+ * y: float32 [n][d]; w_router: q8_0 interchange [n_expert][d]; logits: float32
+ * [n][n_expert]; idx: int32 [n][k]; weight: float32 [n][k]; scratch: dev buffer of
+ * cp_test_router_scratch_bytes(n_expert, d) bytes (router weights unpacked). */
+size_t cp_test_router_scratch_bytes(int32_t n_expert, int32_t d);
+int cp_test_router(const float* y, const void* w_router, int32_t n, int32_t d, int32_t n_expert,
+                   int32_t k, float* logits, int32_t* idx, float* weight, void* scratch,
+                   void* hip_stream);
+
+/* One q8_0 GEMM as the layer runs it: out = A * W^T with A bf16 [M][K] (lda = K),
+ * W in the interchange layout [N][K].  mode 0: out float32 [M][N] = result;
+ * mode 1: out float32 [M][N] += result; mode 2 (SwiGLU): W holds gate rows then up rows
+ * ([2F][K], F % 32 == 0) and out is bf16 [M][F] = silu(gate) * up.  splits > 1 forces
+ * split-K with a deterministic reduction (0 = the library's own choice).  scratch: dev
+ * buffer of cp_test_gemm_scratch_bytes(M, N, K, splits) bytes (repacked weights and
+ * partial sums). */
+size_t cp_test_gemm_scratch_bytes(int32_t M, int32_t N, int32_t K, int32_t splits);
+int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
+                 int32_t splits, void* out, void* scratch, void* hip_stream);
+
+/* Causal flash attention of a chunk against a one-layer cache (rows already appended):
+ * q: f16 [n][n_head][head_dim]; kv: one-layer cache (capacity n_ctx) holding positions
+ * 0 .. start+n-1; out: bf16 [n][n_head*head_dim].  kv_splits > 0 forces that many
+ * KV-range splits (0 = the library's choice).  scratch: dev buffer of
+ * cp_test_attention_scratch_bytes(...) bytes. */
+size_t cp_test_attention_scratch_bytes(int32_t n, int32_t n_head, int32_t head_dim,
+                                       int32_t kv_splits);
+int cp_test_attention(const void* q, const void* kv, int32_t n, int32_t start, int32_t n_head,
+                      int32_t n_kv_head, int32_t head_dim, int32_t kv_type, int32_t n_ctx,
+                      int32_t kv_splits, void* out, void* scratch, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CHUNK_PREFILL_H */

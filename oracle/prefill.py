@@ -167,8 +167,14 @@ class OracleModel:
         o = attention(q32, K, V, positions)
         return np.asarray(x, np.float64) + o.reshape(x.shape[0], -1) @ W["wo"].T
 
-    def ffn_rows(self, l: int, x: np.ndarray, return_routing: bool = False):
-        """x + FFN(RMSNorm(x)): dense SwiGLU, or routed experts."""
+    def ffn_rows(self, l: int, x: np.ndarray, return_routing: bool = False, route_idx=None):
+        """x + FFN(RMSNorm(x)): dense SwiGLU, or routed experts.
+
+        route_idx: optional [n][k] expert indices to combine instead of the oracle's own
+        top-k (weights are still the softmax of the oracle's logits over those experts).
+        Callers pass it only for an index set they have checked is a top-k set of the
+        oracle's logits up to a stated tolerance (near ties make several sets correct).
+        """
         c, W = self.cfg, self.weights(l)
         y = rmsnorm(x, W["ffn_norm"], c.rms_eps)
         if not c.n_expert:
@@ -178,17 +184,26 @@ class OracleModel:
         d16, q = q8_0_from_bytes(self.layers[l]["w_router"], nb)
         r = router_logits_ordered(y.astype(np.float32), d16, q)
         idx, w = moe_route(r, c.n_expert_used)
+        if route_idx is not None:
+            idx = np.asarray(route_idx, dtype=np.int32)
+            sel = np.take_along_axis(r, idx, axis=1).astype(np.float64)
+            e = np.exp(sel - sel.max(axis=1, keepdims=True))
+            w = e / e.sum(axis=1, keepdims=True)
         out = x + moe_ffn(y, idx, w, W["w_gate"], W["w_up"], W["w_down"])
         return (out, (r, idx, w)) if return_routing else out
 
-    def layer(self, l: int, x: np.ndarray, cache: OracleCache, start: int) -> np.ndarray:
+    def layer(self, l: int, x: np.ndarray, cache: OracleCache, start: int, route_idx=None,
+              routing_out: Optional[List] = None) -> np.ndarray:
         """One layer over rows at positions start .. start+n-1 (append, then attend)."""
         n = x.shape[0]
         pos = np.arange(start, start + n)
         q32, k32, v32 = self.qkv_rows(l, x, pos)
         cache.write(l, start, k32, v32)
         x = self.attn_out_rows(l, x, q32, cache.kval[l], cache.vval[l], pos)
-        return self.ffn_rows(l, x)
+        out, routing = self.ffn_rows(l, x, return_routing=True, route_idx=route_idx)
+        if routing_out is not None:
+            routing_out.append(routing)
+        return out
 
     # -- drivers ------------------------------------------------------------------------
     def forward_chunk(self, x: np.ndarray, cache: OracleCache) -> np.ndarray:
@@ -212,15 +227,19 @@ class OracleModel:
         return np.concatenate(outs, axis=0) if outs else np.zeros((0, self.cfg.d_model))
 
     def prefill_layer_major(self, x: np.ndarray, cache: Optional[OracleCache] = None,
-                            n_ctx: Optional[int] = None, layer_outputs: Optional[List] = None
-                            ) -> np.ndarray:
-        """Layer-major driver: the whole prompt through layer 0, then layer 1, ..."""
+                            n_ctx: Optional[int] = None, layer_outputs: Optional[List] = None,
+                            routes: Optional[Sequence] = None,
+                            routing_out: Optional[List] = None) -> np.ndarray:
+        """Layer-major driver: the whole prompt through layer 0, then layer 1, ...
+
+        routes: optional per-layer expert index sets (see ffn_rows); routing_out collects
+        each layer's (logits, indices, weights)."""
         if cache is None:
             cache = self.new_cache(n_ctx or x.shape[0])
         start = cache.n_past
         h = np.asarray(x, dtype=np.float64)
         for l in range(self.cfg.n_layer):
-            h = self.layer(l, h, cache, start)
+            h = self.layer(l, h, cache, start, None if routes is None else routes[l], routing_out)
             if layer_outputs is not None:
                 layer_outputs.append(h.copy())
         cache.n_past = start + x.shape[0]

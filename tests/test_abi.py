@@ -1,0 +1,81 @@
+"""The C-ABI library loads without a GPU, exports every declared call, and its host-only
+logic (configuration checks, arena sizing, state header validation) behaves (CPU only)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "chunk_prefill.h")
+
+
+@pytest.fixture(scope="module")
+def cpa():
+    import chunked_prompt_prefill_amd as m
+    m.lib()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if not n.startswith("_")))
+
+
+def test_every_declared_symbol_is_exported(cpa):
+    names = declared_functions()
+    assert "prefill_init" in names and "kv_cache_set_state" in names and len(names) >= 25
+    lib = ctypes.CDLL(cpa.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    from chunked_prompt_prefill_amd._lib import SIGNATURES
+    assert set(SIGNATURES) == set(names), set(names) ^ set(SIGNATURES)
+
+
+def test_arena_sizes_for_every_workload(cpa):
+    for name, w in synth.WORKLOADS.items():
+        n_ctx = w.n_prompt + max(w.depths, default=0)
+        chunk = max(w.chunk_sweep) if w.chunk_sweep else w.chunk
+        cfg = cpa.make_config(w, n_ctx, chunk)
+        assert cpa.validate_config(cfg) == "", name
+        wb, kb, sb = cpa.arena_sizes(cfg)
+        assert wb > 0 and kb > 0 and sb > 0
+        # the cache holds K and V of every layer at capacity
+        row = w.head_dim * 2 if w.kv_type == "f16" else w.head_dim // 32 * 34
+        assert kb >= w.n_layer * 2 * n_ctx * w.n_kv_head * row
+
+
+@pytest.mark.parametrize("field,value", [("head_dim", 96), ("n_kv_head", 3), ("d_model", 100),
+                                         ("kv_type", 2), ("n_chunk_max", 0), ("rms_eps", 0.0),
+                                         ("n_expert_used", 3), ("n_ctx_max", 0)])
+def test_invalid_configs_are_rejected(cpa, field, value):
+    cfg = cpa.make_config(synth.WORKLOADS["dense27b_f16"], 1024, 512)
+    setattr(cfg, field, value)
+    assert cpa.validate_config(cfg) != ""
+    assert cpa.arena_sizes(cfg) == (0, 0, 0)
+
+
+def test_state_header_check_matches_oracle_blobs(cpa):
+    from model_inputs import TINY_DENSE, q8_layers
+    w = synth.Workload("abi_state", 2, 64, 4, 2, 64, 64, kv_type="q8_0")
+    m = oracle.OracleModel(w, q8_layers(w))
+    cache = m.new_cache(32)
+    m.prefill(synth.prompt_inputs(w, 9), 4, cache=cache)
+    blob = oracle.state_bytes(cache, w.rope_theta)
+    L = cpa.lib()
+    cfg = cpa.make_config(w, 32, 8)
+    assert L.cp_state_bytes(ctypes.byref(cfg), 9) == len(blob)
+    assert L.cp_state_check(ctypes.byref(cfg), blob, len(blob)) == 0
+    for off in (0, 4, 8, 12, 16, 20, 24, 28):
+        bad = bytearray(blob)
+        bad[off] ^= 0x11
+        assert L.cp_state_check(ctypes.byref(cfg), bytes(bad), len(bad)) == -3
+    assert L.cp_state_check(ctypes.byref(cfg), blob[:-2], len(blob) - 2) == -3
+    small = cpa.make_config(w, 8, 8)      # capacity below the blob's 9 tokens
+    assert L.cp_state_check(ctypes.byref(small), blob, len(blob)) == -3
