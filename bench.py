@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Chunked prompt prefill benchmark on one MI355X.
+
+A step is one full prefill of the workload's prompt from an empty cache: every chunk
+through every layer of the GPU's share (RMSNorm, q8_0 QKV GEMM, RoPE + KV append,
+causal GQA flash attention, output GEMM, SwiGLU FFN).  Weights and inputs are
+synthetic N(0, 0.02) values of the workload's shapes, generated in device memory and
+q8_0-encoded by the library.  Default workload: the dense 27B-class share of 16 layers
+(d_model 5120, 40/8 heads, head_dim 128, SwiGLU 17408, f16 cache), a 17,055-token prompt
+in 512-token chunks.
+
+Also reported: the chunk-size sweep (4 layers, chunks 128..8192, depth 0 and 16,384)
+with the per-layer cost fit t = b + a*C ("Prompt chunks sized for a layer split's
+pipeline", sections "Summary" and "What changed"), the dominant kernel's roofline
+fraction from HIP events around its launches, and the CPU oracle timed on a bounded
+sample on this host.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-sweep] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def note(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def dense_params(w) -> int:
+    d, hd = w.d_model, w.head_dim
+    attn = (w.n_head + 2 * w.n_kv_head) * hd * d + d * w.n_head * hd
+    if w.n_expert:
+        return attn + w.n_expert * d + w.n_expert * 3 * w.expert_ffn_dim * d
+    return attn + 3 * w.ffn_dim * d
+
+
+def active_params(w) -> int:
+    d, hd = w.d_model, w.head_dim
+    attn = (w.n_head + 2 * w.n_kv_head) * hd * d + d * w.n_head * hd
+    if w.n_expert:
+        return attn + w.n_expert * d + w.n_expert_used * 3 * w.expert_ffn_dim * d
+    return attn + 3 * w.ffn_dim * d
+
+
+def chunk_flops(w, C: int, D: int) -> float:
+    """Algorithmic flops of one chunk through one layer: 2*P_active*C plus the unmasked
+    causal half of attention, 4*Hq*hd*(C*D + C(C+1)/2)."""
+    return 2.0 * active_params(w) * C + 4.0 * w.n_head * w.head_dim * (C * D + C * (C + 1) / 2)
+
+
+def chunk_bytes(w, C: int, D: int) -> float:
+    """Algorithmic HBM bytes of one chunk-layer: q8_0 weights (all experts touched), K/V
+    read over D + C positions, K/V write of C rows, x in and out."""
+    e = 2.0 if w.kv_type == "f16" else 34.0 / 32.0
+    kv = 2.0 * w.n_kv_head * w.head_dim * e
+    return dense_params(w) * 34.0 / 32.0 + kv * (D + C) + kv * C + 2.0 * C * w.d_model * 4
+
+
+def roofline_s(w, C, D):
+    return max(chunk_flops(w, C, D) / (PEAK_BF16_TFLOPS * 1e12),
+               chunk_bytes(w, C, D) / (PEAK_HBM_GBS * 1e9))
+
+
+def fit_linear(C, t):
+    """Least-squares line t = b + a*C: returns (b, a, r2)."""
+    import numpy as np
+    C = np.asarray(C, dtype=np.float64)
+    t = np.asarray(t, dtype=np.float64)
+    a, b = np.polyfit(C, t, 1)
+    res = t - (b + a * C)
+    sst = float(np.sum((t - t.mean()) ** 2))
+    return float(b), float(a), (1.0 - float(np.sum(res ** 2)) / sst) if sst > 0 else 1.0
+
+
+def gpu_layers(w, torch, cpa, synth):
+    layers = []
+    for l in range(w.n_layer):
+        lw = {}
+        for name, shape in synth.weight_shapes(w):
+            t = synth.layer_weight(w, l, name, shape, backend="torch", device="cuda")
+            lw[name] = t if name.endswith("_norm") else cpa.cp_quantize_q8_0(t)
+            del t
+        layers.append(lw)
+    torch.cuda.synchronize()
+    return layers
+
+
+def run_main(args, torch, cpa, synth):
+    w = synth.WORKLOADS[args.workload]
+    n, C = w.n_prompt, w.chunk
+    note(f"workload {w.name}: {w.n_layer} layers, {n} tokens in {C}-token chunks, {w.kv_type} cache")
+    t = time.time()
+    layers = gpu_layers(w, torch, cpa, synth)
+    ctx = cpa.PrefillContext(cpa.make_config(w, n, C), layers)
+    del layers
+    torch.cuda.empty_cache()
+    x = synth.prompt_inputs(w, backend="torch", device="cuda")
+    out = torch.empty_like(x)
+    note(f"weights generated, encoded and repacked in {time.time() - t:.1f}s")
+    chunks = [(s, min(n, s + C)) for s in range(0, n, C)]
+
+    def step():
+        ctx.kv_cache_truncate(0)
+        for s, e in chunks:
+            rc = ctx.prefill_chunk_raw(x[s:e].data_ptr(), out[s:e].data_ptr(), e - s)
+            if rc != 0:
+                raise RuntimeError(f"prefill_chunk failed: {rc} {ctx.last_error()}")
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        note(f"warmup step {i + 1}/{args.warmup} done")
+    dom = "moe_gemm_gate_up" if w.n_expert else "gemm_gate_up"
+    ctx.cp_kernel_timing(dom)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dom_ms, dom_launches = ctx.cp_kernel_times(dom)
+    ctx.cp_kernel_timing(None)
+    note(f"timed {args.steps} steps in {t1 - t0:.3f}s")
+    total = t1 - t0
+    tps = n * args.steps / total
+    # roofline of the dominant kernel (algorithmic flops of every timed launch)
+    if w.n_expert:
+        per_tok = 2.0 * w.n_expert_used * 2 * w.expert_ffn_dim * w.d_model
+    else:
+        per_tok = 2.0 * 2 * w.ffn_dim * w.d_model
+    dom_flops = per_tok * n * w.n_layer * args.steps
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else 0.0
+    # whole-prompt roofline: sum of per-chunk-layer bounds
+    bound = sum(roofline_s(w, e - s, s) for s, e in chunks) * w.n_layer
+    res = {
+        "value": tps,
+        "ms_per_step": total / args.steps * 1e3,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "launches": dom_launches, "avg_launch_us": dom_ms * 1e3 / max(1, dom_launches),
+                     "flops_per_token": per_tok},
+        "prompt_roofline": {"bound_ms_per_step": bound * 1e3,
+                            "frac": bound / (total / args.steps)},
+    }
+    ctx.close()
+    del x, out
+    torch.cuda.empty_cache()
+    return w, res
+
+
+def run_sweep(args, torch, cpa, synth, oracle_fit):
+    w = synth.WORKLOADS["dense27b_sweep"]
+    sizes, depths = w.chunk_sweep, w.depths
+    Cmax = max(sizes)
+    note(f"sweep {w.name}: {w.n_layer} layers, chunks {list(sizes)}, depths {list(depths)}")
+    layers = gpu_layers(w, torch, cpa, synth)
+    ctx = cpa.PrefillContext(cpa.make_config(w, w.depth_prefill + Cmax, Cmax), layers)
+    del layers
+    torch.cuda.empty_cache()
+    x = synth.prompt_inputs(w, w.depth_prefill + Cmax, backend="torch", device="cuda")
+    out = torch.empty_like(x)
+    table = {}
+    for D in depths:
+        ctx.kv_cache_truncate(0)
+        for s in range(0, D, Cmax):
+            ctx.prefill_chunk(x[s:s + Cmax], out[s:s + Cmax])
+        torch.cuda.synchronize()
+        for C in sizes:
+            reps = []
+            for r in range(2 + args.sweep_reps):          # two warm-up chunks, then R timed
+                ctx.kv_cache_truncate(D)
+                _, ms = ctx.prefill_chunk_timed(x[D:D + C], out[D:D + C])
+                if r >= 2:
+                    reps.append(ms)
+            import numpy as np
+            med = np.median(np.array(reps), axis=0)       # per layer
+            table[(C, D)] = med
+        note(f"sweep depth {D} done")
+    import numpy as np
+    fit = {}
+    for D in depths:
+        per_layer = []
+        for l in range(w.n_layer):
+            b, a, r2 = oracle_fit(list(sizes), [table[(C, D)][l] for C in sizes])
+            per_layer.append({"b_ms": b, "a_ms_per_token": a, "r2": r2})
+        fit[str(D)] = {"per_layer": per_layer,
+                       "mean_b_ms": float(np.mean([p["b_ms"] for p in per_layer])),
+                       "mean_a_ms_per_token": float(np.mean([p["a_ms_per_token"] for p in per_layer])),
+                       "b_over_a_tokens": float(np.mean([p["b_ms"] for p in per_layer]) /
+                                                np.mean([p["a_ms_per_token"] for p in per_layer]))}
+    points = []
+    for D in depths:
+        for C in sizes:
+            t_layer = float(np.mean(table[(C, D)]))
+            points.append({"chunk": C, "depth": D, "ms_per_layer": t_layer,
+                           "tokens_per_s_per_layer": C / (t_layer * 1e-3),
+                           "tokens_per_s_4_layers": C / (float(np.sum(table[(C, D)])) * 1e-3),
+                           "roofline_frac": roofline_s(w, C, D) / (t_layer * 1e-3),
+                           "mfma_frac": chunk_flops(w, C, D) / (PEAK_BF16_TFLOPS * 1e12) / (t_layer * 1e-3)})
+    ctx.close()
+    return {"workload": f"{w.name}: {w.n_layer} layers of the dense 27B-class shapes, f16 cache",
+            "fit": fit, "points": points}
+
+
+def run_cpu_baseline(args, w):
+    """The oracle as it stands, on a bounded sample: one layer of the workload's shapes over
+    the first `cpu_tokens` prompt tokens (layer-major from an empty cache), weights
+    dequantised inside the timed region.  Scaled to the whole share: tokens/s =
+    tokens / (n_layer * seconds per layer)."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+    except Exception:
+        blas = []
+    n = min(args.cpu_tokens, w.n_prompt)
+    one = w.with_(n_layer=1)
+    note(f"cpu baseline: generating one {w.d_model}-wide layer and {n} input rows")
+    fp = {name: synth.layer_weight(one, 0, name, shape) for name, shape in synth.weight_shapes(one)}
+    ql = [oracle.quantize_layer(fp)]
+    del fp
+    x = synth.prompt_inputs(w, n)
+    m = oracle.OracleModel(one, ql)
+    t0 = time.perf_counter()
+    m.prefill_layer_major(x)
+    dt = time.perf_counter() - t0
+    threads = max([t for _, t in blas if t] or [os.cpu_count() or 1])
+    note(f"cpu baseline: {dt:.1f}s for one layer x {n} tokens")
+    return {"value": n / (w.n_layer * dt), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"1 of {w.n_layer} layers, first {n} prompt tokens, float64 NumPy, "
+                      f"weights dequantised in the timed region ({dt:.2f} s)",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas": blas}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="dense27b_f16")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--sweep-reps", type=int, default=5)
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the multi-GPU layer split is a design note, not part of this build)", flush=True)
+        sys.exit(2)
+    import torch
+    import chunked_prompt_prefill_amd as cpa
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", flush=True)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    w, res = run_main(args, torch, cpa, synth)
+    sweep = None
+    if not args.no_sweep:
+        sweep = run_sweep(args, torch, cpa, synth, fit_linear)
+    cpu = None if args.no_cpu else run_cpu_baseline(args, w)
+    line = {
+        "metric": "prefill tokens/s at chunk C and KV depth (1 GPU); fitted b, a per layer",
+        "value": res["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) q8_0 weights and hidden states)",
+        "config": {"workload": f"{w.name}: {w.n_layer}-layer share, d_model {w.d_model}, "
+                               f"{w.n_head}/{w.n_kv_head} heads, head_dim {w.head_dim}, "
+                               f"{'experts' if w.n_expert else 'SwiGLU ' + str(w.ffn_dim)}, "
+                               f"{w.kv_type} cache, {w.n_prompt}-token prompt in {w.chunk}-token chunks",
+                   "n_layer": w.n_layer, "prompt_tokens": w.n_prompt, "chunk": w.chunk,
+                   "kv_type": w.kv_type},
+        "roofline": res["roofline"],
+        "prompt_roofline": res["prompt_roofline"],
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

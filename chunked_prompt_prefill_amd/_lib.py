@@ -57,7 +57,7 @@ SIGNATURES = {
     "prefill_n_past": (c_i32, [c_vp]),
     "prefill_last_error": (ctypes.c_char_p, [c_vp]),
     "prefill_free": (None, [c_vp]),
-    "cp_kernel_timing": (ctypes.c_int, [c_vp, ctypes.c_int]),
+    "cp_kernel_timing": (ctypes.c_int, [c_vp, ctypes.c_char_p]),
     "cp_kernel_times": (ctypes.c_int, [c_vp, ctypes.c_char_p, ctypes.POINTER(c_f),
                                        ctypes.POINTER(c_i32)]),
     "cp_quantize_q8_0": (ctypes.c_int, [c_vp, c_i64, c_i32, c_i64, c_vp, c_vp]),

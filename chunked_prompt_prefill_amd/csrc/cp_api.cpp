@@ -289,6 +289,7 @@ struct cp_ctx {
   std::string err;
   // timing
   bool timing = false;
+  std::string timing_classes;   // comma-separated class names, or "*" for all
   struct Rec { std::string cls; hipEvent_t a, b; };
   std::vector<Rec> pending;
   std::vector<hipEvent_t> pool;
@@ -325,6 +326,10 @@ int hip_fail(cp_ctx* c, hipError_t e, const char* what) {
 template <typename F>
 hipError_t timed(cp_ctx* c, const char* cls, F&& launch) {
   if (!c->timing) return launch();
+  if (c->timing_classes != "*") {
+    const std::string key = std::string(",") + cls + ",";
+    if (("," + c->timing_classes + ",").find(key) == std::string::npos) return launch();
+  }
   hipEvent_t a = c->ev(), b = c->ev();
   if (!a || !b) return launch();
   hipEventRecord(a, c->stream);
@@ -687,13 +692,14 @@ void prefill_free(cp_ctx* c) {
   delete c;
 }
 
-int cp_kernel_timing(cp_ctx* c, int enable) {
+int cp_kernel_timing(cp_ctx* c, const char* classes) {
   if (!c) return CP_E_INVALID;
   CP_HIP(c, hipStreamSynchronize(c->stream), "stream sync");
   for (auto& r : c->pending) { c->pool.push_back(r.a); c->pool.push_back(r.b); }
   c->pending.clear();
   c->totals.clear();
-  c->timing = enable != 0;
+  c->timing = classes != nullptr;
+  c->timing_classes = classes ? classes : "";
   return CP_OK;
 }
 

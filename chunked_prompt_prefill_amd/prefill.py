@@ -127,8 +127,9 @@ class PrefillContext:
     def last_error(self) -> str:
         return self.L.prefill_last_error(self._ctx).decode()
 
-    def cp_kernel_timing(self, enable: bool):
-        self._check(self.L.cp_kernel_timing(self._ctx, int(enable)))
+    def cp_kernel_timing(self, classes: Optional[str]):
+        """None: off; "*": every class; else comma-separated class names."""
+        self._check(self.L.cp_kernel_timing(self._ctx, None if classes is None else classes.encode()))
 
     def cp_kernel_times(self, cls: str):
         ms, n = ctypes.c_float(), ctypes.c_int32()

@@ -164,13 +164,14 @@ int32_t prefill_n_past(const cp_ctx* ctx);
 const char* prefill_last_error(const cp_ctx* ctx);
 void prefill_free(cp_ctx* ctx);   /* releases host-side state only; buffers stay the caller's */
 
-/* Per-kernel timing.  With timing on, every launch of the named kernel class is
+/* Per-kernel timing.  classes: NULL turns timing off; "*" times every kernel class; else
+ * a comma-separated list of class names.  While on, every launch of a selected class is
  * bracketed by hipEvents on the context's stream; cp_kernel_times() synchronises and
- * returns the summed duration (ms) and launch count since the last reset.  Classes:
- * "gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attention", "rope_kv_append",
- * "rmsnorm", "moe_route", "moe_permute", "moe_gemm_gate_up", "moe_gemm_down",
- * "moe_unpermute", "splitk_reduce". */
-int cp_kernel_timing(cp_ctx* ctx, int enable);
+ * returns the summed duration (ms) and launch count since the last cp_kernel_timing()
+ * call.  Classes: "gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attention",
+ * "rope_kv_append", "rmsnorm", "moe_route", "moe_permute", "moe_gemm_gate_up",
+ * "moe_gemm_down", "moe_unpermute". */
+int cp_kernel_timing(cp_ctx* ctx, const char* classes);
 int cp_kernel_times(cp_ctx* ctx, const char* kernel_class, float* total_ms, int32_t* launches);
 
 /* q8_0 encode of float32 rows into the interchange layout, on the GPU (used to build
