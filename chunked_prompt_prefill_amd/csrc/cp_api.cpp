@@ -36,10 +36,11 @@ int64_t round_up(int64_t v, int64_t g) { return (v + g - 1) / g * g; }
 std::string validate(const cp_config* c) {
   if (!c) return "config is NULL";
   if (c->n_layer < 1) return "n_layer must be >= 1";
-  if (c->d_model < 64 || c->d_model % 64) return "d_model must be a positive multiple of 64";
+  if (c->d_model < 128 || c->d_model % 128) return "d_model must be a positive multiple of 128";
   if (c->head_dim != 64 && c->head_dim != 128) return "head_dim must be 64 or 128";
   if (c->n_kv_head < 1 || c->n_head < 1 || c->n_head % c->n_kv_head)
     return "n_head must be a positive multiple of n_kv_head";
+  if ((c->n_head * c->head_dim) % 128) return "n_head * head_dim must be a multiple of 128";
   if (c->n_head / c->n_kv_head > 64) return "n_head / n_kv_head must be <= 64";
   const bool moe = c->n_expert > 0;
   if (!moe && c->ffn_dim < 1) return "dense FFN needs ffn_dim >= 1";
@@ -67,7 +68,7 @@ Dims dims_of(const cp_config* c) {
   D.G = D.Hq / D.Hkv; D.F = c->ffn_dim; D.E = c->n_expert; D.k = c->n_expert_used;
   D.Fe = c->expert_ffn_dim; D.moe = D.E > 0; D.kv_type = c->kv_type;
   D.Nqkv = (D.Hq + 2 * D.Hkv) * D.hd; D.Dq = D.Hq * D.hd;
-  D.Fp = (int)round_up(D.F, 64); D.Fep = (int)round_up(D.Fe, 64);
+  D.Fp = (int)round_up(D.F, 128); D.Fep = (int)round_up(D.Fe, 128);
   D.n_ctx = (int)round_up(c->n_ctx_max, 64);
   D.Cm = c->n_chunk_max;
   return D;
@@ -76,17 +77,75 @@ Dims dims_of(const cp_config* c) {
 // --------------------------------------------------------------------------------------
 // Launch policies
 // --------------------------------------------------------------------------------------
-int gemm_mt(int M) { return M <= 64 ? 64 : (M <= 128 ? 128 : 256); }
+// 128-row tiles run two workgroups per CU (two waves per SIMD hide each other's load
+// and dequantisation latency); measured faster than 256-row tiles at one per CU.
+int gemm_mt(int M) { return M <= 64 ? 64 : 128; }
 
-int gemm_splits(int M, int N, int K) {
-  const int mt = gemm_mt(M);
-  const int64_t tiles = ceil_div(M, mt) * ceil_div(N, 256);
-  const int ks = K / 64;
-  if (tiles >= 192) return 1;
-  int s = (int)ceil_div(256, tiles);
-  s = std::min(s, std::max(1, ks / 4));
-  s = std::min(s, 16);
-  return std::max(s, 1);
+constexpr int g_cus = 256;   // compute units of an MI355X; plans and workspace sizes use it
+// workgroups resident per CU for a row tile (the 256-row tile takes all of LDS)
+inline int wg_per_cu(int mt) { return mt >= 256 ? 1 : 2; }
+
+// A GEMM call runs as one or two launches over column ranges: the tiles that fill whole
+// rounds of the chip run unsplit, and (optionally) a tail of whole 256-column tiles runs
+// with split-K so that it fills the chip too.  The plan minimises a simple time model:
+// rounds of workgroups x stages per workgroup, plus the partial-sum traffic and an extra
+// launch for any split.
+struct GemmPart { int n0, n1, splits; };
+struct GemmPlan {
+  int mt = 256, nparts = 0;
+  GemmPart part[2];
+  size_t partial_bytes = 0;
+};
+
+GemmPlan plan_gemm(int M, int N, int K, int force_splits = 0) {
+  GemmPlan p;
+  p.mt = gemm_mt(M);
+  const int64_t Mt = ceil_div(M, p.mt), Nt = ceil_div(N, 256), KS = K / 128, T = Mt * Nt;
+  const int slots = g_cus * wg_per_cu(p.mt);
+  // one K stage of a tile, with wg_per_cu tiles sharing a CU
+  const double t_stage = 2.0 * p.mt * 256 * 128 * wg_per_cu(p.mt) / (9.77e12 * 0.6);
+  const double launch = 4e-6;
+  auto red = [&](int64_t S, int64_t cols) { return (double)(S + 1) * M * cols * 4 / 5e12 + launch; };
+  auto rounds = [&](int64_t wgs) { return (double)ceil_div(wgs, slots); };
+  if (force_splits > 0) {
+    const int S = (int)std::min<int64_t>(force_splits, KS);
+    p.nparts = 1;
+    p.part[0] = {0, N, S};
+    p.partial_bytes = S > 1 ? (size_t)S * M * N * 4 : 0;
+    return p;
+  }
+  double best = rounds(T) * KS * t_stage;
+  p.nparts = 1;
+  p.part[0] = {0, N, 1};
+  for (int64_t S = 2; S <= std::min<int64_t>(16, KS); ++S) {
+    const double c = rounds(T * S) * ceil_div(KS, S) * t_stage + red(S, N);
+    if (c < best) {
+      best = c;
+      p.nparts = 1;
+      p.part[0] = {0, N, (int)S};
+    }
+  }
+  if (T > slots) {
+    const int64_t Nf = (T / slots) * slots / Mt;
+    if (Nf > 0 && Nf < Nt) {
+      const int64_t R = Mt * (Nt - Nf);
+      const int64_t cols = N - Nf * 256;
+      for (int64_t S = 2; S <= std::min<int64_t>(16, KS); ++S) {
+        const double c = rounds(Mt * Nf) * KS * t_stage + rounds(R * S) * ceil_div(KS, S) * t_stage +
+                         red(S, cols);
+        if (c < best) {
+          best = c;
+          p.nparts = 2;
+          p.part[0] = {0, (int)(Nf * 256), 1};
+          p.part[1] = {(int)(Nf * 256), N, (int)S};
+        }
+      }
+    }
+  }
+  for (int i = 0; i < p.nparts; ++i)
+    if (p.part[i].splits > 1)
+      p.partial_bytes = std::max(p.partial_bytes, (size_t)p.part[i].splits * M * (p.part[i].n1 - p.part[i].n0) * 4);
+  return p;
 }
 
 int attn_splits(const Dims& D, int n, int start) {
@@ -160,10 +219,7 @@ size_t max_partial_bytes(const Dims& D) {
   const int Ks[4] = {D.d, D.Dq, D.d, D.moe ? 0 : D.Fp};
   for (int g = 0; g < 4; ++g) {
     if (!Ns[g] || !Ks[g]) continue;
-    for (int M = 1; M <= D.Cm; ++M) {
-      const int s = gemm_splits(M, Ns[g], Ks[g]);
-      if (s > 1) best = std::max(best, (size_t)s * M * Ns[g] * 4);
-    }
+    for (int M = 1; M <= D.Cm; ++M) best = std::max(best, plan_gemm(M, Ns[g], Ks[g]).partial_bytes);
   }
   return best;
 }
@@ -341,13 +397,19 @@ hipError_t timed(cp_ctx* c, const char* cls, F&& launch) {
 
 hipError_t gemm(cp_ctx* c, const char* cls, const __bf16* A, int lda, int M, const QMat& W,
                 int mode, void* out, int ldo) {
-  GemmArgs g;
-  g.A = A; g.lda = lda; g.M = M; g.N = W.N; g.K = W.K;
-  g.wq = W.q; g.wd = W.d; g.mode = mode; g.out = out; g.ldo = ldo;
-  g.splits = gemm_splits(M, W.N, W.K);
-  g.partial = c->wsp<float>(c->WS.partial);
-  const int mt = gemm_mt(M);
-  return timed(c, cls, [&] { return launch_gemm(g, 0, mt, c->stream); });
+  const GemmPlan p = plan_gemm(M, W.N, W.K);
+  return timed(c, cls, [&] {
+    for (int i = 0; i < p.nparts; ++i) {
+      GemmArgs g;
+      g.A = A; g.lda = lda; g.M = M; g.N = p.part[i].n1; g.K = W.K; g.n0 = p.part[i].n0;
+      g.wq = W.q; g.wd = W.d; g.mode = mode; g.out = out; g.ldo = ldo;
+      g.splits = p.part[i].splits;
+      g.partial = c->wsp<float>(c->WS.partial);
+      const hipError_t e = launch_gemm(g, 0, p.mt, c->stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  });
 }
 
 int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int start) {
@@ -774,14 +836,14 @@ int cp_test_router(const float* y, const void* w_router, int32_t n, int32_t d, i
 }
 
 size_t cp_test_gemm_scratch_bytes(int32_t M, int32_t N, int32_t K, int32_t splits) {
-  if (M < 1 || N < 32 || N % 32 || K < 64 || K % 64) return 0;
-  const int s = splits > 0 ? splits : gemm_splits(M, N, K);
-  return align_up(QMat::q_bytes(N, K)) + align_up(QMat::d_bytes(N, K)) + align_up((size_t)s * M * N * 4);
+  if (M < 1 || N < 32 || N % 32 || K < 128 || K % 128) return 0;
+  const GemmPlan p = plan_gemm(M, N, K, splits);
+  return align_up(QMat::q_bytes(N, K)) + align_up(QMat::d_bytes(N, K)) + align_up(p.partial_bytes + 4);
 }
 
 int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
                  int32_t splits, void* out, void* scratch, void* stream) {
-  if (!A || !W || !out || !scratch || M < 1 || N < 32 || N % 32 || K < 64 || K % 64 || mode < 0 || mode > 2)
+  if (!A || !W || !out || !scratch || M < 1 || N < 32 || N % 32 || K < 128 || K % 128 || mode < 0 || mode > 2)
     return CP_E_INVALID;
   if (mode == GM_SWIGLU && N % 64) return CP_E_INVALID;
   hipStream_t s = (hipStream_t)stream;
@@ -799,13 +861,28 @@ int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, 
     e = launch_repack_q8_0(W, nullptr, N, K, 0, N, 0, q, s);
   }
   if (e != hipSuccess) return CP_E_DEVICE;
-  GemmArgs g;
-  g.A = (const __bf16*)A; g.lda = K; g.M = M; g.N = N; g.K = K; g.wq = q.q; g.wd = q.d;
-  g.mode = mode; g.out = out; g.ldo = mode == GM_SWIGLU ? N / 2 : N;
-  g.splits = splits > 0 ? splits : gemm_splits(M, N, K);
-  g.splits = std::min(g.splits, K / 64);
-  g.partial = partial;
-  return launch_gemm(g, 0, gemm_mt(M), s) == hipSuccess ? CP_OK : CP_E_DEVICE;
+  const GemmPlan p = plan_gemm(M, N, K, splits);
+  for (int i = 0; i < p.nparts; ++i) {
+    GemmArgs g;
+    g.A = (const __bf16*)A; g.lda = K; g.M = M; g.N = p.part[i].n1; g.K = K; g.n0 = p.part[i].n0;
+    g.wq = q.q; g.wd = q.d;
+    g.mode = mode; g.out = out; g.ldo = mode == GM_SWIGLU ? N / 2 : N;
+    g.splits = p.part[i].splits;
+    g.partial = partial;
+    if (launch_gemm(g, 0, p.mt, s) != hipSuccess) return CP_E_DEVICE;
+  }
+  return CP_OK;
+}
+
+int cp_test_gemm_plan(int32_t M, int32_t N, int32_t K, int32_t* out6) {
+  if (!out6 || M < 1 || N < 32 || K < 128) return CP_E_INVALID;
+  const GemmPlan p = plan_gemm(M, N, K);
+  out6[0] = p.mt; out6[1] = p.nparts;
+  for (int i = 0; i < 2; ++i) {
+    out6[2 + 2 * i] = i < p.nparts ? p.part[i].n0 : 0;
+    out6[3 + 2 * i] = i < p.nparts ? p.part[i].splits : 0;
+  }
+  return CP_OK;
 }
 
 size_t cp_test_attention_scratch_bytes(int32_t n, int32_t n_head, int32_t head_dim, int32_t kv_splits) {

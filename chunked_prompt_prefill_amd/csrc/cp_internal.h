@@ -17,12 +17,12 @@ __host__ __device__ inline size_t align_up(size_t v, size_t a = kAlign) { return
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // --------------------------------------------------------------------------------------
-// Repacked q8_0 matrix [N][K] (N % 32 == 0, K % 64 == 0).
+// Repacked q8_0 matrix [N][K] (N % 32 == 0, K % 128 == 0).
 //   q: int8, for every 32-row group n32 and 32-column block kb, 1 KiB laid out in MFMA
 //      lane order: lane l (row n32*32 + l%32) holds bytes 16*(l/32) .. +15 of that
 //      row's block -> offset ((n32*KB + kb)*64 + l)*16.
-//   d: fp16 scales, two per u32: for 32-row group n32 and block pair kp (blocks 2kp and
-//      2kp+1) -> u32 index (n32*KP + kp)*32 + row%32.
+//   d: fp16 scales, four per 8 bytes: for 32-row group n32 and block quad kq (blocks
+//      4kq .. 4kq+3) -> fp16 index ((n32*KQ + kq)*32 + row%32)*4 + kb%4.
 // --------------------------------------------------------------------------------------
 struct QMat {
   int8_t* q = nullptr;
@@ -43,19 +43,20 @@ struct GemmArgs {
   const uint32_t* wd = nullptr;
   int64_t wq_estride = 0, wd_estride = 0;   // grouped: per-expert strides (elements)
   int32_t M = 0, N = 0, K = 0;
+  int32_t n0 = 0;                     // first output column of this launch (N = end)
   const int32_t* tiles = nullptr;     // grouped: [max_tiles][4] {expert, m0, m1, 0}
   const int32_t* n_tiles = nullptr;   // grouped: device count of valid tiles
   int32_t mode = GM_F32;
   void* out = nullptr;
   int32_t ldo = 0;
-  float* partial = nullptr;           // split-K partial sums [splits][M][N]
+  float* partial = nullptr;           // split-K partial sums [splits][M][N - n0]
   int32_t splits = 1;
 };
 
 // Kernel launchers (return hipError_t of the launch).
 hipError_t launch_gemm(const GemmArgs& a, int grid_m_tiles, int mt, hipStream_t s);
-hipError_t launch_splitk_reduce(const float* partial, int32_t splits, int32_t M, int32_t N,
-                                int32_t mode, void* out, int32_t ldo, hipStream_t s);
+hipError_t launch_splitk_reduce(const float* partial, int32_t splits, int32_t M, int32_t n0,
+                                int32_t N, int32_t mode, void* out, int32_t ldo, hipStream_t s);
 // Repack interchange q8_0 rows into a QMat.  mode 0: destination rows dst_row0 ..
 // dst_row0+dst_rows-1 take source rows 0 .. (rows >= src_rows are zero).  mode 1 (gate/up
 // interleave for the SwiGLU epilogue): destination row n = 64*g + 32*w + i takes row

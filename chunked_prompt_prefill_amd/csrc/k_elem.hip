@@ -15,7 +15,7 @@ __global__ void repack_kernel(const uint8_t* __restrict__ src0, const uint8_t* _
                               int64_t src_rows, int32_t nb_src, int64_t dst_row0, int64_t dst_rows,
                               int32_t mode, int8_t* __restrict__ dq, uint16_t* __restrict__ dd,
                               int32_t K) {
-  const int KB = K / QK, KP = K / 64;
+  const int KB = K / QK, KQ = K / 128;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= dst_rows * KB) return;
   const int64_t nl = i / KB;
@@ -46,7 +46,7 @@ __global__ void repack_kernel(const uint8_t* __restrict__ src0, const uint8_t* _
   uint4* q = reinterpret_cast<uint4*>(dq);
   q[(n32 * KB + kb) * 64 + r] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
   q[(n32 * KB + kb) * 64 + 32 + r] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
-  dd[((n32 * KP + kb / 2) * 32 + r) * 2 + (kb & 1)] = dbits;
+  dd[((n32 * KQ + kb / 4) * 32 + r) * 4 + (kb & 3)] = dbits;
 }
 
 hipError_t launch_repack_q8_0(const void* src0, const void* src1, int64_t src_rows, int32_t k_src,

@@ -4,18 +4,25 @@
 //
 // Tiling.  A workgroup of 4 waves owns an MT x 256 output tile (MT = 32*MI); each wave
 // owns 64 columns (two 32-column MFMA blocks) across all MT rows, so every weight
-// element is dequantised exactly once per workgroup.  Per 64-wide K stage:
-//   * A: MT x 64 bf16 staged in LDS (double buffered, 16-byte chunks XOR-swizzled by
-//     row), read as the MFMA A operand by all four waves;
-//   * W: loaded straight into registers from the repacked layout (1 KiB contiguous per
-//     wave per 32-row group and 32-column block, already in MFMA lane order), dequantised
-//     in registers (d*q exact in fp32, rounded to bf16) as the MFMA B operand.
+// element is dequantised exactly once per workgroup.  Per 128-wide K stage (4 q8_0
+// blocks):
+//   * A: MT x 128 bf16 staged in LDS by asynchronous global->LDS loads (16 bytes per
+//     lane, landing in lane order), double buffered; the 16-byte chunks of a row are
+//     XOR-swizzled by the row so the 32 rows an MFMA operand spans hit distinct banks.
+//     The swizzle is applied by choosing each lane's source address.
+//   * W: loaded straight into registers one stage ahead from the repacked layout (1 KiB
+//     contiguous per wave per 32-row group and block, already in MFMA lane order),
+//     dequantised in registers (d*q exact in fp32, rounded to bf16) as the B operand.
 // The K index inside a q8_0 block is permuted consistently on both operands so that a
 // lane's 16 weight bytes are contiguous: lane half h, MFMA step s, element c <-> block
 // column 16h + 8s + c.
+// Rows beyond M and columns beyond N are computed from clamped (valid) addresses and
+// simply not stored, so the main loop has no branches.
 // Epilogues: fp32 store, fp32 residual add, SwiGLU (gate/up columns interleaved in
-// 32-column groups) to bf16, or split-K partials reduced by a separate kernel in a
-// fixed order (deterministic: no float atomics).
+// 32-column groups) to bf16, or split-K partials summed by a separate kernel in split
+// order (deterministic: no float atomics).  A launch may cover a column range [n0, N)
+// so that the host can run the tiles that fill whole rounds of the chip without
+// splitting and split only the tail.
 // Grouped mode (routed experts): the row tile comes from a device tile table
 // {expert, m0, m1}; A rows may be gathered through an index array.
 #include "cp_internal.h"
@@ -23,18 +30,42 @@
 
 namespace cp {
 
-constexpr int KT = 64;
+constexpr int KT = 128;
 constexpr int NT = 256;
+constexpr int CPR = KT * 2 / 16;   // 16-byte chunks per A row per stage
+
+typedef __attribute__((address_space(1))) const void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// Loads through global (address space 1) pointers: the pointers come from a struct
+// argument, so without this the compiler would emit flat loads.
+__device__ __forceinline__ uint4 gload(const uint4* p) {
+  const u32x4_t v = *(const __attribute__((address_space(1))) u32x4_t*)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 gload(const uint2* p) {
+  const u32x2_t v = *(const __attribute__((address_space(1))) u32x2_t*)(p);
+  return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+template <int MI>
+struct MinBlocks { static constexpr int v = MI >= 8 ? 1 : 2; };
 
 template <int MI, int MODE, bool GROUPED>
-__global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256, MinBlocks<MI>::v) void gemm_q8_kernel(GemmArgs g) {
   constexpr int MT = MI * 32;
-  constexpr int CHUNKS = MT * 8;           // 16-byte chunks per stage (8 per row)
-  constexpr int LOADS = CHUNKS / 256;      // per thread
-  __shared__ uint4 sA[2][CHUNKS];
+  constexpr int NCH = MT * CPR;      // 16-byte chunks per stage
+  constexpr int JPW = NCH / 256;     // async A loads per thread per stage
+  __shared__ uint4 sA[2][NCH];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const int KS = g.K / KT;
 
@@ -52,7 +83,7 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs g) {
     // XCD-aware order: workgroup i runs on XCD i % 8; give each XCD a contiguous range
     // of logical tiles (row tiles fastest) so tiles sharing weight columns share an L2.
     const int mtiles = (int)ceil_div(g.M, MT);
-    const int ntiles = (int)ceil_div(g.N, NT);
+    const int ntiles = (int)ceil_div(g.N - g.n0, NT);
     const int total = mtiles * ntiles * g.splits;
     const int i = blockIdx.x;
     const int xcd = i & 7, idx = i >> 3;
@@ -68,60 +99,46 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs g) {
 
   const int ks0 = (int)((int64_t)split * KS / g.splits);
   const int ks1 = (int)((int64_t)(split + 1) * KS / g.splits);
-  const int n_wave = ntile * NT + wave * 64;
+  const int n_wave = g.n0 + ntile * NT + wave * 64;
   const bool col_ok0 = n_wave < g.N;
   const bool col_ok1 = n_wave + 32 < g.N;
 
-  // Per-thread A rows: row i*32 + tid/8, chunk tid%8.
-  const __bf16* arow[LOADS];
+  // A: async load j of wave w fills physical chunks [(4j + w)*64, +64) of a stage; lane L
+  // lands on row r = 16j + 4w + L/16, physical chunk L%16, which holds logical chunk
+  // (L%16) ^ (r%16) = (L%16) ^ (4w + L/16).
+  const int rsub = 4 * wave + (lane >> 4);
+  const int lchunk = (lane & 15) ^ rsub;
+  int32_t aoff[JPW];
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int r = i * 32 + (tid >> 3);
-    if (r < rows) {
-      int64_t pr = m0 + r;
-      if (g.a_rows) pr = g.a_rows[m0 + r] / g.a_row_div;
-      arow[i] = g.A + pr * g.lda + (tid & 7) * 8;
-    } else {
-      arow[i] = nullptr;
-    }
+  for (int j = 0; j < JPW; ++j) {
+    const int r = min(16 * j + rsub, rows - 1);
+    int32_t pr = m0 + r;
+    if (g.a_rows) pr = g.a_rows[m0 + r] / g.a_row_div;
+    aoff[j] = pr * g.lda + lchunk * 8;
   }
+  auto issue_a = [&](int ks, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < JPW; ++j)
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(g.A + aoff[j] + ks * KT),
+                                       (lvoid_t*)&sA[buf][(4 * j + wave) * 64], 16, 0, 0);
+  };
 
-  const int KB = g.K / QK, KP = g.K / KT;
+  const int KB = g.K / QK, KQ = g.K / KT;
+  const int last32 = g.N / 32 - 1;
   const uint4* bq[2];
-  const uint32_t* bd[2];
+  const uint2* bd[2];
 #pragma unroll
   for (int ni = 0; ni < 2; ++ni) {
-    const int64_t n32 = (n_wave >> 5) + ni;
+    const int64_t n32 = min((n_wave >> 5) + ni, last32);
     bq[ni] = reinterpret_cast<const uint4*>(g.wq + expert * g.wq_estride) + n32 * KB * 64 + lane;
-    bd[ni] = g.wd + expert * g.wd_estride + n32 * KP * 32 + l32;
+    bd[ni] = reinterpret_cast<const uint2*>(g.wd + expert * g.wd_estride) + n32 * KQ * 32 + l32;
   }
-
-  uint4 ra[LOADS];
-  uint4 rb[2][2];
-  uint32_t rs[2];
-  auto load_stage = [&](int ks) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      ra[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + ks * KT) : make_uint4(0, 0, 0, 0);
+  auto load_b = [&](int ks, uint4 (&rb)[2][4], uint2 (&rs)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
-      const bool ok = ni ? col_ok1 : col_ok0;
-      if (ok) {
-        rb[ni][0] = bq[ni][(2 * ks) * 64];
-        rb[ni][1] = bq[ni][(2 * ks + 1) * 64];
-        rs[ni] = bd[ni][ks * 32];
-      } else {
-        rb[ni][0] = rb[ni][1] = make_uint4(0, 0, 0, 0);
-        rs[ni] = 0;
-      }
-    }
-  };
-  auto store_stage = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int r = i * 32 + (tid >> 3);
-      const int c = tid & 7;
-      sA[buf][r * 8 + (c ^ (r & 7))] = ra[i];
+      for (int kb = 0; kb < 4; ++kb) rb[ni][kb] = gload(bq[ni] + (4 * ks + kb) * 64);
+      rs[ni] = gload(bd[ni] + ks * 32);
     }
   };
 
@@ -133,48 +150,61 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
 
-  if (ks0 < ks1) {
-    load_stage(ks0);
-    store_stage(0);
-  }
-  __syncthreads();
-
-  for (int ks = ks0; ks < ks1; ++ks) {
-    const int cur = (ks - ks0) & 1;
-    uint4 cb[2][2] = {{rb[0][0], rb[0][1]}, {rb[1][0], rb[1][1]}};
-    uint32_t cs[2] = {rs[0], rs[1]};
-    const bool more = ks + 1 < ks1;
-    if (more) load_stage(ks + 1);
+  auto compute = [&](int buf, const uint4 (&rb)[2][4], const uint2 (&rs)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kbl = 0; kbl < 2; ++kbl) {
+    for (int kb = 0; kb < 4; ++kb) {
       uint4 b[2][2];
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
-        const float d = half_bits_to_float(kbl ? (cs[ni] >> 16) : (cs[ni] & 0xFFFFu));
-        dequant16_bf16(cb[ni][kbl], d, b[ni][0], b[ni][1]);
+        const uint32_t pair = (kb < 2) ? rs[ni].x : rs[ni].y;
+        const float d = half_bits_to_float((kb & 1) ? (pair >> 16) : (pair & 0xFFFFu));
+        dequant16_bf16(rb[ni][kb], d, b[ni][0], b[ni][1]);
       }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
-          const int r = mi * 32 + l32;
-          const int c = kbl * 4 + 2 * h + s;
-          const uint4 a = sA[cur][r * 8 + (c ^ (r & 7))];
+          const int c = kb * 4 + 2 * h + s;
+          const uint4 a = sA[buf][(mi * 32 + l32) * CPR + (c ^ (l32 & 15))];
           const bf16x8 av = __builtin_bit_cast(bf16x8, a);
-          if (col_ok0)
-            acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                av, __builtin_bit_cast(bf16x8, b[0][s]), acc[mi][0], 0, 0, 0);
-          if (col_ok1)
-            acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                av, __builtin_bit_cast(bf16x8, b[1][s]), acc[mi][1], 0, 0, 0);
+          acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, b[0][s]),
+                                                               acc[mi][0], 0, 0, 0);
+          acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, b[1][s]),
+                                                               acc[mi][1], 0, 0, 0);
         }
       }
     }
-    if (more) store_stage(cur ^ 1);
-    __syncthreads();
+  };
+
+  if (ks0 < ks1) {
+    uint4 rb0[2][4], rb1[2][4];
+    uint2 rs0[2], rs1[2];
+    issue_a(ks0, 0);
+    load_b(ks0, rb0, rs0);
+    int ks = ks0;
+    for (; ks + 1 < ks1; ks += 2) {
+      wait_vm0();
+      __syncthreads();                 // stage ks in LDS (all waves); buffer 1 free
+      issue_a(ks + 1, 1);
+      load_b(ks + 1, rb1, rs1);
+      compute(0, rb0, rs0);
+      wait_vm0();
+      __syncthreads();                 // stage ks+1 in LDS; buffer 0 free
+      if (ks + 2 < ks1) {
+        issue_a(ks + 2, 0);
+        load_b(ks + 2, rb0, rs0);
+      }
+      compute(1, rb1, rs1);
+    }
+    if (ks < ks1) {                    // odd number of stages: the last one is in buffer 0
+      wait_vm0();
+      __syncthreads();
+      compute(0, rb0, rs0);
+    }
   }
 
   // Epilogue.  acc[mi][ni][e]: row mi*32 + 8*(e/4) + 4*h + e%4, column n_wave + 32*ni + l32.
+  const int pn = g.N - g.n0;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -199,7 +229,7 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs g) {
             float* p = reinterpret_cast<float*>(g.out) + row * g.ldo + col;
             *p = *p + v;
           } else {
-            g.partial[((int64_t)split * g.M + row) * g.N + col] = v;
+            g.partial[((int64_t)split * g.M + row) * pn + (col - g.n0)] = v;
           }
         }
       }
@@ -207,41 +237,43 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_kernel(GemmArgs g) {
   }
 }
 
-// Sum split-K partials in split order and apply the epilogue.  One thread per 4 output
-// columns (SwiGLU: 4 gate/up pairs).
+// Sum split-K partials of columns [n0, N) in split order and apply the epilogue.  One
+// thread per 4 output columns (SwiGLU: 4 gate/up pairs).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
-                                                            int32_t splits, int32_t M, int32_t N,
-                                                            int32_t mode, void* out, int32_t ldo) {
-  const int64_t ncols = (mode == GM_SWIGLU) ? N / 2 : N;
+                                                            int32_t splits, int32_t M, int32_t n0,
+                                                            int32_t N, int32_t mode, void* out,
+                                                            int32_t ldo) {
+  const int64_t pn = N - n0;
+  const int64_t ncols = (mode == GM_SWIGLU) ? pn / 2 : pn;
   const int64_t quads = ncols / 4;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)M * quads) return;
   const int64_t row = i / quads;
   const int64_t c4 = (i % quads) * 4;
-  const int64_t plane = (int64_t)M * N;
+  const int64_t plane = (int64_t)M * pn;
   if (mode == GM_SWIGLU) {
     const int64_t gc = (c4 / 32) * 64 + (c4 % 32);
-    float4 gs = *reinterpret_cast<const float4*>(partial + row * N + gc);
-    float4 us = *reinterpret_cast<const float4*>(partial + row * N + gc + 32);
+    float4 gs = *reinterpret_cast<const float4*>(partial + row * pn + gc);
+    float4 us = *reinterpret_cast<const float4*>(partial + row * pn + gc + 32);
     for (int s = 1; s < splits; ++s) {
-      const float4 a = *reinterpret_cast<const float4*>(partial + s * plane + row * N + gc);
-      const float4 b = *reinterpret_cast<const float4*>(partial + s * plane + row * N + gc + 32);
+      const float4 a = *reinterpret_cast<const float4*>(partial + s * plane + row * pn + gc);
+      const float4 b = *reinterpret_cast<const float4*>(partial + s * plane + row * pn + gc + 32);
       gs.x += a.x; gs.y += a.y; gs.z += a.z; gs.w += a.w;
       us.x += b.x; us.y += b.y; us.z += b.z; us.w += b.w;
     }
-    __bf16* o = reinterpret_cast<__bf16*>(out) + row * ldo + c4;
+    __bf16* o = reinterpret_cast<__bf16*>(out) + row * ldo + n0 / 2 + c4;
     o[0] = (__bf16)(silu(gs.x) * us.x);
     o[1] = (__bf16)(silu(gs.y) * us.y);
     o[2] = (__bf16)(silu(gs.z) * us.z);
     o[3] = (__bf16)(silu(gs.w) * us.w);
     return;
   }
-  float4 acc = *reinterpret_cast<const float4*>(partial + row * N + c4);
+  float4 acc = *reinterpret_cast<const float4*>(partial + row * pn + c4);
   for (int s = 1; s < splits; ++s) {
-    const float4 a = *reinterpret_cast<const float4*>(partial + s * plane + row * N + c4);
+    const float4 a = *reinterpret_cast<const float4*>(partial + s * plane + row * pn + c4);
     acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
   }
-  float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + row * ldo + c4);
+  float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + row * ldo + n0 + c4);
   if (mode == GM_F32_ADD) {
     const float4 x = *o;
     acc.x = x.x + acc.x; acc.y = x.y + acc.y; acc.z = x.z + acc.z; acc.w = x.w + acc.w;
@@ -251,7 +283,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 template <int MI, bool GROUPED>
 static hipError_t launch_mode(const GemmArgs& a, int grid_m_tiles, hipStream_t s) {
-  const int ntiles = (int)ceil_div(a.N, NT);
+  const int ntiles = (int)ceil_div(a.N - a.n0, NT);
   dim3 grid, block(256);
   if (GROUPED) {
     grid = dim3(grid_m_tiles, ntiles);
@@ -269,7 +301,7 @@ static hipError_t launch_mode(const GemmArgs& a, int grid_m_tiles, hipStream_t s
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int grid_m_tiles, int mt, hipStream_t s) {
-  if (a.M <= 0) return hipSuccess;
+  if (a.M <= 0 || a.N <= a.n0) return hipSuccess;
   const bool grouped = a.tiles != nullptr;
   hipError_t e;
   if (grouped) {
@@ -282,15 +314,16 @@ hipError_t launch_gemm(const GemmArgs& a, int grid_m_tiles, int mt, hipStream_t 
   else if (mt == 128) e = launch_mode<4, false>(a, 0, s);
   else e = launch_mode<8, false>(a, 0, s);
   if (e != hipSuccess || a.splits <= 1) return e;
-  return launch_splitk_reduce(a.partial, a.splits, a.M, a.N, a.mode, a.out, a.ldo, s);
+  return launch_splitk_reduce(a.partial, a.splits, a.M, a.n0, a.N, a.mode, a.out, a.ldo, s);
 }
 
-hipError_t launch_splitk_reduce(const float* partial, int32_t splits, int32_t M, int32_t N,
-                                int32_t mode, void* out, int32_t ldo, hipStream_t s) {
-  const int64_t ncols = (mode == GM_SWIGLU) ? N / 2 : N;
+hipError_t launch_splitk_reduce(const float* partial, int32_t splits, int32_t M, int32_t n0,
+                                int32_t N, int32_t mode, void* out, int32_t ldo, hipStream_t s) {
+  const int64_t pn = N - n0;
+  const int64_t ncols = (mode == GM_SWIGLU) ? pn / 2 : pn;
   const int64_t work = (int64_t)M * (ncols / 4);
   const unsigned blocks = (unsigned)ceil_div(work, 256);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, partial, splits, M, N,
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, partial, splits, M, n0, N,
                      mode, out, ldo);
   return hipGetLastError();
 }

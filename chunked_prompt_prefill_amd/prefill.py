@@ -201,6 +201,15 @@ def cp_test_gemm(A, W, M, N, K, mode, splits, out):
         raise PrefillError(rc, "cp_test_gemm failed")
 
 
+def cp_test_gemm_plan(M, N, K):
+    """(row tile, [(first column, split-K factor), ...]) of the layer's launch plan."""
+    out = (ctypes.c_int32 * 6)()
+    rc = lib().cp_test_gemm_plan(M, N, K, out)
+    if rc != CP_OK:
+        raise PrefillError(rc, "cp_test_gemm_plan failed")
+    return out[0], [(out[2 + 2 * i], out[3 + 2 * i]) for i in range(out[1])]
+
+
 def cp_test_attention(q, kv, n, start, n_head, n_kv_head, head_dim, kv_type, n_ctx, kv_splits, out):
     L = lib()
     scratch = torch.empty(L.cp_test_attention_scratch_bytes(n, n_head, head_dim, kv_splits),

@@ -218,14 +218,19 @@ int cp_test_router(const float* y, const void* w_router, int32_t n, int32_t d, i
                    int32_t k, float* logits, int32_t* idx, float* weight, void* scratch,
                    void* hip_stream);
 
-/* One q8_0 GEMM as the layer runs it: out = A * W^T with A bf16 [M][K] (lda = K),
- * W in the interchange layout [N][K].  mode 0: out float32 [M][N] = result;
- * mode 1: out float32 [M][N] += result; mode 2 (SwiGLU): W holds gate rows then up rows
- * ([2F][K], F % 32 == 0) and out is bf16 [M][F] = silu(gate) * up.  splits > 1 forces
- * split-K with a deterministic reduction (0 = the library's own choice).  scratch: dev
+/* One q8_0 GEMM as the layer runs it: out = A * W^T with A bf16 [M][K] (lda = K,
+ * K % 128 == 0), W in the interchange layout [N][K] (N % 32 == 0).  mode 0: out float32
+ * [M][N] = result; mode 1: out float32 [M][N] += result; mode 2 (SwiGLU): W holds gate rows
+ * then up rows ([2F][K], F % 32 == 0) and out is bf16 [M][F] = silu(gate) * up.  splits > 0
+ * forces one launch with that split-K factor and a deterministic reduction (0 = the
+ * layer's own launch plan, cp_test_gemm_plan).  scratch: dev
  * buffer of cp_test_gemm_scratch_bytes(M, N, K, splits) bytes (repacked weights and
  * partial sums). */
 size_t cp_test_gemm_scratch_bytes(int32_t M, int32_t N, int32_t K, int32_t splits);
+/* The launch plan the layer uses for an M x N x K GEMM (host only): out6 = {row tile,
+ * number of launches, first column of launch 0, its split-K factor, first column of
+ * launch 1, its split-K factor}. */
+int cp_test_gemm_plan(int32_t M, int32_t N, int32_t K, int32_t* out6);
 int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
                  int32_t splits, void* out, void* scratch, void* hip_stream);
 

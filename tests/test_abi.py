@@ -63,7 +63,7 @@ def test_invalid_configs_are_rejected(cpa, field, value):
 
 def test_state_header_check_matches_oracle_blobs(cpa):
     from model_inputs import TINY_DENSE, q8_layers
-    w = synth.Workload("abi_state", 2, 64, 4, 2, 64, 64, kv_type="q8_0")
+    w = synth.Workload("abi_state", 2, 128, 4, 2, 64, 64, kv_type="q8_0")
     m = oracle.OracleModel(w, q8_layers(w))
     cache = m.new_cache(32)
     m.prefill(synth.prompt_inputs(w, 9), 4, cache=cache)

@@ -98,11 +98,12 @@ def bf16_round(torch, a: np.ndarray) -> np.ndarray:
 
 
 @pytest.mark.parametrize("M,N,K,splits", [(1, 256, 256, 0), (57, 512, 256, 0), (128, 5120, 512, 0),
-                                          (300, 768, 2048, 1), (300, 768, 2048, 3), (513, 1024, 704, 0),
-                                          (64, 7168, 5120, 0), (1000, 256, 17408, 0)])
+                                          (300, 768, 2048, 1), (300, 768, 2048, 3), (513, 1024, 768, 0),
+                                          (64, 7168, 5120, 0), (1000, 256, 17408, 0),
+                                          (512, 7168, 5120, 0), (2048, 5120, 5120, 0)])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_gemm_q8_0_within_bf16_bound(torch, cpa, M, N, K, splits, mode):
-    log(f"gemm M={M} N={N} K={K} splits={splits} mode={mode}")
+    log(f"gemm M={M} N={N} K={K} splits={splits} mode={mode} plan={cpa.cp_test_gemm_plan(M, N, K)}")
     A = bf16_round(torch, synth.normal(synth.tensor_seed("A", M, K), (M, K), scale=1.0))
     W = synth.normal(synth.tensor_seed("W", N, K), (N, K))
     Wb = oracle.q8_0_encode_bytes(W)
@@ -122,9 +123,10 @@ def test_gemm_q8_0_within_bf16_bound(torch, cpa, M, N, K, splits, mode):
     assert np.all(err <= bound + 1e-30)
 
 
-@pytest.mark.parametrize("M,F,K,splits", [(130, 128, 256, 0), (77, 704, 256, 0), (512, 1024, 2048, 2)])
+@pytest.mark.parametrize("M,F,K,splits", [(130, 128, 256, 0), (77, 704, 256, 0), (512, 1024, 2048, 2),
+                                          (512, 17408, 5120, 0), (159, 17408, 5120, 0)])
 def test_gemm_swiglu(torch, cpa, M, F, K, splits):
-    log(f"gemm swiglu M={M} F={F} K={K}")
+    log(f"gemm swiglu M={M} F={F} K={K} plan={cpa.cp_test_gemm_plan(M, 2 * F, K)}")
     A = bf16_round(torch, synth.normal(synth.tensor_seed("A", M, K), (M, K), scale=1.0))
     W = synth.normal(synth.tensor_seed("Wgu", F, K), (2 * F, K))
     Wb = oracle.q8_0_encode_bytes(W)
