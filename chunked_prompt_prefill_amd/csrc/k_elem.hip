@@ -173,49 +173,66 @@ KvLayer kv_layer_at(void* base, int32_t Hkv, int32_t hd, int32_t n_ctx, int32_t 
 }
 
 // RoPE on q and k (rotate-half pairs (i, i+hd/2)), then q -> f16 output and k -> cache.
-// One workgroup per token; each wave handles 64 consecutive values of one head.
+// Each lane handles 4 consecutive values of one head (16-byte loads); a wave covers 256
+// values of one token.  For a q8_0 cache the 32 values of a block sit in 8 lanes and
+// their amax is a reduction over those lanes.
 __global__ __launch_bounds__(256) void rope_qk_kernel(const float* __restrict__ qkv,
                                                       const float* __restrict__ cos_t,
-                                                      const float* __restrict__ sin_t,
+                                                      const float* __restrict__ sin_t, int32_t n,
                                                       int32_t start, int32_t Hq, int32_t Hkv,
                                                       int32_t hd, int32_t kv_type, int32_t n_ctx,
                                                       _Float16* __restrict__ q_out, KvLayer kv) {
-  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int E = (Hq + Hkv) * hd;                      // rotated values per token
+  const int segs = (E + 255) / 256;
+  const int64_t seg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t t = seg / segs;
+  if (t >= n) return;
+  const int e0 = (int)(seg % segs) * 256 + lane * 4;
+  if (e0 >= E) return;                                // whole 8-lane groups drop out together
   const int64_t p = start + t;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = hd / 2;
   const int64_t Nqkv = (int64_t)(Hq + 2 * Hkv) * hd;
   const float* row = qkv + t * Nqkv;
-  const int nseg = (Hq + Hkv) * hd / 64;
-  for (int seg = wave; seg < nseg; seg += 4) {
-    const int e = seg * 64 + lane;
-    const int head = e / hd, i = e % hd;
-    const int ic = i < half ? i : i - half;
-    const float c = cos_t[p * half + ic], s = sin_t[p * half + ic];
-    const float x = row[e];
-    float out;
-    if (i < half) {
-      const float y = row[head * hd + i + half];
-      out = __fsub_rn(__fmul_rn(x, c), __fmul_rn(y, s));
-    } else {
-      const float y = row[head * hd + i - half];
-      out = __fadd_rn(__fmul_rn(x, c), __fmul_rn(y, s));
-    }
-    if (head < Hq) {
-      q_out[(t * Hq + head) * hd + i] = (_Float16)out;
-    } else {
-      const int64_t gi = (int64_t)(head - Hq) * n_ctx + p;
-      if (kv_type == CP_KV_F16) {
-        reinterpret_cast<_Float16*>(kv.k)[gi * hd + i] = (_Float16)out;
-      } else {
-        float d;
-        int q;
-        q8_encode_lane(out, d, q);
-        reinterpret_cast<int8_t*>(kv.k)[gi * hd + i] = (int8_t)q;
-        if ((i & 31) == 0) kv.kd[gi * (hd / QK) + i / QK] = float_to_half_bits(d);
-      }
-    }
+  const int head = e0 / hd, i0 = e0 % hd;
+  const bool lo = i0 < half;
+  const int ic0 = lo ? i0 : i0 - half;
+  const float4 x = *reinterpret_cast<const float4*>(row + e0);
+  const float4 y = *reinterpret_cast<const float4*>(row + head * hd + (lo ? i0 + half : i0 - half));
+  const float4 c = *reinterpret_cast<const float4*>(cos_t + p * half + ic0);
+  const float4 s = *reinterpret_cast<const float4*>(sin_t + p * half + ic0);
+  const float xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+  const float cs[4] = {c.x, c.y, c.z, c.w}, ss[4] = {s.x, s.y, s.z, s.w};
+  float out[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    out[k] = lo ? __fsub_rn(__fmul_rn(xs[k], cs[k]), __fmul_rn(ys[k], ss[k]))
+                : __fadd_rn(__fmul_rn(xs[k], cs[k]), __fmul_rn(ys[k], ss[k]));
+  if (head < Hq) {
+    *reinterpret_cast<uint2*>(q_out + (t * Hq + head) * hd + i0) =
+        make_uint2(pack_f16x2(out[0], out[1]), pack_f16x2(out[2], out[3]));
+    return;
   }
+  const int64_t gi = (int64_t)(head - Hq) * n_ctx + p;
+  if (kv_type == CP_KV_F16) {
+    *reinterpret_cast<uint2*>(reinterpret_cast<_Float16*>(kv.k) + gi * hd + i0) =
+        make_uint2(pack_f16x2(out[0], out[1]), pack_f16x2(out[2], out[3]));
+    return;
+  }
+  float amax = fmaxf(fmaxf(fabsf(out[0]), fabsf(out[1])), fmaxf(fabsf(out[2]), fabsf(out[3])));
+#pragma unroll
+  for (int o = 4; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  const float d = __fdiv_rn(amax, 127.0f);
+  const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
+  uint32_t packed = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int v = (int)roundf(__fmul_rn(out[k], id));
+    v = v > 127 ? 127 : (v < -127 ? -127 : v);
+    packed |= (uint32_t)(uint8_t)(int8_t)v << (8 * k);
+  }
+  *reinterpret_cast<uint32_t*>(reinterpret_cast<int8_t*>(kv.k) + gi * hd + i0) = packed;
+  if ((i0 & 31) == 0) kv.kd[gi * (hd / QK) + i0 / QK] = float_to_half_bits(d);
 }
 
 hipError_t launch_rope_qk(const float* qkv, const float* cos_t, const float* sin_t, int32_t n,
@@ -223,56 +240,54 @@ hipError_t launch_rope_qk(const float* qkv, const float* cos_t, const float* sin
                           int32_t kv_type, int32_t n_ctx, _Float16* q_out, KvLayer kv,
                           hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_qk_kernel, dim3(n), dim3(256), 0, s, qkv, cos_t, sin_t, start, n_head,
-                     n_kv_head, head_dim, kv_type, n_ctx, q_out, kv);
+  const int64_t segs = ceil_div((int64_t)(n_head + n_kv_head) * head_dim, 256) * n;
+  hipLaunchKernelGGL(rope_qk_kernel, dim3((unsigned)ceil_div(segs, 4)), dim3(256), 0, s, qkv, cos_t,
+                     sin_t, n, start, n_head, n_kv_head, head_dim, kv_type, n_ctx, q_out, kv);
   return hipGetLastError();
 }
 
-// V rows -> transposed cache.  A workgroup takes 64 tokens of one kv head: each wave
-// converts 64 consecutive dims of a token row (q8_0: per-32 amax by wavefront
-// reduction), the codes are transposed through LDS, then written 64 positions at a time.
+// V rows -> transposed cache.  A workgroup takes 32 tokens x 64 dims of one kv head: each
+// wave converts 64 consecutive dims of a token row (q8_0: per-32 amax by wavefront
+// reduction), the codes are transposed through LDS, then written 32 positions per dim.
+constexpr int VT = 32;
 __global__ __launch_bounds__(256) void v_append_kernel(const float* __restrict__ qkv, int32_t n,
                                                        int32_t start, int32_t Hq, int32_t Hkv,
                                                        int32_t hd, int32_t kv_type, int32_t n_ctx,
                                                        KvLayer kv) {
-  __shared__ uint16_t sv[128][66];
-  __shared__ int8_t sq[128][68];
-  __shared__ uint16_t sd[4][64];
-  const int t0 = blockIdx.x * 64;
-  const int g = blockIdx.y;
+  __shared__ uint16_t sv[64][VT + 2];
+  __shared__ int8_t sq[64][VT + 4];
+  __shared__ uint16_t sd[2][VT];
+  const int t0 = blockIdx.x * VT;
+  const int g = blockIdx.y / (hd / 64);
+  const int d0 = (blockIdx.y % (hd / 64)) * 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t Nqkv = (int64_t)(Hq + 2 * Hkv) * hd;
-  const int64_t vcol = (int64_t)(Hq + Hkv + g) * hd;
-  const int parts = hd / 64;
-  for (int seg = wave; seg < 64 * parts; seg += 4) {
-    const int tl = seg / parts, i = (seg % parts) * 64 + lane;
+  const int64_t vcol = (int64_t)(Hq + Hkv + g) * hd + d0;
+  for (int tl = wave; tl < VT; tl += 4) {
     const int t = t0 + tl;
-    const float v = t < n ? qkv[(int64_t)t * Nqkv + vcol + i] : 0.0f;
+    const float v = t < n ? qkv[(int64_t)t * Nqkv + vcol + lane] : 0.0f;
     if (kv_type == CP_KV_F16) {
-      sv[i][tl] = float_to_half_bits(v);
+      sv[lane][tl] = float_to_half_bits(v);
     } else {
       float d;
       int q;
       q8_encode_lane(v, d, q);
-      sq[i][tl] = (int8_t)q;
-      if ((i & 31) == 0) sd[i / QK][tl] = float_to_half_bits(d);
+      sq[lane][tl] = (int8_t)q;
+      if ((lane & 31) == 0) sd[lane / QK][tl] = float_to_half_bits(d);
     }
   }
   __syncthreads();
-  const int nt = min(64, n - t0);
-  for (int e = threadIdx.x; e < hd * 64; e += 256) {
-    const int i = e / 64, tl = e % 64;
+  const int nt = min(VT, n - t0);
+  for (int e = threadIdx.x; e < 64 * VT; e += 256) {
+    const int i = e / VT, tl = e % VT;
     if (tl >= nt) continue;
-    const int64_t dst = ((int64_t)g * hd + i) * n_ctx + start + t0 + tl;
+    const int64_t dst = ((int64_t)g * hd + d0 + i) * n_ctx + start + t0 + tl;
     if (kv_type == CP_KV_F16) reinterpret_cast<uint16_t*>(kv.v)[dst] = sv[i][tl];
     else reinterpret_cast<int8_t*>(kv.v)[dst] = sq[i][tl];
   }
-  if (kv_type != CP_KV_F16) {
-    for (int e = threadIdx.x; e < (hd / QK) * 64; e += 256) {
-      const int b = e / 64, tl = e % 64;
-      if (tl >= nt) continue;
-      kv.vd[((int64_t)g * (hd / QK) + b) * n_ctx + start + t0 + tl] = sd[b][tl];
-    }
+  if (kv_type != CP_KV_F16 && threadIdx.x < 2 * VT) {
+    const int b = threadIdx.x / VT, tl = threadIdx.x % VT;
+    if (tl < nt) kv.vd[((int64_t)g * (hd / QK) + d0 / QK + b) * n_ctx + start + t0 + tl] = sd[b][tl];
   }
 }
 
@@ -280,8 +295,8 @@ hipError_t launch_v_append(const float* qkv, int32_t n, int32_t start, int32_t n
                            int32_t n_kv_head, int32_t head_dim, int32_t kv_type, int32_t n_ctx,
                            KvLayer kv, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(v_append_kernel, dim3((unsigned)ceil_div(n, 64), n_kv_head), dim3(256), 0, s,
-                     qkv, n, start, n_head, n_kv_head, head_dim, kv_type, n_ctx, kv);
+  hipLaunchKernelGGL(v_append_kernel, dim3((unsigned)ceil_div(n, VT), n_kv_head * (head_dim / 64)),
+                     dim3(256), 0, s, qkv, n, start, n_head, n_kv_head, head_dim, kv_type, n_ctx, kv);
   return hipGetLastError();
 }
 
