@@ -77,33 +77,33 @@ Dims dims_of(const cp_config* c) {
 // --------------------------------------------------------------------------------------
 // Launch policies
 // --------------------------------------------------------------------------------------
-// 128-row tiles run two workgroups per CU (two waves per SIMD hide each other's load
-// and dequantisation latency); measured faster than 256-row tiles at one per CU.
-int gemm_mt(int M) { return M <= 64 ? 64 : 128; }
-
 constexpr int g_cus = 256;   // compute units of an MI355X; plans and workspace sizes use it
 // workgroups resident per CU for a row tile (the 256-row tile takes all of LDS)
 inline int wg_per_cu(int mt) { return mt >= 256 ? 1 : 2; }
+// Sustained fraction of the CU's MFMA rate per row tile (measured): the 256-row kernel
+// dequantises each weight for 256 rows, the smaller tiles for 128 or 64.
+inline double tile_eff(int mt) { return mt >= 256 ? 0.60 : (mt >= 128 ? 0.40 : 0.25); }
 
 // A GEMM call runs as one or two launches over column ranges: the tiles that fill whole
 // rounds of the chip run unsplit, and (optionally) a tail of whole 256-column tiles runs
-// with split-K so that it fills the chip too.  The plan minimises a simple time model:
-// rounds of workgroups x stages per workgroup, plus the partial-sum traffic and an extra
-// launch for any split.
+// with split-K so that it fills the chip too.  For each row tile the plan minimises a
+// simple time model (rounds of workgroups x K stages per workgroup, plus the partial-sum
+// traffic and an extra launch for any split); the cheapest row tile wins.
 struct GemmPart { int n0, n1, splits; };
 struct GemmPlan {
   int mt = 256, nparts = 0;
   GemmPart part[2];
   size_t partial_bytes = 0;
+  double cost = 0.0;
 };
 
-GemmPlan plan_gemm(int M, int N, int K, int force_splits = 0) {
+GemmPlan plan_gemm_mt(int M, int N, int K, int mt, int force_splits) {
   GemmPlan p;
-  p.mt = gemm_mt(M);
+  p.mt = mt;
   const int64_t Mt = ceil_div(M, p.mt), Nt = ceil_div(N, 256), KS = K / 128, T = Mt * Nt;
   const int slots = g_cus * wg_per_cu(p.mt);
-  // one K stage of a tile, with wg_per_cu tiles sharing a CU
-  const double t_stage = 2.0 * p.mt * 256 * 128 * wg_per_cu(p.mt) / (9.77e12 * 0.6);
+  // one 128-wide K stage of a tile, with wg_per_cu tiles sharing a CU
+  const double t_stage = 2.0 * p.mt * 256 * 128 * wg_per_cu(p.mt) / (9.77e12 * tile_eff(p.mt));
   const double launch = 4e-6;
   auto red = [&](int64_t S, int64_t cols) { return (double)(S + 1) * M * cols * 4 / 5e12 + launch; };
   auto rounds = [&](int64_t wgs) { return (double)ceil_div(wgs, slots); };
@@ -112,6 +112,7 @@ GemmPlan plan_gemm(int M, int N, int K, int force_splits = 0) {
     p.nparts = 1;
     p.part[0] = {0, N, S};
     p.partial_bytes = S > 1 ? (size_t)S * M * N * 4 : 0;
+    p.cost = rounds(T * S) * ceil_div(KS, S) * t_stage;
     return p;
   }
   double best = rounds(T) * KS * t_stage;
@@ -145,7 +146,21 @@ GemmPlan plan_gemm(int M, int N, int K, int force_splits = 0) {
   for (int i = 0; i < p.nparts; ++i)
     if (p.part[i].splits > 1)
       p.partial_bytes = std::max(p.partial_bytes, (size_t)p.part[i].splits * M * (p.part[i].n1 - p.part[i].n0) * 4);
+  p.cost = best;
   return p;
+}
+
+// force_mt > 0 pins the row tile (tests); force_splits > 0 forces one launch with that
+// split-K factor.
+GemmPlan plan_gemm(int M, int N, int K, int force_splits = 0, int force_mt = 0) {
+  if (force_mt > 0) return plan_gemm_mt(M, N, K, force_mt, force_splits);
+  if (M <= 64) return plan_gemm_mt(M, N, K, 64, force_splits);
+  GemmPlan best = plan_gemm_mt(M, N, K, 128, force_splits);
+  if (M > 128) {
+    const GemmPlan big = plan_gemm_mt(M, N, K, 256, force_splits);
+    if (big.cost < best.cost) best = big;
+  }
+  return best;
 }
 
 int attn_splits(const Dims& D, int n, int start) {
@@ -841,16 +856,23 @@ int cp_test_router(const float* y, const void* w_router, int32_t n, int32_t d, i
   return launch_router(y, q, dd, n, d, E, k, logits, idx, weight, s) == hipSuccess ? CP_OK : CP_E_DEVICE;
 }
 
-size_t cp_test_gemm_scratch_bytes(int32_t M, int32_t N, int32_t K, int32_t splits) {
-  if (M < 1 || N < 32 || N % 32 || K < 128 || K % 128) return 0;
-  const GemmPlan p = plan_gemm(M, N, K, splits);
+size_t cp_test_gemm_scratch_bytes_ex(int32_t M, int32_t N, int32_t K, int32_t splits, int32_t row_tile) {
+  if (M < 1 || N < 32 || N % 32 || K < 128 || K % 128 || splits < 0) return 0;
+  if (row_tile != 0 && row_tile != 64 && row_tile != 128 && row_tile != 256) return 0;
+  const GemmPlan p = plan_gemm(M, N, K, splits, row_tile);
   return align_up(QMat::q_bytes(N, K)) + align_up(QMat::d_bytes(N, K)) + align_up(p.partial_bytes + 4);
 }
 
-int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
-                 int32_t splits, void* out, void* scratch, void* stream) {
-  if (!A || !W || !out || !scratch || M < 1 || N < 32 || N % 32 || K < 128 || K % 128 || mode < 0 || mode > 2)
+size_t cp_test_gemm_scratch_bytes(int32_t M, int32_t N, int32_t K, int32_t splits) {
+  return cp_test_gemm_scratch_bytes_ex(M, N, K, splits, 0);
+}
+
+int cp_test_gemm_ex(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
+                    int32_t splits, int32_t row_tile, void* out, void* scratch, void* stream) {
+  if (!A || !W || !out || !scratch || M < 1 || N < 32 || N % 32 || K < 128 || K % 128 || mode < 0 ||
+      mode > 2 || splits < 0)
     return CP_E_INVALID;
+  if (row_tile != 0 && row_tile != 64 && row_tile != 128 && row_tile != 256) return CP_E_INVALID;
   if (mode == GM_SWIGLU && N % 64) return CP_E_INVALID;
   hipStream_t s = (hipStream_t)stream;
   QMat q;
@@ -867,7 +889,7 @@ int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, 
     e = launch_repack_q8_0(W, nullptr, N, K, 0, N, 0, q, s);
   }
   if (e != hipSuccess) return CP_E_DEVICE;
-  const GemmPlan p = plan_gemm(M, N, K, splits);
+  const GemmPlan p = plan_gemm(M, N, K, splits, row_tile);
   for (int i = 0; i < p.nparts; ++i) {
     GemmArgs g;
     g.A = (const __bf16*)A; g.lda = K; g.M = M; g.N = p.part[i].n1; g.K = K; g.n0 = p.part[i].n0;
@@ -878,6 +900,11 @@ int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, 
     if (launch_gemm(g, 0, p.mt, s) != hipSuccess) return CP_E_DEVICE;
   }
   return CP_OK;
+}
+
+int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
+                 int32_t splits, void* out, void* scratch, void* stream) {
+  return cp_test_gemm_ex(A, W, M, N, K, mode, splits, 0, out, scratch, stream);
 }
 
 int cp_test_gemm_plan(int32_t M, int32_t N, int32_t K, int32_t* out6) {

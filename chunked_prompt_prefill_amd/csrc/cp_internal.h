@@ -55,6 +55,9 @@ struct GemmArgs {
 
 // Kernel launchers (return hipError_t of the launch).
 hipError_t launch_gemm(const GemmArgs& a, int grid_m_tiles, int mt, hipStream_t s);
+// 256-row tiles, one workgroup per CU (non-grouped only); the partial-sum reduction of a
+// split launch is left to the caller.
+hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* partial, int32_t splits, int32_t M, int32_t n0,
                                 int32_t N, int32_t mode, void* out, int32_t ldo, hipStream_t s);
 // Repack interchange q8_0 rows into a QMat.  mode 0: destination rows dst_row0 ..

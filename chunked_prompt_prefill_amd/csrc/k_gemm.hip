@@ -2,6 +2,9 @@
 //
 //   out[m][n] = sum_k A[m][k] * W[n][k],  A bf16 activations, W q8_0 blocks of 32.
 //
+// This kernel takes row tiles of 64 and 128 (two workgroups per CU) and the grouped
+// expert GEMMs; 256-row tiles run the deeper-pipelined kernel in k_gemm_big.hip.
+//
 // Tiling.  A workgroup of 4 waves owns an MT x 256 output tile (MT = 32*MI); each wave
 // owns 64 columns (two 32-column MFMA blocks) across all MT rows, so every weight
 // element is dequantised exactly once per workgroup.  Per 128-wide K stage (4 q8_0
@@ -304,15 +307,10 @@ hipError_t launch_gemm(const GemmArgs& a, int grid_m_tiles, int mt, hipStream_t 
   if (a.M <= 0 || a.N <= a.n0) return hipSuccess;
   const bool grouped = a.tiles != nullptr;
   hipError_t e;
-  if (grouped) {
-    if (mt == 128) e = launch_mode<4, true>(a, grid_m_tiles, s);
-    else if (mt == 64) e = launch_mode<2, true>(a, grid_m_tiles, s);
-    else e = launch_mode<8, true>(a, grid_m_tiles, s);
-    return e;
-  }
+  if (grouped) return mt == 64 ? launch_mode<2, true>(a, grid_m_tiles, s) : launch_mode<4, true>(a, grid_m_tiles, s);
   if (mt == 64) e = launch_mode<2, false>(a, 0, s);
   else if (mt == 128) e = launch_mode<4, false>(a, 0, s);
-  else e = launch_mode<8, false>(a, 0, s);
+  else e = launch_gemm_big(a, s);
   if (e != hipSuccess || a.splits <= 1) return e;
   return launch_splitk_reduce(a.partial, a.splits, a.M, a.n0, a.N, a.mode, a.out, a.ldo, s);
 }

@@ -192,11 +192,15 @@ def cp_test_router(y, w_router, n, d, n_expert, k, logits, idx, weight):
         raise PrefillError(rc, "cp_test_router failed")
 
 
-def cp_test_gemm(A, W, M, N, K, mode, splits, out):
+def cp_test_gemm(A, W, M, N, K, mode, splits, out, row_tile=0):
+    """One q8_0 GEMM through the library (row_tile 0: the layer's own launch plan)."""
     L = lib()
-    scratch = torch.empty(max(1, L.cp_test_gemm_scratch_bytes(M, N, K, splits)), dtype=torch.uint8,
-                          device=A.device)
-    rc = L.cp_test_gemm(ptr(A), ptr(W), M, N, K, mode, splits, ptr(out), ptr(scratch), stream_ptr())
+    nbytes = L.cp_test_gemm_scratch_bytes_ex(M, N, K, splits, row_tile)
+    if nbytes == 0:
+        raise PrefillError(-1, "cp_test_gemm: unsupported shape")
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device=A.device)
+    rc = L.cp_test_gemm_ex(ptr(A), ptr(W), M, N, K, mode, splits, row_tile, ptr(out), ptr(scratch),
+                           stream_ptr())
     if rc != CP_OK:
         raise PrefillError(rc, "cp_test_gemm failed")
 

@@ -233,6 +233,13 @@ size_t cp_test_gemm_scratch_bytes(int32_t M, int32_t N, int32_t K, int32_t split
 int cp_test_gemm_plan(int32_t M, int32_t N, int32_t K, int32_t* out6);
 int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
                  int32_t splits, void* out, void* scratch, void* hip_stream);
+/* Same with the row tile pinned: row_tile 64 or 128 runs the kernel that keeps two
+ * workgroups per CU, 256 the one-workgroup-per-CU kernel with the three-stage LDS
+ * pipeline; 0 = the layer's own choice.  Scratch: cp_test_gemm_scratch_bytes_ex. */
+size_t cp_test_gemm_scratch_bytes_ex(int32_t M, int32_t N, int32_t K, int32_t splits,
+                                     int32_t row_tile);
+int cp_test_gemm_ex(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
+                    int32_t splits, int32_t row_tile, void* out, void* scratch, void* hip_stream);
 
 /* Causal flash attention of a chunk against a one-layer cache (rows already appended):
  * q: f16 [n][n_head][head_dim]; kv: one-layer cache (capacity n_ctx) holding positions

@@ -123,17 +123,45 @@ def test_gemm_q8_0_within_bf16_bound(torch, cpa, M, N, K, splits, mode):
     assert np.all(err <= bound + 1e-30)
 
 
-@pytest.mark.parametrize("M,F,K,splits", [(130, 128, 256, 0), (77, 704, 256, 0), (512, 1024, 2048, 2),
-                                          (512, 17408, 5120, 0), (159, 17408, 5120, 0)])
-def test_gemm_swiglu(torch, cpa, M, F, K, splits):
-    log(f"gemm swiglu M={M} F={F} K={K} plan={cpa.cp_test_gemm_plan(M, 2 * F, K)}")
+@pytest.mark.parametrize("row_tile", [128, 256])
+@pytest.mark.parametrize("M,N,K,splits", [(1, 256, 256, 0), (200, 512, 384, 0), (300, 768, 2048, 3),
+                                          (513, 1024, 768, 0), (777, 1280, 1152, 5),
+                                          (2048, 5120, 5120, 0), (256, 7168, 5120, 7)])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_gemm_q8_0_row_tiles(torch, cpa, M, N, K, splits, mode, row_tile):
+    """Both GEMM kernels with the row tile pinned: ragged M and N, K stage counts that are
+    and are not multiples of the 256-row kernel's three-stage pipeline, split-K."""
+    log(f"gemm row_tile={row_tile} M={M} N={N} K={K} splits={splits} mode={mode}")
+    A = bf16_round(torch, synth.normal(synth.tensor_seed("A", M, K), (M, K), scale=1.0))
+    W = synth.normal(synth.tensor_seed("W", N, K), (N, K))
+    Wb = oracle.q8_0_encode_bytes(W)
+    Wd = oracle.q8_0_decode_bytes(Wb, K).astype(np.float64)
+    X0 = synth.normal(synth.tensor_seed("X0", M, N), (M, N), scale=1.0)
+    out = torch.from_numpy(X0.copy() if mode == 1 else np.zeros((M, N), np.float32)).cuda()
+    At = torch.from_numpy(A).cuda().to(torch.bfloat16)
+    cpa.cp_test_gemm(At, torch.from_numpy(Wb).cuda(), M, N, K, mode, splits, out, row_tile=row_tile)
+    got = out.cpu().numpy().astype(np.float64)
+    ref = A.astype(np.float64) @ Wd.T + (X0.astype(np.float64) if mode == 1 else 0.0)
+    mag = np.abs(A.astype(np.float64)) @ np.abs(Wd).T
+    bound = (2.0 ** -9 * 1.001 + (K + 2) * 2.0 ** -24) * mag + (np.abs(ref) * 2.0 ** -23 if mode == 1 else 0)
+    err = np.abs(got - ref)
+    log(f"  max rel err {rel_err(got, ref):.3e}, worst err/bound {np.max(err / (bound + 1e-30)):.3f}")
+    assert np.all(err <= bound + 1e-30)
+
+
+@pytest.mark.parametrize("M,F,K,splits,row_tile", [(130, 128, 256, 0, 0), (77, 704, 256, 0, 0),
+                                                   (512, 1024, 2048, 2, 0), (512, 17408, 5120, 0, 0),
+                                                   (159, 17408, 5120, 0, 0), (300, 1024, 2048, 0, 256),
+                                                   (2048, 2048, 1280, 0, 256), (600, 1536, 768, 4, 256)])
+def test_gemm_swiglu(torch, cpa, M, F, K, splits, row_tile):
+    log(f"gemm swiglu M={M} F={F} K={K} row_tile={row_tile} plan={cpa.cp_test_gemm_plan(M, 2 * F, K)}")
     A = bf16_round(torch, synth.normal(synth.tensor_seed("A", M, K), (M, K), scale=1.0))
     W = synth.normal(synth.tensor_seed("Wgu", F, K), (2 * F, K))
     Wb = oracle.q8_0_encode_bytes(W)
     Wd = oracle.q8_0_decode_bytes(Wb, K).astype(np.float64)
     out = torch.zeros((M, F), dtype=torch.bfloat16, device="cuda")
     cpa.cp_test_gemm(torch.from_numpy(A).cuda().to(torch.bfloat16), torch.from_numpy(Wb).cuda(),
-                     M, 2 * F, K, 2, splits, out)
+                     M, 2 * F, K, 2, splits, out, row_tile=row_tile)
     got = out.float().cpu().numpy()
     g = A.astype(np.float64) @ Wd[:F].T
     u = A.astype(np.float64) @ Wd[F:].T
@@ -143,14 +171,15 @@ def test_gemm_swiglu(torch, cpa, M, F, K, splits):
     assert e < 1e-2
 
 
-def test_gemm_deterministic_split_k(torch, cpa):
+@pytest.mark.parametrize("row_tile", [128, 256])
+def test_gemm_deterministic_split_k(torch, cpa, row_tile):
     M, N, K = 200, 5120, 5120
     A = torch.from_numpy(synth.normal(5, (M, K), scale=1.0)).cuda().to(torch.bfloat16)
     Wb = torch.from_numpy(oracle.q8_0_encode_bytes(synth.normal(6, (N, K)))).cuda()
     outs = []
     for _ in range(2):
         o = torch.zeros((M, N), dtype=torch.float32, device="cuda")
-        cpa.cp_test_gemm(A, Wb, M, N, K, 0, 4, o)
+        cpa.cp_test_gemm(A, Wb, M, N, K, 0, 4, o, row_tile=row_tile)
         outs.append(o.cpu().numpy())
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
 
