@@ -57,6 +57,8 @@ std::string validate(const cp_config* c) {
   if (!(c->rope_theta > 0.0f) || !std::isfinite(c->rope_theta)) return "rope_theta must be > 0";
   if (c->kv_type != CP_KV_F16 && c->kv_type != CP_KV_Q8_0) return "kv_type must be 0 (f16) or 1 (q8_0)";
   if (c->n_ctx_max < 1 || c->n_ctx_max > (1 << 24)) return "n_ctx_max must be in [1, 2^24]";
+  // attention addresses one kv head's cache (n_ctx x head_dim f16) with 32-bit byte offsets
+  if ((int64_t)(c->n_ctx_max + 63) * c->head_dim * 2 >= (1LL << 31)) return "n_ctx_max * head_dim too large";
   if (c->n_chunk_max < 1 || c->n_chunk_max > c->n_ctx_max) return "n_chunk_max must be in [1, n_ctx_max]";
   if ((int64_t)c->n_chunk_max * c->n_head * c->head_dim > (1LL << 31)) return "n_chunk_max too large";
   return "";

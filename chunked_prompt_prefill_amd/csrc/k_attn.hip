@@ -32,6 +32,21 @@ typedef __attribute__((address_space(3))) void lvoid_a;
 int attention_rows_total(int32_t n, int32_t n_head) { return n * n_head; }
 
 __device__ __forceinline__ void attn_wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding, expcnt not waited).
+template <int N>
+__device__ __forceinline__ void attn_wait_vm_lgkm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
+// Compiler-only fence: memory operations are not moved across it.
+__device__ __forceinline__ void attn_cfence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+// 16-byte buffer load into LDS.  Buffer loads (unlike the global form) are not counted
+// as LDS events, so LDS reads of the current tile keep partial lgkmcnt waits while the
+// next tiles are in flight; the scalar offset is made explicitly uniform (otherwise the
+// compiler may wrap each load in a loop over its distinct values).
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, lvoid_a* dst, int32_t voff, int32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, __builtin_amdgcn_readfirstlane(soff), 0, 0);
+}
 
 // V^T tile swizzle: 16-byte chunk lc of row d sits at physical chunk lc ^ vswz(d).
 __device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
@@ -43,8 +58,21 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
   constexpr int DB = HD / 32;
   constexpr int KCH = KVT * NCH;   // chunks per K tile
   constexpr int VCH = HD * 8;      // chunks per V tile (8 per dim row)
-  __shared__ uint4 sK[2][KCH];
-  __shared__ uint4 sV[2][VCH];
+  constexpr int NKL = KCH / (AW * 64); // K loads per thread per tile (f16)
+  constexpr int NVL = VCH / (AW * 64); // V loads per thread per tile (f16)
+  constexpr int NLOAD = NKL + NVL;
+  // three tile buffers, separate LDS objects so the compiler can tell reads of one tile
+  // from asynchronous writes into another
+  __shared__ uint4 sK0[KCH], sK1[KCH], sK2[Q8 ? 1 : KCH];
+  __shared__ uint4 sV0[VCH], sV1[VCH], sV2[Q8 ? 1 : VCH];
+  auto bufK = [&](auto J) __attribute__((always_inline)) -> uint4* {
+    constexpr int j = decltype(J)::value;
+    if constexpr (j == 0) return sK0; else if constexpr (j == 1) return sK1; else return sK2;
+  };
+  auto bufV = [&](auto J) __attribute__((always_inline)) -> uint4* {
+    constexpr int j = decltype(J)::value;
+    if constexpr (j == 0) return sV0; else if constexpr (j == 1) return sV1; else return sV2;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -80,25 +108,34 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
   }
 
   // ---- tile staging ----
-  const _Float16* Kf = reinterpret_cast<const _Float16*>(a.kv.k) + (int64_t)g * n_ctx * HD;
-  const _Float16* Vf = reinterpret_cast<const _Float16*>(a.kv.v) + (int64_t)g * HD * n_ctx;
-  // f16: asynchronous loads; wave instruction j fills physical chunks [(j*AW + wave)*64, +64).
-  auto issue_f16 = [&](int jt, int buf) __attribute__((always_inline)) {
+  // f16: buffer loads into LDS.  Load j of wave w fills physical chunks [(j*AW + w)*64,
+  // +64); the swizzle is chosen through each lane's source offset (constant per lane; the
+  // tile's first position goes into the scalar offset).
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const _Float16*>(a.kv.k) + (int64_t)g * n_ctx * HD), (short)0,
+      (int)min(n_ctx * HD * 2, (int64_t)0x7FFFFFFF), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const _Float16*>(a.kv.v) + (int64_t)g * HD * n_ctx), (short)0,
+      (int)min(n_ctx * HD * 2, (int64_t)0x7FFFFFFF), 0x00020000);
+  int32_t koff[NKL], voff[NVL];
+#pragma unroll
+  for (int j = 0; j < NKL; ++j) {
+    const int P = (j * AW + wave) * 64 + lane;
+    const int row = P / NCH, lc = (P % NCH) ^ (row % NCH);
+    koff[j] = (row * HD + lc * 8) * 2;
+  }
+#pragma unroll
+  for (int j = 0; j < NVL; ++j) {
+    const int P = (j * AW + wave) * 64 + lane;
+    const int d = P >> 3, lc = (P & 7) ^ vswz(d);
+    voff[j] = (int32_t)(((int64_t)d * n_ctx + lc * 8) * 2);
+  }
+  auto issue_f16 = [&](auto J, int jt) __attribute__((always_inline)) {
     const int j0 = jt * KVT;
 #pragma unroll
-    for (int j = 0; j < KCH / (AW * 64); ++j) {
-      const int P = (j * AW + wave) * 64 + lane;
-      const int row = P / NCH, lc = (P % NCH) ^ (row % NCH);
-      __builtin_amdgcn_global_load_lds((gvoid_a*)(Kf + (int64_t)(j0 + row) * HD + lc * 8),
-                                       (lvoid_a*)&sK[buf][(j * AW + wave) * 64], 16, 0, 0);
-    }
+    for (int j = 0; j < NKL; ++j) lds_dma16(krs, (lvoid_a*)&bufK(J)[(j * AW + wave) * 64], koff[j], j0 * HD * 2);
 #pragma unroll
-    for (int j = 0; j < VCH / (AW * 64); ++j) {
-      const int P = (j * AW + wave) * 64 + lane;
-      const int d = P >> 3, lc = (P & 7) ^ vswz(d);
-      __builtin_amdgcn_global_load_lds((gvoid_a*)(Vf + (int64_t)d * n_ctx + j0 + lc * 8),
-                                       (lvoid_a*)&sV[buf][(j * AW + wave) * 64], 16, 0, 0);
-    }
+    for (int j = 0; j < NVL; ++j) lds_dma16(vrs, (lvoid_a*)&bufV(J)[(j * AW + wave) * 64], voff[j], j0 * 2);
   };
   // q8_0: one 16-int8 chunk of K and of V per thread (and its scales), held in registers.
   constexpr int KQ = KVT * (HD / 16), VQ = HD * (KVT / 16);   // int8 chunks per tile
@@ -145,14 +182,14 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
       }
     }
   };
-  auto store_q8 = [&](int buf) __attribute__((always_inline)) {
+  auto store_q8 = [&](uint4* kb, uint4* vb) __attribute__((always_inline)) {
     if (tid < KQ) {
       const int row = tid / (HD / 16), c16 = tid % (HD / 16);
       const float d = half_bits_to_float(qk_sc);
       const float ds[8] = {d, d, d, d, d, d, d, d};
       const int sw = row % NCH;
-      sK[buf][row * NCH + ((2 * c16) ^ sw)] = dequant8_f16(qk_raw.x, qk_raw.y, ds);
-      sK[buf][row * NCH + ((2 * c16 + 1) ^ sw)] = dequant8_f16(qk_raw.z, qk_raw.w, ds);
+      kb[row * NCH + ((2 * c16) ^ sw)] = dequant8_f16(qk_raw.x, qk_raw.y, ds);
+      kb[row * NCH + ((2 * c16 + 1) ^ sw)] = dequant8_f16(qk_raw.z, qk_raw.w, ds);
     }
     if (tid < VQ) {
       const int d = tid / (KVT / 16), c16 = tid % (KVT / 16);
@@ -164,8 +201,8 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
         ds[2 * e + 1] = half_bits_to_float(s[e] >> 16);
       }
       const int sw = vswz(d);
-      sV[buf][d * 8 + ((2 * c16) ^ sw)] = dequant8_f16(qv_raw.x, qv_raw.y, ds);
-      sV[buf][d * 8 + ((2 * c16 + 1) ^ sw)] = dequant8_f16(qv_raw.z, qv_raw.w, ds + 8);
+      vb[d * 8 + ((2 * c16) ^ sw)] = dequant8_f16(qv_raw.x, qv_raw.y, ds);
+      vb[d * 8 + ((2 * c16 + 1) ^ sw)] = dequant8_f16(qv_raw.z, qv_raw.w, ds + 8);
     }
   };
 
@@ -177,7 +214,7 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
 
-  auto compute = [&](int buf, int j0) __attribute__((always_inline)) {
+  auto compute = [&](const uint4* kb, const uint4* vb, int j0) __attribute__((always_inline)) {
     // ---- S^T = K Q^T ----
     f32x16 s[2];
 #pragma unroll
@@ -188,7 +225,7 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         const int ch = kk * 2 + h;
-        const uint4 av = sK[buf][row * NCH + (ch ^ (row % NCH))];
+        const uint4 av = kb[row * NCH + (ch ^ (row % NCH))];
         s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av),
                                                        __builtin_bit_cast(f16x8, qf[kk]), s[jb], 0, 0, 0);
       }
@@ -230,7 +267,7 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
         s[jb][e] = p;
         ls += p;
       }
-    l += ls + __shfl_xor(ls, 32, 64);
+    l += ls;                           // lane half; halves are combined at the end
     // ---- O^T += V^T P^T ----
     uint4 pb[4];
 #pragma unroll
@@ -241,7 +278,7 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
                           pack_f16x2(s[jb][8 * kk + 4], s[jb][8 * kk + 5]),
                           pack_f16x2(s[jb][8 * kk + 6], s[jb][8 * kk + 7]));
     }
-    const uint2* sv2 = reinterpret_cast<const uint2*>(&sV[buf][0]);
+    const uint2* sv2 = reinterpret_cast<const uint2*>(vb);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int dd = db * 32 + l32, sw = vswz(dd);
@@ -256,26 +293,47 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
     }
   };
 
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   if (jt0 < jt1) {
+    const int last = jt1 - 1;
+    // Tile t lives in buffer (t - jt0) % NB.  The loop runs in groups of NB tiles; steps
+    // past the range still wait, synchronise and issue (a clamped repeat of the last tile)
+    // so every wave sees the same count of loads in flight, but skip the arithmetic.
     if constexpr (!Q8) {
-      issue_f16(jt0, 0);
-      for (int jt = jt0; jt < jt1; ++jt) {
-        attn_wait_vm0();
-        __syncthreads();               // tile jt landed for all waves; the other buffer is free
-        if (jt + 1 < jt1) issue_f16(jt + 1, (jt + 1 - jt0) & 1);
-        compute((jt - jt0) & 1, jt * KVT);
+      // NB = 3: two tiles in flight while one is consumed
+      auto step = [&](auto J, int t) __attribute__((always_inline)) {
+        attn_wait_vm_lgkm<NLOAD>();    // own loads of tile t landed; own LDS reads of t-1 done
+        __builtin_amdgcn_s_barrier();  // everyone's: tile t complete, buffer of t-1 free
+        attn_cfence();
+        issue_f16(std::integral_constant<int, (decltype(J)::value + 2) % 3>{}, min(t + 2, last));
+        attn_cfence();
+        if (t < jt1) compute(bufK(J), bufV(J), t * KVT);
+      };
+      issue_f16(I0{}, jt0);
+      issue_f16(I1{}, min(jt0 + 1, last));
+      for (int t = jt0; t < jt1; t += 3) {
+        step(I0{}, t);
+        step(I1{}, t + 1);
+        step(I2{}, t + 2);
       }
+      attn_wait_vm0();
     } else {
+      // NB = 2: the next tile is loaded to registers during the arithmetic, dequantised after
+      // it (no asynchronous LDS writes here, so the buffer is picked at run time)
       load_q8(jt0);
-      store_q8(0);
-      for (int jt = jt0; jt < jt1; ++jt) {
-        __syncthreads();               // tile jt in LDS; the other buffer is free
-        if (jt + 1 < jt1) load_q8(jt + 1);
-        compute((jt - jt0) & 1, jt * KVT);
-        if (jt + 1 < jt1) store_q8((jt + 1 - jt0) & 1);
+      store_q8(sK0, sV0);
+      for (int t = jt0; t < jt1; ++t) {
+        const bool odd = (t - jt0) & 1;
+        __syncthreads();               // tile t in LDS; the buffer of t+1 is free
+        if (t + 1 < jt1) load_q8(t + 1);
+        compute(odd ? sK1 : sK0, odd ? sV1 : sV0, t * KVT);
+        if (t + 1 < jt1) store_q8(odd ? sK0 : sK1, odd ? sV0 : sV1);
       }
     }
   }
+  l += __shfl_xor(l, 32, 64);          // per-lane partial sums -> row sum
 
   if (!row_ok) return;
   if (a.splits == 1) {
