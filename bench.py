@@ -28,7 +28,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F16_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 MFMA (same rate)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -67,7 +67,7 @@ def chunk_bytes(w, C: int, D: int) -> float:
 
 
 def roofline_s(w, C, D):
-    return max(chunk_flops(w, C, D) / (PEAK_BF16_TFLOPS * 1e12),
+    return max(chunk_flops(w, C, D) / (PEAK_F16_TFLOPS * 1e12),
                chunk_bytes(w, C, D) / (PEAK_HBM_GBS * 1e9))
 
 
@@ -95,6 +95,73 @@ def gpu_layers(w, torch, cpa, synth):
     return layers
 
 
+def dominant_work(w, cpa, chunks):
+    """Algorithmic work of the dominant kernel's launches in one pass over `chunks`.
+
+    Dense: the unsplit column range of the SwiGLU gate/up GEMM (the layer's launch plan,
+    cp_test_gemm_plan).  Per launch of M rows over columns [n0, n1) of W_gate|W_up with
+    K = d_model: flops 2*M*(n1-n0)*K; bytes = q8_0 weights (n1-n0)*K*34/32 + A rows
+    M*K*2 (fp16) + h written M*(n1-n0)/2*2 (fp16).  Routed experts: the grouped gate/up
+    GEMM over the C*k token-slots, flops 2*C*k*2*Fe*d, bytes = every expert's gate/up
+    weights + the gathered A rows + h.
+    Returns (flops, bytes, per-launch figures of the full-size chunk)."""
+    flops = bytes_ = 0.0
+    launches = 0
+    first = None
+    for s, e in chunks:
+        M = e - s
+        if w.n_expert:
+            Fe = w.expert_ffn_dim
+            f = 2.0 * M * w.n_expert_used * 2 * Fe * w.d_model
+            b = w.n_expert * 2 * Fe * w.d_model * 34 / 32 + M * w.n_expert_used * (w.d_model + Fe) * 2
+            flops += f
+            bytes_ += b
+            launches += 1
+            if first is None:
+                first = {"flops": f, "bytes": b, "rows": M}
+            continue
+        N = 2 * (-(-w.ffn_dim // 128) * 128)
+        K = w.d_model
+        _, parts = cpa.cp_test_gemm_plan(M, N, K)
+        for i, (n0, splits) in enumerate(parts):
+            n1 = parts[i + 1][0] if i + 1 < len(parts) else N
+            if splits > 1:
+                continue
+            f = 2.0 * M * (n1 - n0) * K
+            b = (n1 - n0) * K * 34 / 32 + M * K * 2 + M * (n1 - n0) // 2 * 2
+            flops += f
+            bytes_ += b
+            launches += 1
+            if first is None:
+                first = {"flops": f, "bytes": b, "rows": M}
+    first = dict(first or {"flops": 0.0, "bytes": 0.0, "rows": 0})
+    first["launches"] = launches
+    return flops, bytes_, first
+
+
+def measured_traffic(kernel, per_launch):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 PMC
+    readings (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or None when the
+    readings are absent or were taken on another version of the kernel's source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    r = rec.get(kernel)
+    if not r:
+        return None
+    h = hashlib.sha256()
+    for src in r.get("sources", []):
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != r.get("sources_sha256") or r.get("rows") != per_launch.get("rows"):
+        return None
+    return r.get("hbm_bytes_per_launch")
+
+
 def run_main(args, torch, cpa, synth):
     w = synth.WORKLOADS[args.workload]
     n, C = w.n_prompt, w.chunk
@@ -120,7 +187,9 @@ def run_main(args, torch, cpa, synth):
         step()
         torch.cuda.synchronize()
         note(f"warmup step {i + 1}/{args.warmup} done")
-    dom = "moe_gemm_gate_up" if w.n_expert else "gemm_gate_up"
+    # dominant kernel: the unsplit SwiGLU gate/up launch (one kernel per launch), or the
+    # grouped expert gate/up GEMM of a routed FFN
+    dom = "moe_gemm_gate_up" if w.n_expert else "gemm_gate_up/full"
     ctx.cp_kernel_timing(dom)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -133,23 +202,25 @@ def run_main(args, torch, cpa, synth):
     note(f"timed {args.steps} steps in {t1 - t0:.3f}s")
     total = t1 - t0
     tps = n * args.steps / total
-    # roofline of the dominant kernel (algorithmic flops of every timed launch)
-    if w.n_expert:
-        per_tok = 2.0 * w.n_expert_used * 2 * w.expert_ffn_dim * w.d_model
-    else:
-        per_tok = 2.0 * 2 * w.ffn_dim * w.d_model
-    dom_flops = per_tok * n * w.n_layer * args.steps
+    # roofline of the dominant kernel: algorithmic flops of every timed launch
+    dom_flops, dom_bytes, per_launch = dominant_work(w, cpa, chunks)
+    dom_flops *= w.n_layer * args.steps
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else 0.0
+    expect = per_launch["launches"] * w.n_layer * args.steps
+    if dom_launches != expect:
+        raise RuntimeError(f"timed {dom_launches} launches of {dom}, expected {expect}")
     # whole-prompt roofline: sum of per-chunk-layer bounds
     bound = sum(roofline_s(w, e - s, s) for s, e in chunks) * w.n_layer
     res = {
         "value": tps,
         "ms_per_step": total / args.steps * 1e3,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_F16_TFLOPS,
+                     "traffic": measured_traffic(dom, per_launch),
                      "launches": dom_launches, "avg_launch_us": dom_ms * 1e3 / max(1, dom_launches),
-                     "flops_per_token": per_tok},
+                     "flops_per_launch": per_launch["flops"],
+                     "algorithmic_bytes_per_launch": per_launch["bytes"]},
         "prompt_roofline": {"bound_ms_per_step": bound * 1e3,
                             "frac": bound / (total / args.steps)},
     }
@@ -207,7 +278,7 @@ def run_sweep(args, torch, cpa, synth, oracle_fit):
                            "tokens_per_s_per_layer": C / (t_layer * 1e-3),
                            "tokens_per_s_4_layers": C / (float(np.sum(table[(C, D)])) * 1e-3),
                            "roofline_frac": roofline_s(w, C, D) / (t_layer * 1e-3),
-                           "mfma_frac": chunk_flops(w, C, D) / (PEAK_BF16_TFLOPS * 1e12) / (t_layer * 1e-3)})
+                           "mfma_frac": chunk_flops(w, C, D) / (PEAK_F16_TFLOPS * 1e12) / (t_layer * 1e-3)})
     ctx.close()
     return {"workload": f"{w.name}: {w.n_layer} layers of the dense 27B-class shapes, f16 cache",
             "fit": fit, "points": points}
@@ -256,6 +327,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep-reps", type=int, default=5)
     ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB: the "
+                         "reference reading that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -268,6 +342,14 @@ def main():
         print("bench.py needs a GPU", flush=True)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_probe_mib > 0:
+        src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        note(f"copy probe: {args.copy_probe_mib} MiB device-to-device")
+        del src, dst
     w, res = run_main(args, torch, cpa, synth)
     sweep = None
     if not args.no_sweep:
@@ -277,7 +359,7 @@ def main():
         "metric": "prefill tokens/s at chunk C and KV depth (1 GPU); fitted b, a per layer",
         "value": res["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic (seeded N(0,0.02) q8_0 weights and hidden states)",
         "config": {"workload": f"{w.name}: {w.n_layer}-layer share, d_model {w.d_model}, "
                                f"{w.n_head}/{w.n_kv_head} heads, head_dim {w.head_dim}, "

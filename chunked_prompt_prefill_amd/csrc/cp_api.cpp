@@ -412,7 +412,7 @@ hipError_t timed(cp_ctx* c, const char* cls, F&& launch) {
   return e;
 }
 
-hipError_t gemm(cp_ctx* c, const char* cls, const __bf16* A, int lda, int M, const QMat& W,
+hipError_t gemm(cp_ctx* c, const char* cls, const _Float16* A, int lda, int M, const QMat& W,
                 int mode, void* out, int ldo) {
   const GemmPlan p = plan_gemm(M, W.N, W.K);
   return timed(c, cls, [&] {
@@ -422,7 +422,10 @@ hipError_t gemm(cp_ctx* c, const char* cls, const __bf16* A, int lda, int M, con
       g.wq = W.q; g.wd = W.d; g.mode = mode; g.out = out; g.ldo = ldo;
       g.splits = p.part[i].splits;
       g.partial = c->wsp<float>(c->WS.partial);
-      const hipError_t e = launch_gemm(g, 0, p.mt, c->stream);
+      // each launch is also timed on its own: "<class>/full" for an unsplit column range
+      // (one kernel), "<class>/split" for a split-K range (partial GEMM + ordered reduce)
+      const std::string sub = std::string(cls) + (g.splits > 1 ? "/split" : "/full");
+      const hipError_t e = timed(c, sub.c_str(), [&] { return launch_gemm(g, 0, p.mt, c->stream); });
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -433,10 +436,10 @@ int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int sta
   const Dims& D = c->D;
   const LayerW& L = c->layers[li];
   hipStream_t s = c->stream;
-  __bf16* xn = c->wsp<__bf16>(c->WS.xn);
+  _Float16* xn = c->wsp<_Float16>(c->WS.xn);
   float* qkv = c->wsp<float>(c->WS.qkv);
   _Float16* q = c->wsp<_Float16>(c->WS.q);
-  __bf16* attn = c->wsp<__bf16>(c->WS.attn);
+  _Float16* attn = c->wsp<_Float16>(c->WS.attn);
   const float* cos_t = c->wsp<float>(c->WS.cos);
   const float* sin_t = c->wsp<float>(c->WS.sin);
 
@@ -460,7 +463,7 @@ int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int sta
 
   if (!D.moe) {
     CP_HIP(c, timed(c, "rmsnorm", [&] { return launch_rmsnorm(x, L.ffn_norm, n, D.d, c->cfg.rms_eps, xn, nullptr, s); }), "rmsnorm");
-    __bf16* hbuf = c->wsp<__bf16>(c->WS.h);
+    _Float16* hbuf = c->wsp<_Float16>(c->WS.h);
     CP_HIP(c, gemm(c, "gemm_gate_up", xn, D.d, n, L.gu, GM_SWIGLU, hbuf, D.Fp), "gemm_gate_up");
     CP_HIP(c, gemm(c, "gemm_down", hbuf, D.Fp, n, L.dn, GM_F32_ADD, x, D.d), "gemm_down");
     return CP_OK;
@@ -477,7 +480,7 @@ int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int sta
   const int mt = 128;
   const int max_tiles = (int)(ceil_div((int64_t)n * D.k, mt) + D.E);
   CP_HIP(c, timed(c, "moe_permute", [&] { return launch_moe_permute(mb, n, D.E, D.k, mt, max_tiles, s); }), "moe_permute");
-  __bf16* hperm = c->wsp<__bf16>(c->WS.h);
+  _Float16* hperm = c->wsp<_Float16>(c->WS.h);
   float* yperm = c->wsp<float>(c->WS.yperm);
   GemmArgs g;
   g.A = xn; g.lda = D.d; g.a_rows = mb.perm; g.a_row_div = D.k;
@@ -894,7 +897,7 @@ int cp_test_gemm_ex(const void* A, const void* W, int32_t M, int32_t N, int32_t 
   const GemmPlan p = plan_gemm(M, N, K, splits, row_tile);
   for (int i = 0; i < p.nparts; ++i) {
     GemmArgs g;
-    g.A = (const __bf16*)A; g.lda = K; g.M = M; g.N = p.part[i].n1; g.K = K; g.n0 = p.part[i].n0;
+    g.A = (const _Float16*)A; g.lda = K; g.M = M; g.N = p.part[i].n1; g.K = K; g.n0 = p.part[i].n0;
     g.wq = q.q; g.wd = q.d;
     g.mode = mode; g.out = out; g.ldo = mode == GM_SWIGLU ? N / 2 : N;
     g.splits = p.part[i].splits;
@@ -938,7 +941,7 @@ int cp_test_attention(const void* q, const void* kv, int32_t n, int32_t start, i
   a.q = (const _Float16*)q;
   a.kv = kv_layer_at(const_cast<void*>(kv), n_kv_head, head_dim, nc, kv_type);
   a.n = n; a.start = start; a.n_head = n_head; a.n_kv_head = n_kv_head; a.head_dim = head_dim;
-  a.kv_type = kv_type; a.n_ctx = nc; a.out = (__bf16*)out;
+  a.kv_type = kv_type; a.n_ctx = nc; a.out = (_Float16*)out;
   a.splits = kv_splits > 0 ? kv_splits : attn_splits(D, n, start);
   a.part_o = (float*)scratch;
   a.part_ml = (float*)((uint8_t*)scratch + align_up((size_t)a.splits * n * n_head * head_dim * 4));

@@ -35,7 +35,7 @@ struct QMat {
 enum GemmMode : int32_t { GM_F32 = 0, GM_F32_ADD = 1, GM_SWIGLU = 2, GM_PARTIAL = 3 };
 
 struct GemmArgs {
-  const __bf16* A = nullptr;    // [rows][lda]
+  const _Float16* A = nullptr;    // [rows][lda]
   int32_t lda = 0;
   const int32_t* a_rows = nullptr;   // grouped: physical A row = a_rows[m] / a_row_div
   int32_t a_row_div = 1;
@@ -71,7 +71,7 @@ hipError_t launch_repack_q8_0(const void* src0, const void* src1, int64_t src_ro
 hipError_t launch_quantize_q8_0(const float* x, int64_t rows, int32_t k, int64_t ldx,
                                 void* out, hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, const float* gamma, int32_t n, int32_t d, float eps,
-                          __bf16* y, float* y32, hipStream_t s);
+                          _Float16* y, float* y32, hipStream_t s);
 
 struct KvLayer {          // one layer's cache (device pointers), capacity n_ctx
   void* k = nullptr;      // f16 [Hkv][n_ctx][hd]  | int8 [Hkv][n_ctx][hd]
@@ -95,7 +95,7 @@ struct AttnArgs {
   const _Float16* q = nullptr;   // [n][Hq][hd]
   KvLayer kv;
   int32_t n = 0, start = 0, n_head = 0, n_kv_head = 0, head_dim = 0, kv_type = 0, n_ctx = 0;
-  __bf16* out = nullptr;         // [n][Hq*hd]
+  _Float16* out = nullptr;         // [n][Hq*hd]
   int32_t splits = 1;
   float* part_o = nullptr;       // [splits][rows_total][hd]
   float* part_ml = nullptr;      // [splits][rows_total][2]

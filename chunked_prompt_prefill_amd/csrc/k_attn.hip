@@ -338,14 +338,14 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
   if (!row_ok) return;
   if (a.splits == 1) {
     const float inv_l = 1.0f / l;
-    __bf16* orow = a.out + ((int64_t)t_i * a.n_head + hq) * HD;
+    _Float16* orow = a.out + ((int64_t)t_i * a.n_head + hq) * HD;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int d0 = db * 32 + 8 * rq + 4 * h;
-        const uint2 pk = make_uint2(pack_bf16x2(o[db][4 * rq] * inv_l, o[db][4 * rq + 1] * inv_l),
-                                    pack_bf16x2(o[db][4 * rq + 2] * inv_l, o[db][4 * rq + 3] * inv_l));
+        const uint2 pk = make_uint2(pack_f16x2(o[db][4 * rq] * inv_l, o[db][4 * rq + 1] * inv_l),
+                                    pack_f16x2(o[db][4 * rq + 2] * inv_l, o[db][4 * rq + 3] * inv_l));
         *reinterpret_cast<uint2*>(orow + d0) = pk;
       }
   } else {
@@ -393,9 +393,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const float inv = 1.0f / den;
   const int64_t g = rg / R, i = rg % R;
   const int64_t t = i / G, hq = g * G + i % G;
-  __bf16* orow = a.out + (t * a.n_head + hq) * hd + d0;
-  *reinterpret_cast<uint2*>(orow) = make_uint2(pack_bf16x2(num.x * inv, num.y * inv),
-                                              pack_bf16x2(num.z * inv, num.w * inv));
+  _Float16* orow = a.out + (t * a.n_head + hq) * hd + d0;
+  *reinterpret_cast<uint2*>(orow) = make_uint2(pack_f16x2(num.x * inv, num.y * inv),
+                                              pack_f16x2(num.z * inv, num.w * inv));
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {

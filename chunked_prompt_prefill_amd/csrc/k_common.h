@@ -7,9 +7,6 @@
 
 namespace cp {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -25,35 +22,47 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float v) {
   return __builtin_bit_cast(uint16_t, (_Float16)v);   // IEEE round-to-nearest-even
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  f32x2 f = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
-}
-
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   f32x2 f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
 }
 
-// 16 signed bytes times a scale, exactly (|q| <= 128, d from fp16: the product fits in
-// float32), then rounded to bf16.  q is formed as ubyte(x ^ 0x80) - 128 so that each
-// value costs one byte convert and one fused multiply-add: u*d - 128*d == q*d exactly.
-__device__ __forceinline__ void dequant16_bf16(uint4 raw, float d, uint4& lo, uint4& hi) {
-  const float nd = -128.0f * d;
-  uint32_t w[4] = {raw.x ^ 0x80808080u, raw.y ^ 0x80808080u, raw.z ^ 0x80808080u,
-                   raw.w ^ 0x80808080u};
+// Two int8 weights as exact fp16 integers: byte b of x (x = raw ^ 0x80808080, so b is
+// the weight + 128) becomes the fp16 bit pattern 0x64bb = 1024 + b, and subtracting 1152
+// leaves the weight itself (every integer below 2048 is exact in fp16).  sel picks the two
+// bytes (v_perm_b32: bytes 0-3 from x, byte 4 = 0x64 from the constant).
+__device__ __forceinline__ f16x2 q8_pair_f16(uint32_t x, uint32_t sel) {
+  const uint32_t bits = __builtin_amdgcn_perm(0x64646464u, x, sel);
+  const f16x2 big = __builtin_bit_cast(f16x2, bits);
+  const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  return big - off;
+}
+
+// 4 int8 weights (one dword) times the block's fp16 scale d -> two packed fp16 pairs, each
+// the correctly rounded fp16 of d*q (one packed fp16 multiply of exact operands).
+__device__ __forceinline__ void dequant4_f16(uint32_t raw, f16x2 d2, uint32_t& lo, uint32_t& hi) {
+  const uint32_t x = raw ^ 0x80808080u;
+  lo = __builtin_bit_cast(uint32_t, q8_pair_f16(x, 0x04010400u) * d2);
+  hi = __builtin_bit_cast(uint32_t, q8_pair_f16(x, 0x04030402u) * d2);
+}
+
+// 16 signed bytes times a block scale (fp16 bits) -> 16 fp16 in two uint4, in byte order.
+__device__ __forceinline__ void dequant16_f16(uint4 raw, uint32_t d_bits, uint4& lo, uint4& hi) {
+  const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)d_bits);
+  const f16x2 d2 = {d, d};
   uint32_t o[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float f0 = fmaf((float)(w[i] & 0xFFu), d, nd);
-    float f1 = fmaf((float)((w[i] >> 8) & 0xFFu), d, nd);
-    float f2 = fmaf((float)((w[i] >> 16) & 0xFFu), d, nd);
-    float f3 = fmaf((float)(w[i] >> 24), d, nd);
-    o[2 * i] = pack_bf16x2(f0, f1);
-    o[2 * i + 1] = pack_bf16x2(f2, f3);
-  }
+  dequant4_f16(raw.x, d2, o[0], o[1]);
+  dequant4_f16(raw.y, d2, o[2], o[3]);
+  dequant4_f16(raw.z, d2, o[4], o[5]);
+  dequant4_f16(raw.w, d2, o[6], o[7]);
   lo = make_uint4(o[0], o[1], o[2], o[3]);
   hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// float -> fp16 for stored activations that are not bounded by construction (the SwiGLU
+// product): saturated to the finite fp16 range, then rounded to nearest even.
+__device__ __forceinline__ _Float16 f16_sat(float v) {
+  return (_Float16)__builtin_amdgcn_fmed3f(v, -65504.0f, 65504.0f);
 }
 
 // 8 signed bytes (two dwords) times per-element float scales -> 8 f16 (one uint4).

@@ -106,11 +106,11 @@ hipError_t launch_quantize_q8_0(const float* x, int64_t rows, int32_t k, int64_t
 }
 
 // ======================================================================================
-// RMSNorm: y = x / sqrt(mean(x^2) + eps) * gamma  -> bf16 (and optionally float32)
+// RMSNorm: y = x / sqrt(mean(x^2) + eps) * gamma  -> fp16 (and optionally float32)
 // ======================================================================================
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
                                                       const float* __restrict__ gamma, int32_t d,
-                                                      float eps, __bf16* __restrict__ y,
+                                                      float eps, _Float16* __restrict__ y,
                                                       float* __restrict__ y32) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
@@ -131,14 +131,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
     const float4 gm = *reinterpret_cast<const float4*>(gamma + i);
     const float a = v.x * scale * gm.x, b = v.y * scale * gm.y;
     const float c = v.z * scale * gm.z, e = v.w * scale * gm.w;
-    uint2 pk = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, e));
+    uint2 pk = make_uint2(pack_f16x2(a, b), pack_f16x2(c, e));
     *reinterpret_cast<uint2*>(y + row * d + i) = pk;
     if (y32) *reinterpret_cast<float4*>(y32 + row * d + i) = make_float4(a, b, c, e);
   }
 }
 
 hipError_t launch_rmsnorm(const float* x, const float* gamma, int32_t n, int32_t d, float eps,
-                          __bf16* y, float* y32, hipStream_t s) {
+                          _Float16* y, float* y32, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(n), dim3(256), 0, s, x, gamma, d, eps, y, y32);
   return hipGetLastError();

@@ -1,6 +1,6 @@
-// q8_0-weight GEMM on bf16 MFMA (gfx950), fp32 accumulate.
+// q8_0-weight GEMM on fp16 MFMA (gfx950), fp32 accumulate.
 //
-//   out[m][n] = sum_k A[m][k] * W[n][k],  A bf16 activations, W q8_0 blocks of 32.
+//   out[m][n] = sum_k A[m][k] * W[n][k],  A fp16 activations, W q8_0 blocks of 32.
 //
 // This kernel takes row tiles of 64 and 128 (two workgroups per CU) and the grouped
 // expert GEMMs; 256-row tiles run the deeper-pipelined kernel in k_gemm_big.hip.
@@ -9,20 +9,22 @@
 // owns 64 columns (two 32-column MFMA blocks) across all MT rows, so every weight
 // element is dequantised exactly once per workgroup.  Per 128-wide K stage (4 q8_0
 // blocks):
-//   * A: MT x 128 bf16 staged in LDS by asynchronous global->LDS loads (16 bytes per
+//   * A: MT x 128 fp16 staged in LDS by asynchronous global->LDS loads (16 bytes per
 //     lane, landing in lane order), double buffered; the 16-byte chunks of a row are
 //     XOR-swizzled by the row so the 32 rows an MFMA operand spans hit distinct banks.
 //     The swizzle is applied by choosing each lane's source address.
 //   * W: loaded straight into registers one stage ahead from the repacked layout (1 KiB
 //     contiguous per wave per 32-row group and block, already in MFMA lane order),
-//     dequantised in registers (d*q exact in fp32, rounded to bf16) as the B operand.
+//     dequantised in registers as the B operand: each int8 becomes an exact fp16
+//     integer by a byte permute and a packed add, and one packed fp16 multiply by the
+//     block scale gives the correctly rounded fp16 of d*q.
 // The K index inside a q8_0 block is permuted consistently on both operands so that a
 // lane's 16 weight bytes are contiguous: lane half h, MFMA step s, element c <-> block
 // column 16h + 8s + c.
 // Rows beyond M and columns beyond N are computed from clamped (valid) addresses and
 // simply not stored, so the main loop has no branches.
 // Epilogues: fp32 store, fp32 residual add, SwiGLU (gate/up columns interleaved in
-// 32-column groups) to bf16, or split-K partials summed by a separate kernel in split
+// 32-column groups) to fp16, or split-K partials summed by a separate kernel in split
 // order (deterministic: no float atomics).  A launch may cover a column range [n0, N)
 // so that the host can run the tiles that fill whole rounds of the chip without
 // splitting and split only the tail.
@@ -160,8 +162,7 @@ __global__ __launch_bounds__(256, MinBlocks<MI>::v) void gemm_q8_kernel(GemmArgs
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
         const uint32_t pair = (kb < 2) ? rs[ni].x : rs[ni].y;
-        const float d = half_bits_to_float((kb & 1) ? (pair >> 16) : (pair & 0xFFFFu));
-        dequant16_bf16(rb[ni][kb], d, b[ni][0], b[ni][1]);
+        dequant16_f16(rb[ni][kb], (kb & 1) ? (pair >> 16) : (pair & 0xFFFFu), b[ni][0], b[ni][1]);
       }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -169,11 +170,11 @@ __global__ __launch_bounds__(256, MinBlocks<MI>::v) void gemm_q8_kernel(GemmArgs
         for (int mi = 0; mi < MI; ++mi) {
           const int c = kb * 4 + 2 * h + s;
           const uint4 a = sA[buf][(mi * 32 + l32) * CPR + (c ^ (l32 & 15))];
-          const bf16x8 av = __builtin_bit_cast(bf16x8, a);
-          acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, b[0][s]),
-                                                               acc[mi][0], 0, 0, 0);
-          acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, b[1][s]),
-                                                               acc[mi][1], 0, 0, 0);
+          const f16x8 av = __builtin_bit_cast(f16x8, a);
+          acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, __builtin_bit_cast(f16x8, b[0][s]),
+                                                              acc[mi][0], 0, 0, 0);
+          acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, __builtin_bit_cast(f16x8, b[1][s]),
+                                                              acc[mi][1], 0, 0, 0);
         }
       }
     }
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(256, MinBlocks<MI>::v) void gemm_q8_kernel(GemmArgs
         if (!col_ok0) continue;
         const int f = (n_wave >> 1) + l32;
         const float gte = acc[mi][0][e], up = acc[mi][1][e];
-        reinterpret_cast<__bf16*>(g.out)[row * g.ldo + f] = (__bf16)(silu(gte) * up);
+        reinterpret_cast<_Float16*>(g.out)[row * g.ldo + f] = f16_sat(silu(gte) * up);
       } else {
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
@@ -264,11 +265,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
       gs.x += a.x; gs.y += a.y; gs.z += a.z; gs.w += a.w;
       us.x += b.x; us.y += b.y; us.z += b.z; us.w += b.w;
     }
-    __bf16* o = reinterpret_cast<__bf16*>(out) + row * ldo + n0 / 2 + c4;
-    o[0] = (__bf16)(silu(gs.x) * us.x);
-    o[1] = (__bf16)(silu(gs.y) * us.y);
-    o[2] = (__bf16)(silu(gs.z) * us.z);
-    o[3] = (__bf16)(silu(gs.w) * us.w);
+    _Float16* o = reinterpret_cast<_Float16*>(out) + row * ldo + n0 / 2 + c4;
+    o[0] = f16_sat(silu(gs.x) * us.x);
+    o[1] = f16_sat(silu(gs.y) * us.y);
+    o[2] = f16_sat(silu(gs.z) * us.z);
+    o[3] = f16_sat(silu(gs.w) * us.w);
     return;
   }
   float4 acc = *reinterpret_cast<const float4*>(partial + row * pn + c4);

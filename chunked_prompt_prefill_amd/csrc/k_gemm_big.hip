@@ -1,16 +1,17 @@
-// q8_0-weight GEMM on bf16 MFMA (gfx950) for 256-row tiles, fp32 accumulate.
+// q8_0-weight GEMM on fp16 MFMA (gfx950) for 256-row tiles, fp32 accumulate.
 //
-//   out[m][n] = sum_k A[m][k] * W[n][k],  A bf16 activations, W q8_0 blocks of 32.
+//   out[m][n] = sum_k A[m][k] * W[n][k],  A fp16 activations, W q8_0 blocks of 32.
 //
 // One workgroup of 4 waves per CU owns a 256 x 256 output tile; each wave owns 64 columns
 // (two 32-column MFMA blocks) over all 256 rows, i.e. 256 fp32 accumulators per lane in
 // the AGPRs.  A weight is dequantised once per workgroup and feeds 256 rows, so the
-// dequantisation (one byte convert, one FMA and half a bf16 pack per weight) is about a
-// third of the MFMA issue time and hides under it.
+// dequantisation (per two weights: a byte permute that makes them exact fp16 integers, a
+// packed add and a packed multiply by the fp16 block scale, correctly rounded) hides
+// under the MFMA issue time.
 //
 // Every operand travels global -> LDS by asynchronous loads (no register staging), in
 // 64-wide K stages (two q8_0 blocks) through three LDS buffers:
-//   * A: 256 x 64 bf16 (32 KiB), the eight 16-byte chunks of a row XOR-swizzled by the
+//   * A: 256 x 64 fp16 (32 KiB), the eight 16-byte chunks of a row XOR-swizzled by the
 //     row so that the 16 rows a 16-byte LDS read serves per pass hit distinct banks
 //     (the swizzle is chosen through each lane's source address);
 //   * W: each wave's 64 columns x 64 K int8 (4 KiB) in the repacked lane order, and their
@@ -29,7 +30,7 @@
 // lane's 16 weight bytes are contiguous: lane half h, MFMA step s, element c <-> block
 // column 16h + 8s + c.  Rows beyond M and columns beyond N are computed from clamped
 // (valid) addresses and not stored.  Epilogues as in the smaller-tile kernel: fp32 store,
-// fp32 residual add, SwiGLU to bf16, or split-K partials.
+// fp32 residual add, SwiGLU to fp16, or split-K partials.
 #include <type_traits>
 #include <utility>
 
@@ -189,29 +190,31 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_big_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
 
-  // Dequantised B of one block: dq[ni][s] = the 8 bf16 that MFMA step s of column block
+  // Dequantised B of one block: dq[ni][s] = the 8 fp16 that MFMA step s of column block
   // ni takes.  Two sets alternate: one block's MFMAs read one set while the VALU fills the
   // other for the next block.
   typedef uint4 Deq[2][2];
   Deq dq0, dq1;
 
   // Half-piece p (0..15) of dequantising a block: column block ni = p/8, byte pair
-  // (p%8) of the 16 bytes -> two bf16 (one dword of dq[ni][p%8/4]).  valid == false (a
+  // (p%8) of the 16 bytes -> two fp16 (one dword of dq[ni][p%8/4]).  valid == false (a
   // padding stage) uses scale 0: the block's B is exactly zero.
-  float dsc[2], dnd[2];
+  f16x2 dsc[2];
+  uint32_t xq[2];
   auto deq_piece = [&](auto P, int kb, const Raw& w, bool valid, Deq& dq) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
     constexpr int ni = p / 8, pp = p % 8, dw = pp / 2, hf = pp % 2;
     if constexpr (pp == 0) {
-      const float d = half_bits_to_float(kb ? (w.sc[ni] >> 16) : (w.sc[ni] & 0xFFFFu));
-      dsc[ni] = valid ? d : 0.0f;
-      dnd[ni] = -128.0f * dsc[ni];
+      const uint32_t bits = valid ? (kb ? (w.sc[ni] >> 16) : (w.sc[ni] & 0xFFFFu)) : 0u;
+      const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)bits);
+      dsc[ni] = f16x2{d, d};
     }
-    const uint4 q = w.q[ni][kb];
-    const uint32_t x = (dw == 0 ? q.x : dw == 1 ? q.y : dw == 2 ? q.z : q.w) ^ 0x80808080u;
-    const float f0 = fmaf((float)((x >> (16 * hf)) & 0xFFu), dsc[ni], dnd[ni]);
-    const float f1 = fmaf((float)((x >> (16 * hf + 8)) & 0xFFu), dsc[ni], dnd[ni]);
-    const uint32_t packed = pack_bf16x2(f0, f1);
+    if constexpr (hf == 0) {
+      const uint4 q = w.q[ni][kb];
+      xq[ni] = (dw == 0 ? q.x : dw == 1 ? q.y : dw == 2 ? q.z : q.w) ^ 0x80808080u;
+    }
+    const uint32_t packed =
+        __builtin_bit_cast(uint32_t, q8_pair_f16(xq[ni], hf ? 0x04030402u : 0x04010400u) * dsc[ni]);
     uint4& o = dq[ni][dw >> 1];
     const int comp = (dw & 1) * 2 + hf;
     if (comp == 0) o.x = packed;
@@ -239,9 +242,9 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_big_kernel(GemmArgs g) {
       constexpr int t = decltype(T)::value;
       if constexpr (decltype(ISS)::value && t < BNLOAD) issue_piece(JI, T, iks, wi);
       constexpr int mi = t % 8, st = t / 8;
-      const bf16x8 av = __builtin_bit_cast(bf16x8, af[t % 4]);
-      acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, dq[0][st]), acc[mi][0], 0, 0, 0);
-      acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, dq[1][st]), acc[mi][1], 0, 0, 0);
+      const f16x8 av = __builtin_bit_cast(f16x8, af[t % 4]);
+      acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, __builtin_bit_cast(f16x8, dq[0][st]), acc[mi][0], 0, 0, 0);
+      acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, __builtin_bit_cast(f16x8, dq[1][st]), acc[mi][1], 0, 0, 0);
       if constexpr (t + 3 < 16) af[(t + 3) % 4] = frag(J, kb, t + 3);
       else if constexpr (decltype(NEXTA)::value) af[(t + 3) % 4] = frag(J, kb + 1, t + 3 - 16);
       else af[(t + 3) % 4] = frag(std::integral_constant<int, (decltype(J)::value + 1) % NBUFA>(), 0, t + 3 - 16);
@@ -332,7 +335,7 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_big_kernel(GemmArgs g) {
         if (!col_ok0) continue;
         const int f = (n_wave >> 1) + l32;
         const float gte = acc[mi][0][e], up = acc[mi][1][e];
-        reinterpret_cast<__bf16*>(g.out)[row * g.ldo + f] = (__bf16)(silu(gte) * up);
+        reinterpret_cast<_Float16*>(g.out)[row * g.ldo + f] = f16_sat(silu(gte) * up);
       } else {
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {

@@ -15,6 +15,14 @@
  * There is no final norm and no LM head: the chunk's output is the residual stream
  * after the last layer.
  *
+ * Arithmetic.  The residual stream, norms, RoPE and softmax are float32.  Every matrix
+ * product (the q8_0 projections and both attention products) runs on fp16 MFMA with
+ * float32 accumulation: activations are rounded to fp16 and each q8_0 weight enters as
+ * the correctly rounded fp16 of d*q.  fp16 runs at the bf16 rate on gfx950 and keeps 3
+ * more mantissa bits, which is what holds a full-size layer within 1e-2 of a float64
+ * evaluation (max|delta| / max|ref|).  The SwiGLU product is saturated to +-65504
+ * before its fp16 rounding.
+ *
  * Conventions shared by every call.
  *   - "dev" pointers are device (HBM) addresses, "host" pointers are host memory.
  *   - The caller owns every buffer: weights, arenas, cache, workspace, inputs and
@@ -170,7 +178,10 @@ void prefill_free(cp_ctx* ctx);   /* releases host-side state only; buffers stay
  * returns the summed duration (ms) and launch count since the last cp_kernel_timing()
  * call.  Classes: "gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attention",
  * "rope_kv_append", "rmsnorm", "moe_route", "moe_permute", "moe_gemm_gate_up",
- * "moe_gemm_down", "moe_unpermute". */
+ * "moe_gemm_down", "moe_unpermute".  A dense GEMM class runs as one or two launches over
+ * column ranges; each launch is also its own class, "<gemm class>/full" for an unsplit
+ * range (one kernel launch) and "<gemm class>/split" for a split-K range (the partial
+ * GEMM and its ordered reduce), e.g. "gemm_gate_up/full". */
 int cp_kernel_timing(cp_ctx* ctx, const char* classes);
 int cp_kernel_times(cp_ctx* ctx, const char* kernel_class, float* total_ms, int32_t* launches);
 
@@ -218,10 +229,10 @@ int cp_test_router(const float* y, const void* w_router, int32_t n, int32_t d, i
                    int32_t k, float* logits, int32_t* idx, float* weight, void* scratch,
                    void* hip_stream);
 
-/* One q8_0 GEMM as the layer runs it: out = A * W^T with A bf16 [M][K] (lda = K,
+/* One q8_0 GEMM as the layer runs it: out = A * W^T with A fp16 [M][K] (lda = K,
  * K % 128 == 0), W in the interchange layout [N][K] (N % 32 == 0).  mode 0: out float32
  * [M][N] = result; mode 1: out float32 [M][N] += result; mode 2 (SwiGLU): W holds gate rows
- * then up rows ([2F][K], F % 32 == 0) and out is bf16 [M][F] = silu(gate) * up.  splits > 0
+ * then up rows ([2F][K], F % 32 == 0) and out is fp16 [M][F] = silu(gate) * up.  splits > 0
  * forces one launch with that split-K factor and a deterministic reduction (0 = the
  * layer's own launch plan, cp_test_gemm_plan).  scratch: dev
  * buffer of cp_test_gemm_scratch_bytes(M, N, K, splits) bytes (repacked weights and
@@ -243,7 +254,7 @@ int cp_test_gemm_ex(const void* A, const void* W, int32_t M, int32_t N, int32_t 
 
 /* Causal flash attention of a chunk against a one-layer cache (rows already appended):
  * q: f16 [n][n_head][head_dim]; kv: one-layer cache (capacity n_ctx) holding positions
- * 0 .. start+n-1; out: bf16 [n][n_head*head_dim].  kv_splits > 0 forces that many
+ * 0 .. start+n-1; out: fp16 [n][n_head*head_dim].  kv_splits > 0 forces that many
  * KV-range splits (0 = the library's choice).  scratch: dev buffer of
  * cp_test_attention_scratch_bytes(...) bytes. */
 size_t cp_test_attention_scratch_bytes(int32_t n, int32_t n_head, int32_t head_dim,

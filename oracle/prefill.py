@@ -160,6 +160,17 @@ class OracleModel:
         cs, sn = cos[positions], sin[positions]
         return rope_apply_f32(q, cs, sn), rope_apply_f32(k, cs, sn), v
 
+    def kv_rows(self, l: int, x: np.ndarray, positions: np.ndarray):
+        """RMSNorm -> k/v projections -> RoPE of k (float32) for rows at `positions`:
+        the K/V half of qkv_rows, for rows whose query is not needed."""
+        c, W = self.cfg, self.weights(l)
+        n, hd = x.shape[0], c.head_dim
+        y = rmsnorm(x, W["attn_norm"], c.rms_eps)
+        k = (y @ W["wk"].T).astype(np.float32).reshape(n, c.n_kv_head, hd)
+        v = (y @ W["wv"].T).astype(np.float32).reshape(n, c.n_kv_head, hd)
+        cos, sin = self.rope(int(np.max(positions)) + 1)
+        return rope_apply_f32(k, cos[positions], sin[positions]), v
+
     def attn_out_rows(self, l: int, x: np.ndarray, q32: np.ndarray, K: np.ndarray, V: np.ndarray,
                       positions: np.ndarray) -> np.ndarray:
         """Attention of rows q32 against cache values K/V, then x + o W_o^T."""
@@ -167,14 +178,8 @@ class OracleModel:
         o = attention(q32, K, V, positions)
         return np.asarray(x, np.float64) + o.reshape(x.shape[0], -1) @ W["wo"].T
 
-    def ffn_rows(self, l: int, x: np.ndarray, return_routing: bool = False, route_idx=None):
-        """x + FFN(RMSNorm(x)): dense SwiGLU, or routed experts.
-
-        route_idx: optional [n][k] expert indices to combine instead of the oracle's own
-        top-k (weights are still the softmax of the oracle's logits over those experts).
-        Callers pass it only for an index set they have checked is a top-k set of the
-        oracle's logits up to a stated tolerance (near ties make several sets correct).
-        """
+    def ffn_rows(self, l: int, x: np.ndarray, return_routing: bool = False):
+        """x + FFN(RMSNorm(x)): dense SwiGLU, or routed experts (the oracle's own top-k)."""
         c, W = self.cfg, self.weights(l)
         y = rmsnorm(x, W["ffn_norm"], c.rms_eps)
         if not c.n_expert:
@@ -184,15 +189,10 @@ class OracleModel:
         d16, q = q8_0_from_bytes(self.layers[l]["w_router"], nb)
         r = router_logits_ordered(y.astype(np.float32), d16, q)
         idx, w = moe_route(r, c.n_expert_used)
-        if route_idx is not None:
-            idx = np.asarray(route_idx, dtype=np.int32)
-            sel = np.take_along_axis(r, idx, axis=1).astype(np.float64)
-            e = np.exp(sel - sel.max(axis=1, keepdims=True))
-            w = e / e.sum(axis=1, keepdims=True)
         out = x + moe_ffn(y, idx, w, W["w_gate"], W["w_up"], W["w_down"])
         return (out, (r, idx, w)) if return_routing else out
 
-    def layer(self, l: int, x: np.ndarray, cache: OracleCache, start: int, route_idx=None,
+    def layer(self, l: int, x: np.ndarray, cache: OracleCache, start: int,
               routing_out: Optional[List] = None) -> np.ndarray:
         """One layer over rows at positions start .. start+n-1 (append, then attend)."""
         n = x.shape[0]
@@ -200,10 +200,34 @@ class OracleModel:
         q32, k32, v32 = self.qkv_rows(l, x, pos)
         cache.write(l, start, k32, v32)
         x = self.attn_out_rows(l, x, q32, cache.kval[l], cache.vval[l], pos)
-        out, routing = self.ffn_rows(l, x, return_routing=True, route_idx=route_idx)
+        out, routing = self.ffn_rows(l, x, return_routing=True)
         if routing_out is not None:
             routing_out.append(routing)
         return out
+
+    def layer_rows(self, l: int, x: np.ndarray, rows, block: int = 2048):
+        """Layer l over the prompt x (row t at position t), evaluated at the rows `rows` only.
+
+        Attention of a row reads only cache rows at or before its own position, so K/V are
+        computed and stored (in the cache's type) for every position up to max(rows), while
+        q, attention, the output projection and the FFN run for `rows` alone.  This is
+        `layer` restricted to those rows; it lets long prompts be checked at sampled rows.
+        Returns (outputs [len(rows)][d] float64, the cache holding rows 0 .. max(rows) of
+        layer l)."""
+        rows = np.asarray(rows, dtype=np.int64)
+        T = int(rows.max()) + 1
+        cache = self.new_cache(T)
+        self.rope(T)    # one table for every position, instead of regrowing it per block
+        for r0 in range(0, T, block):
+            r1 = min(T, r0 + block)
+            k32, v32 = self.kv_rows(l, x[r0:r1], np.arange(r0, r1))
+            cache.write(l, r0, k32, v32)
+        xr = np.asarray(x[rows], dtype=np.float64)
+        q32, _, _ = self.qkv_rows(l, xr, rows)
+        h = self.attn_out_rows(l, xr, q32, cache.kval[l], cache.vval[l], rows)
+        out, routing = self.ffn_rows(l, h, return_routing=True)
+        self.last_routing = routing    # (logits, indices, weights) of the rows, routed layers
+        return out, cache
 
     # -- drivers ------------------------------------------------------------------------
     def forward_chunk(self, x: np.ndarray, cache: OracleCache) -> np.ndarray:
@@ -228,18 +252,17 @@ class OracleModel:
 
     def prefill_layer_major(self, x: np.ndarray, cache: Optional[OracleCache] = None,
                             n_ctx: Optional[int] = None, layer_outputs: Optional[List] = None,
-                            routes: Optional[Sequence] = None,
                             routing_out: Optional[List] = None) -> np.ndarray:
         """Layer-major driver: the whole prompt through layer 0, then layer 1, ...
 
-        routes: optional per-layer expert index sets (see ffn_rows); routing_out collects
-        each layer's (logits, indices, weights)."""
+        layer_outputs collects each layer's output; routing_out collects each routed
+        layer's (logits, indices, weights)."""
         if cache is None:
             cache = self.new_cache(n_ctx or x.shape[0])
         start = cache.n_past
         h = np.asarray(x, dtype=np.float64)
         for l in range(self.cfg.n_layer):
-            h = self.layer(l, h, cache, start, None if routes is None else routes[l], routing_out)
+            h = self.layer(l, h, cache, start, routing_out)
             if layer_outputs is not None:
                 layer_outputs.append(h.copy())
         cache.n_past = start + x.shape[0]

@@ -17,6 +17,7 @@ any device.
 """
 from __future__ import annotations
 
+import os
 import zlib
 from dataclasses import dataclass, field, replace
 from typing import Dict, List, Optional, Tuple
@@ -61,15 +62,28 @@ def _index_np(seed: int, start: int, n: int) -> np.ndarray:
     return (z >> np.uint64(64 - TABLE_BITS)).astype(np.int64)
 
 
-def normal(seed: int, shape, scale: float = 0.02, block: int = 1 << 24) -> np.ndarray:
-    """float32 array of `shape` with N(0, scale) values for `seed` (NumPy)."""
+def normal(seed: int, shape, scale: float = 0.02, block: int = 1 << 20) -> np.ndarray:
+    """float32 array of `shape` with N(0, scale) values for `seed` (NumPy).
+
+    Every value depends only on (seed, element index), so the blocks are filled by a
+    thread pool (NumPy releases the GIL in these loops) with the same result."""
+    from concurrent.futures import ThreadPoolExecutor
     n = int(np.prod(shape))
     tab = normal_table()
     out = np.empty(n, dtype=np.float32)
     s32 = np.float32(scale)
-    for s in range(0, n, block):
+
+    def fill(s):
         m = min(block, n - s)
         np.multiply(tab[_index_np(seed, s, m)], s32, out=out[s:s + m])
+
+    starts = range(0, n, block)
+    if len(starts) <= 1:
+        for s in starts:
+            fill(s)
+    else:
+        with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, starts))
     return out.reshape(shape)
 
 

@@ -23,3 +23,26 @@ def fp32_layers(w: synth.Workload, gains: str = "random"):
 
 def q8_layers(w: synth.Workload, gains: str = "random"):
     return [oracle.quantize_layer(t) for t in fp32_layers(w, gains)]
+
+
+def _encode_rows_blocked(t: np.ndarray, rows_per_block: int = 256) -> np.ndarray:
+    """oracle.q8_0_encode_bytes over row blocks in a thread pool.  Each row is encoded on
+    its own, so the bytes equal one call over the whole tensor; blocking keeps the
+    working set in cache, which is what makes full-size layers take seconds."""
+    from concurrent.futures import ThreadPoolExecutor
+    import os
+    flat = t.reshape(-1, t.shape[-1])
+    starts = range(0, flat.shape[0], rows_per_block)
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        parts = list(ex.map(lambda s: oracle.q8_0_encode_bytes(flat[s:s + rows_per_block]), starts))
+    out = np.concatenate(parts, axis=0)
+    return out.reshape(t.shape[:-1] + (out.shape[-1],))
+
+
+def q8_layer_full(w: synth.Workload, l: int, gains: str = "ones"):
+    """Layer l of a full-size workload as interchange bytes, encoded by the oracle."""
+    out = {}
+    for name, shp in synth.weight_shapes(w):
+        t = synth.layer_weight(w, l, name, shp, gains=gains)
+        out[name] = t if name.endswith("_norm") else _encode_rows_blocked(t)
+    return out

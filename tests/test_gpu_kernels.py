@@ -93,8 +93,20 @@ def test_rope_kv_append_bit_exact(torch, cpa, kv, hd, Hq, Hkv, n, start):
 
 
 # --------------------------------------------------------------------------- GEMM
-def bf16_round(torch, a: np.ndarray) -> np.ndarray:
-    return torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+def f16_round(a: np.ndarray) -> np.ndarray:
+    return a.astype(np.float16).astype(np.float32)
+
+
+def gemm_bound(A, Wd, ref, K, mode):
+    """Per-element error bound of the fp16-operand GEMM: each dequantised weight is the
+    correctly rounded fp16 of d*q (relative 2^-11, or 2^-25 absolute when it lands in the
+    subnormal range), fp16 x fp16 products are exact in float32, and float32 accumulation
+    over K terms adds (K+2) * 2^-24 of sum_k |a_k w_k|; mode 1 adds one final rounding."""
+    a = np.abs(A.astype(np.float64))
+    mag = a @ np.abs(Wd).T
+    sub = a.sum(axis=1, keepdims=True) * 2.0 ** -25
+    return ((2.0 ** -11 * 1.001 + (K + 2) * 2.0 ** -24) * mag + sub +
+            (np.abs(ref) * 2.0 ** -23 if mode == 1 else 0))
 
 
 @pytest.mark.parametrize("M,N,K,splits", [(1, 256, 256, 0), (57, 512, 256, 0), (128, 5120, 512, 0),
@@ -102,22 +114,19 @@ def bf16_round(torch, a: np.ndarray) -> np.ndarray:
                                           (64, 7168, 5120, 0), (1000, 256, 17408, 0),
                                           (512, 7168, 5120, 0), (2048, 5120, 5120, 0)])
 @pytest.mark.parametrize("mode", [0, 1])
-def test_gemm_q8_0_within_bf16_bound(torch, cpa, M, N, K, splits, mode):
+def test_gemm_q8_0_within_f16_bound(torch, cpa, M, N, K, splits, mode):
     log(f"gemm M={M} N={N} K={K} splits={splits} mode={mode} plan={cpa.cp_test_gemm_plan(M, N, K)}")
-    A = bf16_round(torch, synth.normal(synth.tensor_seed("A", M, K), (M, K), scale=1.0))
+    A = f16_round(synth.normal(synth.tensor_seed("A", M, K), (M, K), scale=1.0))
     W = synth.normal(synth.tensor_seed("W", N, K), (N, K))
     Wb = oracle.q8_0_encode_bytes(W)
     Wd = oracle.q8_0_decode_bytes(Wb, K).astype(np.float64)
     X0 = synth.normal(synth.tensor_seed("X0", M, N), (M, N), scale=1.0)
     out = torch.from_numpy(X0.copy() if mode == 1 else np.zeros((M, N), np.float32)).cuda()
-    At = torch.from_numpy(A).cuda().to(torch.bfloat16)
+    At = torch.from_numpy(A).cuda().to(torch.float16)
     cpa.cp_test_gemm(At, torch.from_numpy(Wb).cuda(), M, N, K, mode, splits, out)
     got = out.cpu().numpy().astype(np.float64)
     ref = A.astype(np.float64) @ Wd.T + (X0.astype(np.float64) if mode == 1 else 0.0)
-    # bound: bf16 rounding of each dequantised weight (2^-9 relative) plus float32
-    # accumulation over K terms, on sum_k |a_k w_k|; plus the final add for mode 1
-    mag = np.abs(A.astype(np.float64)) @ np.abs(Wd).T
-    bound = (2.0 ** -9 * 1.001 + (K + 2) * 2.0 ** -24) * mag + (np.abs(ref) * 2.0 ** -23 if mode == 1 else 0)
+    bound = gemm_bound(A, Wd, ref, K, mode)
     err = np.abs(got - ref)
     log(f"  max rel err {rel_err(got, ref):.3e}, worst err/bound {np.max(err / (bound + 1e-30)):.3f}")
     assert np.all(err <= bound + 1e-30)
@@ -132,18 +141,17 @@ def test_gemm_q8_0_row_tiles(torch, cpa, M, N, K, splits, mode, row_tile):
     """Both GEMM kernels with the row tile pinned: ragged M and N, K stage counts that are
     and are not multiples of the 256-row kernel's three-stage pipeline, split-K."""
     log(f"gemm row_tile={row_tile} M={M} N={N} K={K} splits={splits} mode={mode}")
-    A = bf16_round(torch, synth.normal(synth.tensor_seed("A", M, K), (M, K), scale=1.0))
+    A = f16_round(synth.normal(synth.tensor_seed("A", M, K), (M, K), scale=1.0))
     W = synth.normal(synth.tensor_seed("W", N, K), (N, K))
     Wb = oracle.q8_0_encode_bytes(W)
     Wd = oracle.q8_0_decode_bytes(Wb, K).astype(np.float64)
     X0 = synth.normal(synth.tensor_seed("X0", M, N), (M, N), scale=1.0)
     out = torch.from_numpy(X0.copy() if mode == 1 else np.zeros((M, N), np.float32)).cuda()
-    At = torch.from_numpy(A).cuda().to(torch.bfloat16)
+    At = torch.from_numpy(A).cuda().to(torch.float16)
     cpa.cp_test_gemm(At, torch.from_numpy(Wb).cuda(), M, N, K, mode, splits, out, row_tile=row_tile)
     got = out.cpu().numpy().astype(np.float64)
     ref = A.astype(np.float64) @ Wd.T + (X0.astype(np.float64) if mode == 1 else 0.0)
-    mag = np.abs(A.astype(np.float64)) @ np.abs(Wd).T
-    bound = (2.0 ** -9 * 1.001 + (K + 2) * 2.0 ** -24) * mag + (np.abs(ref) * 2.0 ** -23 if mode == 1 else 0)
+    bound = gemm_bound(A, Wd, ref, K, mode)
     err = np.abs(got - ref)
     log(f"  max rel err {rel_err(got, ref):.3e}, worst err/bound {np.max(err / (bound + 1e-30)):.3f}")
     assert np.all(err <= bound + 1e-30)
@@ -155,12 +163,12 @@ def test_gemm_q8_0_row_tiles(torch, cpa, M, N, K, splits, mode, row_tile):
                                                    (2048, 2048, 1280, 0, 256), (600, 1536, 768, 4, 256)])
 def test_gemm_swiglu(torch, cpa, M, F, K, splits, row_tile):
     log(f"gemm swiglu M={M} F={F} K={K} row_tile={row_tile} plan={cpa.cp_test_gemm_plan(M, 2 * F, K)}")
-    A = bf16_round(torch, synth.normal(synth.tensor_seed("A", M, K), (M, K), scale=1.0))
+    A = f16_round(synth.normal(synth.tensor_seed("A", M, K), (M, K), scale=1.0))
     W = synth.normal(synth.tensor_seed("Wgu", F, K), (2 * F, K))
     Wb = oracle.q8_0_encode_bytes(W)
     Wd = oracle.q8_0_decode_bytes(Wb, K).astype(np.float64)
-    out = torch.zeros((M, F), dtype=torch.bfloat16, device="cuda")
-    cpa.cp_test_gemm(torch.from_numpy(A).cuda().to(torch.bfloat16), torch.from_numpy(Wb).cuda(),
+    out = torch.zeros((M, F), dtype=torch.float16, device="cuda")
+    cpa.cp_test_gemm(torch.from_numpy(A).cuda().to(torch.float16), torch.from_numpy(Wb).cuda(),
                      M, 2 * F, K, 2, splits, out, row_tile=row_tile)
     got = out.float().cpu().numpy()
     g = A.astype(np.float64) @ Wd[:F].T
@@ -174,7 +182,7 @@ def test_gemm_swiglu(torch, cpa, M, F, K, splits, row_tile):
 @pytest.mark.parametrize("row_tile", [128, 256])
 def test_gemm_deterministic_split_k(torch, cpa, row_tile):
     M, N, K = 200, 5120, 5120
-    A = torch.from_numpy(synth.normal(5, (M, K), scale=1.0)).cuda().to(torch.bfloat16)
+    A = torch.from_numpy(synth.normal(5, (M, K), scale=1.0)).cuda().to(torch.float16)
     Wb = torch.from_numpy(oracle.q8_0_encode_bytes(synth.normal(6, (N, K)))).cuda()
     outs = []
     for _ in range(2):
@@ -216,7 +224,7 @@ def test_attention_matches_oracle(torch, cpa, kv, hd, Hq, Hkv, n, start, splits)
     T = start + n
     q_all, kvbuf, qf, Kv, Vv = build_cache(torch, cpa, Hq, Hkv, hd, kv, T, synth.tensor_seed("att", hd, Hq, T))
     q = q_all[start:].contiguous()
-    out = torch.zeros((n, Hq * hd), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((n, Hq * hd), dtype=torch.float16, device="cuda")
     cpa.cp_test_attention(q, kvbuf, n, start, Hq, Hkv, hd, 0 if kv == "f16" else 1, T, splits, out)
     got = out.float().cpu().numpy().reshape(n, Hq, hd)
     ref = oracle.attention(qf[start:], Kv, Vv, np.arange(start, T))

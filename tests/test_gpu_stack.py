@@ -15,7 +15,7 @@ GPU_DENSE = synth.Workload("gpu_tiny_dense", 2, 128, 4, 2, 64, 200, kv_type="f16
                            n_prompt=150, chunk=37)
 GPU_MOE = synth.Workload("gpu_tiny_moe", 2, 128, 4, 2, 64, 0, n_expert=8, n_expert_used=2,
                          expert_ffn_dim=96, kv_type="f16", n_prompt=150, chunk=37)
-TOL = 1e-2   # max|delta| / max|ref| on hidden states, bf16 MFMA against the oracle
+TOL = 1e-2   # max|delta| / max|ref| on hidden states, fp16-operand MFMA against the oracle
 
 
 @pytest.fixture(scope="module")
@@ -32,35 +32,31 @@ def route_gap(r: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return outside - inside
 
 
-def check_layers(w, qlayers, x, lo, ro, tol=TOL, route_tol=None):
-    """Every layer on its own: the oracle's layer l applied to the GPU's input of layer l
-    (layer-major over the whole prompt) against the GPU's output of layer l."""
+def check_layers(w, qlayers, x, lo, ro, tol=TOL, route_tol=1e-2):
+    """The GPU's output of every layer against the oracle's own layer-major run from the
+    same seeded input (nothing the GPU produced is fed to the oracle).
+
+    Routed layers: the GPU's expert set of each token must be a top-k set of the oracle's
+    logits up to a 16-bit-level perturbation of the router input (route_tol * max|r|); the
+    hidden states are compared where both sides chose the same set, which the seeded
+    inputs here make every token.  Returns the oracle's final output."""
     m = oracle.OracleModel(w, qlayers)
-    worst = 0.0
+    ref_lo, routing = [], []
+    ref = m.prefill_layer_major(x, layer_outputs=ref_lo, routing_out=routing)
     for l in range(w.n_layer):
-        xin = x if l == 0 else lo[l - 1]
-        cache = m.new_cache(x.shape[0])
-        routing = []
-        route = None
         if ro is not None:
-            route = ro[l]
-        out = m.layer(l, xin.astype(np.float64), cache, 0, route_idx=route, routing_out=routing)
-        if ro is not None:
-            r = routing[0][0]
+            r, own, _ = routing[l]
             gap = route_gap(r, ro[l])
-            own = routing[0][1]
-            # the router input is this layer's attention output, which both sides compute
-            # to bf16-level accuracy (~1e-3 relative); a GPU choice is valid when it is a
-            # top-k set of the oracle's logits up to that perturbation
-            tolr = (route_tol if route_tol is not None else 1e-2) * float(np.max(np.abs(r)))
-            agree = float(np.mean(np.sort(own, 1) == np.sort(ro[l], 1)))
-            log(f"  layer {l}: routing agreement {agree:.5f}, worst top-k gap {gap.max():.3e} (tol {tolr:.3e})")
+            tolr = route_tol * float(np.max(np.abs(r)))
+            same = np.all(np.sort(own, 1) == np.sort(ro[l], 1), axis=1)
+            log(f"  layer {l}: routing agreement {float(np.mean(same)):.5f}, "
+                f"worst top-k gap {gap.max():.3e} (tol {tolr:.3e})")
             assert np.all(gap <= tolr)
-        e = rel_err(lo[l], out)
-        worst = max(worst, e)
+            assert np.all(same), "expert sets differ at a near tie: compare per token instead"
+        e = rel_err(lo[l], ref_lo[l])
         log(f"  layer {l}: max rel err {e:.3e}")
         assert e < tol
-    return worst
+    return ref
 
 
 @pytest.mark.parametrize("base", [GPU_DENSE, GPU_MOE])
@@ -73,15 +69,7 @@ def test_stack_end_to_end_and_per_layer(torch, base, kv):
     out, ctx, lo, ro = run_prefill(torch, w, ql, x, w.chunk, trace=True)
     assert ctx.n_past == w.n_prompt
     assert np.all(np.isfinite(out))
-    check_layers(w, ql, x, lo, ro)
-    m = oracle.OracleModel(w, ql)
-    routing = []
-    if w.n_expert:
-        # follow the GPU's expert choice wherever it is a valid top-k of the oracle's
-        # logits (checked per layer above); everything else is the oracle's own math
-        ref = m.prefill_layer_major(x, routes=list(ro), routing_out=routing)
-    else:
-        ref = m.prefill_layer_major(x)
+    ref = check_layers(w, ql, x, lo, ro)
     e = rel_err(out, ref)
     log(f"  end-to-end max rel err {e:.3e}")
     assert e < TOL

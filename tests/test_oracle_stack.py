@@ -34,6 +34,23 @@ def test_prefix_outputs_do_not_change_when_tokens_are_appended():
     assert rel(pre, full[:11]) < 1e-12
 
 
+@pytest.mark.parametrize("base", [TINY_DENSE, TINY_MOE])
+@pytest.mark.parametrize("kv", ["f16", "q8_0"])
+def test_layer_rows_equals_the_full_layer_at_those_rows(base, kv):
+    """The sampled-row evaluation used for long prompts is the full layer restricted to
+    the rows, and writes the same cache rows."""
+    w = base.with_(kv_type=kv, n_layer=1)
+    m = oracle.OracleModel(w, q8_layers(w)[:1])
+    x = synth.prompt_inputs(w).astype(np.float64)
+    full = m.prefill_layer_major(x)
+    rows = [0, 1, 5, w.n_prompt - 2]
+    got, cache = m.layer_rows(0, x, rows)
+    assert rel(got, full[rows]) < 1e-12
+    T = max(rows) + 1
+    assert np.array_equal(cache.kval[0][:T], m.last_cache.kval[0][:T])
+    assert np.array_equal(cache.vval[0][:T], m.last_cache.vval[0][:T])
+
+
 def test_layer_by_hand_matches_stack():
     """One layer written out step by step from the dequantised weights."""
     w = TINY_DENSE.with_(n_layer=1)
