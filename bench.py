@@ -230,6 +230,25 @@ def run_main(args, torch, cpa, synth):
     return w, res
 
 
+def run_pmc_probe(args, torch, cpa, synth):
+    """One chunk of the workload's chunk size through one layer of its shapes, from an
+    empty cache: every kernel of the layer is dispatched once in the launch configuration
+    the benchmark times (the GEMM plans and tiles depend on the chunk size, not the
+    depth), with few enough dispatches for per-dispatch counter collection."""
+    w = synth.WORKLOADS[args.workload].with_(n_layer=1)
+    C = w.chunk
+    layers = gpu_layers(w, torch, cpa, synth)
+    ctx = cpa.PrefillContext(cpa.make_config(w, C, C), layers)
+    x = synth.prompt_inputs(w, C, backend="torch", device="cuda")
+    out = torch.empty_like(x)
+    torch.cuda.synchronize()
+    ctx.prefill_chunk(x, out)
+    torch.cuda.synchronize()
+    note(f"pmc probe: one {C}-token chunk through one {w.name} layer; gemm plan "
+         f"{cpa.cp_test_gemm_plan(C, 2 * (-(-w.ffn_dim // 128) * 128), w.d_model) if w.ffn_dim else None}")
+    ctx.close()
+
+
 def run_sweep(args, torch, cpa, synth, oracle_fit):
     w = synth.WORKLOADS["dense27b_sweep"]
     sizes, depths = w.chunk_sweep, w.depths
@@ -327,6 +346,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep-reps", type=int, default=5)
     ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="for rocprofv3 --pmc: the copy probe, then one chunk of the workload's "
+                         "chunk size through one of its layers (no timing events), and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB: the "
                          "reference reading that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -350,6 +372,9 @@ def main():
         torch.cuda.synchronize()
         note(f"copy probe: {args.copy_probe_mib} MiB device-to-device")
         del src, dst
+    if args.pmc_probe:
+        run_pmc_probe(args, torch, cpa, synth)
+        return
     w, res = run_main(args, torch, cpa, synth)
     sweep = None
     if not args.no_sweep:
