@@ -165,13 +165,24 @@ GemmPlan plan_gemm(int M, int N, int K, int force_splits = 0, int force_mt = 0) 
   return best;
 }
 
+// Split-KV factor of a chunk's attention.  Its workgroups (256 query rows of one kv head;
+// one per CU, their LDS tiles take 96 KiB) run in rounds of g_cus; s splits multiply the
+// workgroups and divide the 64-key tiles each one walks, and add a combine pass that
+// reads the s partial rows.  The factor minimises rounds x tiles per workgroup (the
+// longest query tile's range) plus that pass.
 int attn_splits(const Dims& D, int n, int start) {
-  const int64_t base = ceil_div((int64_t)n * D.G, 256) * D.Hkv;   // 256 query rows per workgroup
+  const int64_t base = ceil_div((int64_t)n * D.G, 256) * D.Hkv;
   const int kvt = (int)ceil_div(start + n, 64);
-  if (base >= 256) return 1;
-  int s = (int)ceil_div(512, base);
-  s = std::min(s, std::max(1, kvt / 4));
-  return std::max(1, std::min(s, 32));
+  const double t_tile = 1.5e-6;                              // one tile, one workgroup
+  const double part = (double)n * D.Hq * D.hd * 4;          // fp32 partial rows of a split
+  double best = 1e30;
+  int bs = 1;
+  for (int s = 1; s <= 32 && s <= kvt; ++s) {
+    double c = (double)ceil_div(base * s, g_cus) * ceil_div(kvt, s) * t_tile;
+    if (s > 1) c += 4e-6 + 1.5 * s * part / 4e12;
+    if (c < best) { best = c; bs = s; }
+  }
+  return bs;
 }
 
 // --------------------------------------------------------------------------------------
@@ -225,7 +236,7 @@ struct WsLayout {
   size_t xn, xn32, qkv, q, attn, h, yperm;
   size_t logits, idx, w, rank, ccnt, offsets, perm, inv, tiles, ntiles;
   size_t partial, partial_bytes;
-  size_t apo, apml;
+  size_t apo, apml, arows;   // split-KV partials: rows of capacity
   int max_tiles;
   size_t total;
 };
@@ -287,6 +298,7 @@ WsLayout workspace_layout(const Dims& D) {
   S.partial_bytes = max_partial_bytes(D);
   S.partial = S.partial_bytes ? b.take(S.partial_bytes) : 0;
   const size_t arows = max_attn_partial_rows(D);
+  S.arows = arows;
   S.apo = arows ? b.take(arows * D.hd * 4) : 0;
   S.apml = arows ? b.take(arows * 2 * 4) : 0;
   S.total = b.off;
@@ -453,7 +465,11 @@ int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int sta
   AttnArgs aa;
   aa.q = q; aa.kv = L.kv; aa.n = n; aa.start = start; aa.n_head = D.Hq; aa.n_kv_head = D.Hkv;
   aa.head_dim = D.hd; aa.kv_type = D.kv_type; aa.n_ctx = D.n_ctx; aa.out = attn;
-  aa.splits = attn_splits(D, n, start);
+  // at most the splits whose partial rows the workspace holds (sized for the deepest
+  // chunk of each length)
+  const int64_t rows1 = (int64_t)D.Hkv * n * D.G;
+  aa.splits = (int)std::max<int64_t>(1, std::min<int64_t>(attn_splits(D, n, start),
+                                                          (int64_t)c->WS.arows / rows1));
   aa.part_o = c->wsp<float>(c->WS.apo);
   aa.part_ml = c->wsp<float>(c->WS.apml);
   CP_HIP(c, timed(c, "attention", [&] { return launch_attention(aa, s); }), "attention");

@@ -6,8 +6,10 @@
 // 8 waves owns 256 query rows; each wave owns 32 and computes S^T = K Q^T (32x32x16
 // MFMA, A = K rows from LDS, B = Q fragments held in registers for the whole kernel).
 // In the S^T accumulator a lane holds one query's scores for 16 keys, which is exactly a
-// B operand of the next product O^T += V^T P^T once the key index is permuted
-// consistently on V^T's side, so the probabilities never leave registers.  Softmax
+// B operand of the next product O^T += V^T P^T, so the probabilities never leave
+// registers.  Lane l of the K operand loads key row l with bits 2 and 3 swapped; then
+// the eight probabilities a lane feeds to each V^T P^T step are eight consecutive keys,
+// and the matching V^T fragment is one 16-byte LDS read.  Softmax
 // statistics are per lane (one query per lane pair); the running maximum is raised
 // lazily: O and l are rescaled only when some lane's maximum grew by more than 2^8,
 // which keeps every probability below 2^8 (safe in f16) and skips the rescale on most
@@ -98,6 +100,7 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
   const int jt0 = (int)((int64_t)split * n_kvt / a.splits);
   const int jt1 = (int)((int64_t)(split + 1) * n_kvt / a.splits);
   const int wave_qmin = a.start + min(rw0, R - 1) / G;
+  const int krow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);   // bits 2, 3 swapped
 
   uint4 qf[KSTEPS];
   {
@@ -216,18 +219,20 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
 
   auto compute = [&](const uint4* kb, const uint4* vb, int j0) __attribute__((always_inline)) {
     // ---- S^T = K Q^T ----
+    // the first product of each block takes a zero accumulator operand (an inline
+    // constant), so no registers are cleared per tile
+    const f32x16 zero = {};
     f32x16 s[2];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[jb][e] = 0.0f;
-      const int row = jb * 32 + l32;
+      const int row = jb * 32 + krow;
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         const int ch = kk * 2 + h;
         const uint4 av = kb[row * NCH + (ch ^ (row % NCH))];
         s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av),
-                                                       __builtin_bit_cast(f16x8, qf[kk]), s[jb], 0, 0, 0);
+                                                       __builtin_bit_cast(f16x8, qf[kk]),
+                                                       kk == 0 ? zero : s[jb], 0, 0, 0);
       }
     }
     // ---- causal mask (only tiles reaching past the wave's earliest query) ----
@@ -236,7 +241,8 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int j = j0 + jb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+          // accumulator row 8*(e/4) + 4h + e%4 holds key (that row with bits 2, 3 swapped)
+          const int j = j0 + jb * 32 + 16 * (e >> 3) + 8 * h + (e & 7);
           if (j > qpos || !row_ok) s[jb][e] = -INFINITY;
         }
     }
@@ -246,7 +252,16 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[jb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale;
+    {
+      // The other lane half holds the same query row's other keys.  v_permlane32_swap
+      // moves the lower half's values into the upper lanes of its first result and the
+      // upper half's into the lower lanes of its second; each lane takes the one from the
+      // other half (selecting, not max-ing, the two results: with equal inputs the
+      // compiler treats them as equal values).
+      const uint32_t b = __builtin_bit_cast(uint32_t, mx);
+      const auto sw = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+      mx = fmaxf(mx, __builtin_bit_cast(float, h ? sw[0] : sw[1])) * scale;
+    }
     if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f)) {
       const float mnew = fmaxf(m, mx);
       const float alpha = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mnew);
@@ -278,15 +293,13 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
                           pack_f16x2(s[jb][8 * kk + 4], s[jb][8 * kk + 5]),
                           pack_f16x2(s[jb][8 * kk + 6], s[jb][8 * kk + 7]));
     }
-    const uint2* sv2 = reinterpret_cast<const uint2*>(vb);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int dd = db * 32 + l32, sw = vswz(dd);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint2 lo = sv2[(dd * 8 + ((2 * ks) ^ sw)) * 2 + h];
-        const uint2 hi = sv2[(dd * 8 + ((2 * ks + 1) ^ sw)) * 2 + h];
-        const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        // keys 16*ks + 8h .. +7: one 16-byte chunk of the V^T row
+        const uint4 av = vb[dd * 8 + ((2 * ks + h) ^ sw)];
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av),
                                                        __builtin_bit_cast(f16x8, pb[ks]), o[db], 0, 0, 0);
       }

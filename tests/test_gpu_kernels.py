@@ -193,11 +193,14 @@ def test_gemm_deterministic_split_k(torch, cpa, row_tile):
 
 
 # --------------------------------------------------------------------------- attention
-def build_cache(torch, cpa, Hq, Hkv, hd, kv, T, seed):
+def build_cache(torch, cpa, Hq, Hkv, hd, kv, T, seed, k_gain=None):
     """Cache rows for positions 0..T-1 written by the append kernel from seeded qkv rows;
-    the oracle side re-derives the same rows itself."""
+    the oracle side re-derives the same rows itself.  k_gain: optional per-position factor
+    on the K part of the rows."""
     kv_code = 0 if kv == "f16" else 1
     qkv = synth.normal(seed, (T, (Hq + 2 * Hkv) * hd), scale=1.0)
+    if k_gain is not None:
+        qkv[:, Hq * hd:(Hq + Hkv) * hd] *= np.asarray(k_gain, np.float32)[:, None]
     cos, sin = oracle.rope_table(T, hd, 1e6)
     q_out = torch.empty((T, Hq, hd), dtype=torch.float16, device="cuda")
     kvbuf = torch.zeros(cpa.cp_test_kv_layer_bytes(Hkv, hd, T, kv_code), dtype=torch.uint8, device="cuda")
@@ -232,6 +235,29 @@ def test_attention_matches_oracle(torch, cpa, kv, hd, Hq, Hkv, n, start, splits)
     log(f"  max rel err {e:.3e}")
     assert e < 1e-2
     assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("kv", ["f16", "q8_0"])
+def test_attention_keys_of_one_lane_half_dominate(torch, cpa, kv):
+    """Keys whose position has bit 3 set get 8x larger K rows, so in every 16-key group the
+    scores one half of the lanes holds exceed the other half's by far more than fp16 can
+    carry: the running maximum must combine both lane halves of each query row."""
+    hd, Hq, Hkv, n, start = 128, 40, 8, 96, 160
+    T = start + n
+    gain = np.where((np.arange(T) & 8) != 0, 8.0, 1.0)
+    log(f"attention kv={kv} with dominant keys at positions with bit 3 set")
+    q_all, kvbuf, qf, Kv, Vv = build_cache(torch, cpa, Hq, Hkv, hd, kv, T,
+                                           synth.tensor_seed("att-half", T), k_gain=gain)
+    q = q_all[start:].contiguous()
+    for splits in (1, 3):
+        out = torch.zeros((n, Hq * hd), dtype=torch.float16, device="cuda")
+        cpa.cp_test_attention(q, kvbuf, n, start, Hq, Hkv, hd, 0 if kv == "f16" else 1, T, splits, out)
+        got = out.float().cpu().numpy().reshape(n, Hq, hd)
+        assert np.all(np.isfinite(got))
+        ref = oracle.attention(qf[start:], Kv, Vv, np.arange(start, T))
+        e = rel_err(got, ref)
+        log(f"  splits {splits}: max rel err {e:.3e}")
+        assert e < 1e-2
 
 
 # --------------------------------------------------------------------------- router
