@@ -230,21 +230,66 @@ def run_main(args, torch, cpa, synth):
     return w, res
 
 
+def run_config(name, torch, cpa, synth, steps=1, warmup=1):
+    """Whole-prompt prefill rate of another workload (chunks of its own size from an empty
+    cache), with its roofline fraction: the sum over chunk-layers of max(flops / MFMA peak,
+    bytes / HBM peak) against the measured time.  Same seeded synthetic weights and inputs."""
+    w = synth.WORKLOADS[name]
+    n, C = w.n_prompt, w.chunk
+    note(f"config {w.name}: {w.n_layer} layers, {n} tokens in {C}-token chunks, {w.kv_type} cache")
+    layers = gpu_layers(w, torch, cpa, synth)
+    ctx = cpa.PrefillContext(cpa.make_config(w, n, C), layers)
+    del layers
+    torch.cuda.empty_cache()
+    if w.vocab:
+        x = torch.from_numpy(synth.prompt_inputs(w)).cuda()
+    else:
+        x = synth.prompt_inputs(w, backend="torch", device="cuda")
+    out = torch.empty_like(x)
+    chunks = [(s, min(n, s + C)) for s in range(0, n, C)]
+
+    def step():
+        ctx.kv_cache_truncate(0)
+        for s, e in chunks:
+            rc = ctx.prefill_chunk_raw(x[s:e].data_ptr(), out[s:e].data_ptr(), e - s)
+            if rc != 0:
+                raise RuntimeError(f"prefill_chunk failed: {rc} {ctx.last_error()}")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    bound = sum(roofline_s(w, e - s, s) for s, e in chunks) * w.n_layer
+    flops = sum(chunk_flops(w, e - s, s) for s, e in chunks) * w.n_layer
+    ctx.close()
+    del x, out
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "n_layer": w.n_layer, "prompt_tokens": n, "chunk": C,
+            "kv_type": w.kv_type, "tokens_per_s": n / dt, "ms_per_prompt": dt * 1e3,
+            "algorithmic_tflop_per_s": flops / dt / 1e12,
+            "roofline_bound_ms": bound * 1e3, "roofline_frac": bound / dt}
+
+
 def run_pmc_probe(args, torch, cpa, synth):
     """One chunk of the workload's chunk size through one layer of its shapes, from an
     empty cache: every kernel of the layer is dispatched once in the launch configuration
     the benchmark times (the GEMM plans and tiles depend on the chunk size, not the
     depth), with few enough dispatches for per-dispatch counter collection."""
     w = synth.WORKLOADS[args.workload].with_(n_layer=1)
-    C = w.chunk
+    C, D = w.chunk, args.pmc_depth
     layers = gpu_layers(w, torch, cpa, synth)
-    ctx = cpa.PrefillContext(cpa.make_config(w, C, C), layers)
-    x = synth.prompt_inputs(w, C, backend="torch", device="cuda")
+    ctx = cpa.PrefillContext(cpa.make_config(w, D + C, C), layers)
+    x = synth.prompt_inputs(w, D + C, backend="torch", device="cuda")
     out = torch.empty_like(x)
     torch.cuda.synchronize()
-    ctx.prefill_chunk(x, out)
+    for s in range(0, D + C, C):
+        ctx.prefill_chunk(x[s:min(D + C, s + C)], out[s:min(D + C, s + C)])
     torch.cuda.synchronize()
-    note(f"pmc probe: one {C}-token chunk through one {w.name} layer; gemm plan "
+    note(f"pmc probe: {C}-token chunks through one {w.name} layer up to depth {D}; gemm plan "
          f"{cpa.cp_test_gemm_plan(C, 2 * (-(-w.ffn_dim // 128) * 128), w.d_model) if w.ffn_dim else None}")
     ctx.close()
 
@@ -344,11 +389,16 @@ def main():
     ap.add_argument("--workload", default="dense27b_f16")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the whole-prompt rates of the other workloads")
     ap.add_argument("--sweep-reps", type=int, default=5)
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for rocprofv3 --pmc: the copy probe, then one chunk of the workload's "
                          "chunk size through one of its layers (no timing events), and exit")
+    ap.add_argument("--pmc-depth", type=int, default=0,
+                    help="with --pmc-probe: first prefill this many positions (in chunks of the "
+                         "workload's chunk size), so the probed chunk attends at that depth")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB: the "
                          "reference reading that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -375,7 +425,15 @@ def main():
     if args.pmc_probe:
         run_pmc_probe(args, torch, cpa, synth)
         return
+    mf_tflops, hbm_gbs = cpa.cp_measure_peaks()
+    note(f"measured peaks: fp16 MFMA {mf_tflops:.0f} TFLOP/s, HBM read {hbm_gbs:.0f} GB/s")
     w, res = run_main(args, torch, cpa, synth)
+    res["roofline"]["measured_peak"] = mf_tflops
+    res["roofline"]["frac_of_measured_peak"] = res["roofline"]["achieved"] / mf_tflops
+    configs = []
+    if not args.no_configs:
+        for name in ("tiny_dense", "dense27b_q8", "moe_a3b"):
+            configs.append(run_config(name, torch, cpa, synth))
     sweep = None
     if not args.no_sweep:
         sweep = run_sweep(args, torch, cpa, synth, fit_linear)
@@ -394,7 +452,10 @@ def main():
                    "kv_type": w.kv_type},
         "roofline": res["roofline"],
         "prompt_roofline": res["prompt_roofline"],
+        "measured_peaks": {"mfma_f16_tflops": mf_tflops, "hbm_read_gbs": hbm_gbs,
+                           "published": {"mfma_f16_tflops": PEAK_F16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}},
         "cpu_baseline": cpu,
+        "configs": configs,
         "sweep": sweep,
     }
     print(json.dumps(line), flush=True)

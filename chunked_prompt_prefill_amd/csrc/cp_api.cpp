@@ -831,6 +831,45 @@ int cp_quantize_q8_0(const float* x, int64_t rows, int32_t k, int64_t ldx, void*
   return launch_quantize_q8_0(x, rows, k, ldx, out, (hipStream_t)stream) == hipSuccess ? CP_OK : CP_E_DEVICE;
 }
 
+size_t cp_peak_sink_bytes(void) { return peak_sink_bytes(); }
+
+int cp_measure_peaks(const void* read_buf, size_t read_bytes, void* sink, size_t sink_bytes,
+                     void* stream, double* mfma_tflops, double* hbm_gbs) {
+  if (!read_buf || !sink || !mfma_tflops || !hbm_gbs || read_bytes < ((size_t)1 << 24) ||
+      read_bytes % 16 || ((uintptr_t)read_buf % 16) || sink_bytes < peak_sink_bytes())
+    return CP_E_INVALID;
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) hipEventDestroy(e0);
+    return CP_E_DEVICE;
+  }
+  int rc = CP_OK;
+  double fl = 0.0;
+  float ms = 0.0f;
+  // MFMA loop: one short warm-up launch, then a timed one of about a millisecond
+  if (launch_mfma_peak(64, (float*)sink, s, &fl) != hipSuccess || hipEventRecord(e0, s) != hipSuccess ||
+      launch_mfma_peak(2048, (float*)sink, s, &fl) != hipSuccess || hipEventRecord(e1, s) != hipSuccess ||
+      hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess || ms <= 0.0f) {
+    rc = CP_E_DEVICE;
+  } else {
+    *mfma_tflops = fl / (ms * 1e-3) / 1e12;
+  }
+  // streaming read: one warm-up pass, then three timed passes
+  if (rc == CP_OK) {
+    const int64_t nb = (int64_t)read_bytes;
+    bool ok = launch_stream_read(read_buf, nb, (uint32_t*)sink, s) == hipSuccess && hipEventRecord(e0, s) == hipSuccess;
+    for (int r = 0; ok && r < 3; ++r) ok = launch_stream_read(read_buf, nb, (uint32_t*)sink, s) == hipSuccess;
+    ok = ok && hipEventRecord(e1, s) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
+         hipEventElapsedTime(&ms, e0, e1) == hipSuccess && ms > 0.0f;
+    if (ok) *hbm_gbs = 3.0 * (double)read_bytes / (ms * 1e-3) / 1e9;
+    else rc = CP_E_DEVICE;
+  }
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  return rc;
+}
+
 // ---------------------------------------------------------------------------------- tests
 size_t cp_test_kv_layer_bytes(int32_t n_kv_head, int32_t head_dim, int32_t n_ctx, int32_t kv_type) {
   return kv_layer_bytes(n_kv_head, head_dim, (int32_t)round_up(n_ctx, 64), kv_type);

@@ -137,4 +137,9 @@ hipError_t launch_unpack_router(const void* src, int32_t E, int32_t d, int8_t* q
 
 constexpr int kMoeChunk = 256;   // slots per permute chunk
 
+// Peak measurement kernels (k_peak.hip).
+size_t peak_sink_bytes();
+hipError_t launch_mfma_peak(int32_t iters, float* sink, hipStream_t s, double* flops);
+hipError_t launch_stream_read(const void* buf, int64_t n_bytes, uint32_t* sink, hipStream_t s);
+
 }  // namespace cp

@@ -82,9 +82,18 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
   const int G = a.n_head / a.n_kv_head;
   const int R = a.n * G;
   const int n_qt = (R + QROWS - 1) / QROWS;
-  const int qt = n_qt - 1 - (int)blockIdx.x;       // longest KV ranges first
-  const int g = blockIdx.y;
-  const int split = blockIdx.z;
+  // Workgroup order.  Workgroup i runs on XCD i % 8; each XCD gets a contiguous range of
+  // logical indices, query tile fastest, so the query tiles that walk the same K/V range
+  // (one kv head, one split) share an XCD's L2 instead of fetching it once per XCD.
+  // Within a range the longest KV spans go first.
+  const int total = n_qt * a.n_kv_head * a.splits;
+  const int bi = blockIdx.x;
+  const int xcd = bi & 7, idx = bi >> 3;
+  const int q8 = total >> 3, r8 = total & 7;
+  const int logical = (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
+  const int qt = n_qt - 1 - logical % n_qt;
+  const int g = (logical / n_qt) % a.n_kv_head;
+  const int split = logical / (n_qt * a.n_kv_head);
   const int64_t n_ctx = a.n_ctx;
 
   const int rw0 = qt * QROWS + wave * 32;
@@ -217,12 +226,10 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
 
-  auto compute = [&](const uint4* kb, const uint4* vb, int j0) __attribute__((always_inline)) {
-    // ---- S^T = K Q^T ----
-    // the first product of each block takes a zero accumulator operand (an inline
-    // constant), so no registers are cleared per tile
+  // ---- S^T = K Q^T of one tile (16 MFMAs).  The first product of each block takes a zero
+  // accumulator operand (an inline constant), so no registers are cleared per tile.
+  auto qk = [&](const uint4* kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
     const f32x16 zero = {};
-    f32x16 s[2];
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
       const int row = jb * 32 + krow;
@@ -235,7 +242,10 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
                                                        kk == 0 ? zero : s[jb], 0, 0, 0);
       }
     }
-    // ---- causal mask (only tiles reaching past the wave's earliest query) ----
+  };
+  // ---- causal mask (only tiles reaching past the wave's earliest query), the tile's row
+  // maximum, and the lazy rescale of O and l; returns the offset the probabilities take.
+  auto stats = [&](f32x16 (&s)[2], int j0) __attribute__((always_inline)) -> float {
     if (j0 + KVT - 1 > wave_qmin || !row_ok) {
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
@@ -246,7 +256,6 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
           if (j > qpos || !row_ok) s[jb][e] = -INFINITY;
         }
     }
-    // ---- online softmax (log2 domain, lazy rescale) ----
     float mx = -INFINITY;
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
@@ -272,7 +281,11 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
         for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
       m = mnew;
     }
-    const float msafe = (m == -INFINITY) ? 0.0f : m;
+    return (m == -INFINITY) ? 0.0f : m;
+  };
+  // ---- probabilities p = 2^(s*scale - m) (every one below 2^8: safe in fp16), their row
+  // sum, and the fp16 B operands of O^T += V^T P^T (keys 16*ks + 8h .. +7 per lane).
+  auto probs = [&](f32x16 (&s)[2], float msafe, uint4 (&pb)[4]) __attribute__((always_inline)) {
     float ls = 0.0f;
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
@@ -283,8 +296,6 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
         ls += p;
       }
     l += ls;                           // lane half; halves are combined at the end
-    // ---- O^T += V^T P^T ----
-    uint4 pb[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int jb = ks >> 1, kk = ks & 1;
@@ -293,6 +304,9 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
                           pack_f16x2(s[jb][8 * kk + 4], s[jb][8 * kk + 5]),
                           pack_f16x2(s[jb][8 * kk + 6], s[jb][8 * kk + 7]));
     }
+  };
+  // ---- O^T += V^T P^T (16 MFMAs)
+  auto pv = [&](const uint4* vb, const uint4 (&pb)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int dd = db * 32 + l32, sw = vswz(dd);
@@ -305,6 +319,15 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
       }
     }
   };
+  // One whole tile, in order (the q8_0 path).
+  auto compute = [&](const uint4* kb, const uint4* vb, int j0) __attribute__((always_inline)) {
+    f32x16 s[2];
+    uint4 pb[4];
+    qk(kb, s);
+    const float msafe = stats(s, j0);
+    probs(s, msafe, pb);
+    pv(vb, pb);
+  };
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -315,17 +338,53 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
     // past the range still wait, synchronise and issue (a clamped repeat of the last tile)
     // so every wave sees the same count of loads in flight, but skip the arithmetic.
     if constexpr (!Q8) {
-      // NB = 3: two tiles in flight while one is consumed
+      // NB = 3, software-pipelined across tiles.  Step t waits for tile t+1 (the only loads
+      // in flight), synchronises (every wave is done with tile t-1), and refills the buffer
+      // of t-1 with tile t+2.  Then, after tile t's mask, maximum and rescale, the K Q^T
+      // products of tile t+1 (issued unconditionally: past the range the clamped loads
+      // keep the buffer valid, and the result is unused) interleave with tile t's
+      // exponentials, so the MFMAs of one tile run under the softmax of the other; V^T P^T
+      // of tile t follows.
+      f32x16 sc[2], sn[2];
       auto step = [&](auto J, int t) __attribute__((always_inline)) {
-        attn_wait_vm_lgkm<NLOAD>();    // own loads of tile t landed; own LDS reads of t-1 done
-        __builtin_amdgcn_s_barrier();  // everyone's: tile t complete, buffer of t-1 free
+        constexpr int j = decltype(J)::value;
+        attn_wait_vm_lgkm<0>();
+        __builtin_amdgcn_s_barrier();
         attn_cfence();
-        issue_f16(std::integral_constant<int, (decltype(J)::value + 2) % 3>{}, min(t + 2, last));
+        issue_f16(std::integral_constant<int, (j + 2) % 3>{}, min(t + 2, last));
         attn_cfence();
-        if (t < jt1) compute(bufK(J), bufV(J), t * KVT);
+        if (t < jt1) {
+          uint4 pb[4];
+          const float msafe = stats(sc, t * KVT);
+          qk(bufK(std::integral_constant<int, (j + 1) % 3>{}), sn);
+          probs(sc, msafe, pb);
+          // three K fragment reads ahead, then {one MFMA of K Q^T, five VALU of the
+          // softmax, the next fragment read} per MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+            if (i < 13) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          pv(bufV(J), pb);
+          // V^T P^T: three V fragment reads ahead, then {one MFMA, the next read}
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i < 13) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb) sc[jb] = sn[jb];
+        }
       };
       issue_f16(I0{}, jt0);
       issue_f16(I1{}, min(jt0 + 1, last));
+      attn_wait_vm_lgkm<NLOAD>();      // tile jt0 landed (own loads)
+      __builtin_amdgcn_s_barrier();    // everyone's
+      attn_cfence();
+      qk(bufK(I0{}), sc);
       for (int t = jt0; t < jt1; t += 3) {
         step(I0{}, t);
         step(I1{}, t + 1);
@@ -415,7 +474,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   const int G = a.n_head / a.n_kv_head;
   const int R = a.n * G;
-  dim3 grid((R + QROWS - 1) / QROWS, a.n_kv_head, a.splits);
+  dim3 grid((unsigned)(((R + QROWS - 1) / QROWS) * a.n_kv_head * a.splits));
   const bool q8 = a.kv_type != CP_KV_F16;
   if (a.head_dim == 128) {
     if (q8) hipLaunchKernelGGL((attn_kernel<128, true>), grid, dim3(AW * 64), 0, s, a);

@@ -162,6 +162,20 @@ def cp_quantize_q8_0(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> tor
     return out
 
 
+def cp_measure_peaks(read_bytes: int = 2 << 30, device="cuda"):
+    """(MFMA fp16 TFLOP/s, HBM read GB/s) measured on the device by the library's own
+    MFMA-only and streaming-read kernels (the buffers are allocated here)."""
+    L = lib()
+    buf = torch.empty(read_bytes, dtype=torch.uint8, device=device)
+    sink = torch.empty(L.cp_peak_sink_bytes(), dtype=torch.uint8, device=device)
+    tf, gb = ctypes.c_double(), ctypes.c_double()
+    rc = L.cp_measure_peaks(ptr(buf), read_bytes, ptr(sink), sink.numel(), stream_ptr(),
+                            ctypes.byref(tf), ctypes.byref(gb))
+    if rc != CP_OK:
+        raise PrefillError(rc, "cp_measure_peaks failed")
+    return tf.value, gb.value
+
+
 def cp_test_kv_layer_bytes(n_kv_head, head_dim, n_ctx, kv_type) -> int:
     return lib().cp_test_kv_layer_bytes(n_kv_head, head_dim, n_ctx, kv_type)
 

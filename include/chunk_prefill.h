@@ -185,6 +185,20 @@ void prefill_free(cp_ctx* ctx);   /* releases host-side state only; buffers stay
 int cp_kernel_timing(cp_ctx* ctx, const char* classes);
 int cp_kernel_times(cp_ctx* ctx, const char* kernel_class, float* total_ms, int32_t* launches);
 
+/* The roofline's denominators, measured on this device (bench reports against both these
+ * and the published 2.5 PFLOP/s dense fp16 / 8 TB/s HBM figures).  Runs, on hip_stream and
+ * synchronising it:
+ *   - an MFMA-only kernel: fp16 32x32x16 MFMAs on register operands, four independent
+ *     accumulators per wave, 2048 workgroups of 4 waves, no memory traffic -> *mfma_tflops;
+ *   - a streaming read of read_buf (dev, 16-byte aligned, read_bytes a multiple of 16 and at
+ *     least 16 MiB; contents ignored) with 16-byte loads, three passes after a warm-up
+ *     -> *hbm_gbs.
+ * sink: dev scratch of at least cp_peak_sink_bytes() bytes (overwritten).  Returns CP_OK,
+ * CP_E_INVALID for bad arguments, CP_E_DEVICE if a HIP call fails. */
+size_t cp_peak_sink_bytes(void);
+int cp_measure_peaks(const void* read_buf, size_t read_bytes, void* sink, size_t sink_bytes,
+                     void* hip_stream, double* mfma_tflops, double* hbm_gbs);
+
 /* q8_0 encode of float32 rows into the interchange layout, on the GPU (used to build
  * seeded weights in device memory).  x: dev float32 [rows][ldx], first k columns used;
  * out: dev bytes [rows][ceil(k/32)*34].  Per block of 32: d = amax/127 (float32,
