@@ -194,27 +194,23 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
       }
     }
   };
+  // Dequantisation into LDS: packed fp16, each value the correctly rounded fp16 of d*q.
   auto store_q8 = [&](uint4* kb, uint4* vb) __attribute__((always_inline)) {
     if (tid < KQ) {
       const int row = tid / (HD / 16), c16 = tid % (HD / 16);
-      const float d = half_bits_to_float(qk_sc);
-      const float ds[8] = {d, d, d, d, d, d, d, d};
       const int sw = row % NCH;
-      kb[row * NCH + ((2 * c16) ^ sw)] = dequant8_f16(qk_raw.x, qk_raw.y, ds);
-      kb[row * NCH + ((2 * c16 + 1) ^ sw)] = dequant8_f16(qk_raw.z, qk_raw.w, ds);
+      uint4 lo, hi;
+      dequant16_f16(qk_raw, qk_sc, lo, hi);
+      kb[row * NCH + ((2 * c16) ^ sw)] = lo;
+      kb[row * NCH + ((2 * c16 + 1) ^ sw)] = hi;
     }
     if (tid < VQ) {
       const int d = tid / (KVT / 16), c16 = tid % (KVT / 16);
-      float ds[16];
-      const uint32_t s[8] = {qv_sc0.x, qv_sc0.y, qv_sc0.z, qv_sc0.w, qv_sc1.x, qv_sc1.y, qv_sc1.z, qv_sc1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        ds[2 * e] = half_bits_to_float(s[e] & 0xFFFFu);
-        ds[2 * e + 1] = half_bits_to_float(s[e] >> 16);
-      }
       const int sw = vswz(d);
-      vb[d * 8 + ((2 * c16) ^ sw)] = dequant8_f16(qv_raw.x, qv_raw.y, ds);
-      vb[d * 8 + ((2 * c16 + 1) ^ sw)] = dequant8_f16(qv_raw.z, qv_raw.w, ds + 8);
+      uint4 lo, hi;
+      dequant16_f16_scales(qv_raw, qv_sc0, qv_sc1, lo, hi);
+      vb[d * 8 + ((2 * c16) ^ sw)] = lo;
+      vb[d * 8 + ((2 * c16 + 1) ^ sw)] = hi;
     }
   };
 

@@ -59,26 +59,26 @@ __device__ __forceinline__ void dequant16_f16(uint4 raw, uint32_t d_bits, uint4&
   hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// 16 signed bytes, each with its own fp16 scale (s0: scales of bytes 0-7, s1: of bytes
+// 8-15, two per dword in byte order) -> 16 fp16, each the correctly rounded d*q.
+__device__ __forceinline__ void dequant16_f16_scales(uint4 raw, uint4 s0, uint4 s1, uint4& lo, uint4& hi) {
+  const uint32_t sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = w[i] ^ 0x80808080u;
+    o[2 * i] = __builtin_bit_cast(uint32_t, q8_pair_f16(x, 0x04010400u) * __builtin_bit_cast(f16x2, sc[2 * i]));
+    o[2 * i + 1] = __builtin_bit_cast(uint32_t, q8_pair_f16(x, 0x04030402u) * __builtin_bit_cast(f16x2, sc[2 * i + 1]));
+  }
+  lo = make_uint4(o[0], o[1], o[2], o[3]);
+  hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 // float -> fp16 for stored activations that are not bounded by construction (the SwiGLU
 // product): saturated to the finite fp16 range, then rounded to nearest even.
 __device__ __forceinline__ _Float16 f16_sat(float v) {
   return (_Float16)__builtin_amdgcn_fmed3f(v, -65504.0f, 65504.0f);
-}
-
-// 8 signed bytes (two dwords) times per-element float scales -> 8 f16 (one uint4).
-__device__ __forceinline__ uint4 dequant8_f16(uint32_t w0, uint32_t w1, const float* d) {
-  uint32_t w[2] = {w0, w1};
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    float f0 = (float)(int8_t)(w[i] & 0xFFu) * d[4 * i + 0];
-    float f1 = (float)(int8_t)((w[i] >> 8) & 0xFFu) * d[4 * i + 1];
-    float f2 = (float)(int8_t)((w[i] >> 16) & 0xFFu) * d[4 * i + 2];
-    float f3 = (float)(int8_t)(w[i] >> 24) * d[4 * i + 3];
-    o[2 * i] = pack_f16x2(f0, f1);
-    o[2 * i + 1] = pack_f16x2(f2, f3);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 __device__ __forceinline__ float warp_max32(float v) {   // max over aligned groups of 32 lanes
