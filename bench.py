@@ -344,8 +344,16 @@ def run_sweep(args, torch, cpa, synth, oracle_fit):
                            "roofline_frac": roofline_s(w, C, D) / (t_layer * 1e-3),
                            "mfma_frac": chunk_flops(w, C, D) / (PEAK_F16_TFLOPS * 1e12) / (t_layer * 1e-3)})
     ctx.close()
+    # the pipeline chunk rule of "Prompt chunks sized for a layer split's pipeline" fed with
+    # the fitted b/a: chunk sizes for these prompt lengths over S layer-split stages
+    planner = {}
+    for D in depths:
+        ba = fit[str(D)]["b_over_a_tokens"]
+        planner[str(D)] = {"b_over_a_tokens": ba, "chunks": {
+            str(n): {str(S): cpa.cp_plan_chunk(n, Cmax, S, ba) for S in (1, 2, 4, 8)}
+            for n in (2013, 3865, 10041, 17055, 28998, 58300)}}
     return {"workload": f"{w.name}: {w.n_layer} layers of the dense 27B-class shapes, f16 cache",
-            "fit": fit, "points": points}
+            "fit": fit, "points": points, "planner": planner}
 
 
 def run_cpu_baseline(args, w):

@@ -7,6 +7,7 @@
 // permute -> grouped GEMMs -> unpermute) (+residual).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -829,6 +830,21 @@ int cp_kernel_times(cp_ctx* c, const char* cls, float* total_ms, int32_t* launch
 int cp_quantize_q8_0(const float* x, int64_t rows, int32_t k, int64_t ldx, void* out, void* stream) {
   if (!x || !out || rows < 0 || k < 1 || ldx < k) return CP_E_INVALID;
   return launch_quantize_q8_0(x, rows, k, ldx, out, (hipStream_t)stream) == hipSuccess ? CP_OK : CP_E_DEVICE;
+}
+
+int32_t cp_plan_chunk(int32_t n_tokens, int32_t cap, int32_t stages, double b_over_a) {
+  if (n_tokens < 0 || cap < 1 || stages < 1 || !(b_over_a > 0.0) || !std::isfinite(b_over_a))
+    return CP_E_INVALID;
+  if (n_tokens == 0) return 0;
+  if (stages == 1) return std::min(n_tokens, cap);
+  // (S - 1 + n/C) chunk-steps of (b + a*C): smallest at C = sqrt(n * (b/a) / (S - 1))
+  auto up256 = [](int64_t v) { return (v + 255) / 256 * 256; };
+  const double c = std::sqrt((double)n_tokens * b_over_a / (double)(stages - 1));
+  int64_t c0 = up256((int64_t)std::ceil(c));
+  c0 = std::max<int64_t>(512, std::min<int64_t>(cap, c0));
+  const int64_t k = (n_tokens + c0 - 1) / c0;
+  if (k <= 1) return std::min(n_tokens, cap);
+  return (int32_t)std::min<int64_t>(cap, up256((n_tokens + k - 1) / k));
 }
 
 size_t cp_peak_sink_bytes(void) { return peak_sink_bytes(); }

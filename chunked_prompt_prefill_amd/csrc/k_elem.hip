@@ -386,9 +386,12 @@ hipError_t launch_unpack_router(const void* src, int32_t E, int32_t d, int8_t* q
 
 // Router logits in the fixed float32 order (per block: products and sums ascending,
 // then acc += d_b * P_b over blocks ascending), then top-k (descending logit, ties to
-// the lower expert index) and softmax over the k selected logits.  A workgroup takes
-// RT tokens; thread e computes expert e for all of them; y is staged 256 columns at a time.
-constexpr int RT = 8;
+// the lower expert index) and softmax over the k selected logits.  Threads are (expert,
+// token group): with E <= 128 two groups of 128 threads each take 8 of the workgroup's 16
+// tokens, otherwise one group of 256 takes 8.  Each thread converts a block's 32 weights
+// to float once and applies them to its 8 tokens; y is staged 256 columns at a time.
+constexpr int RT = 16;       // tokens per workgroup, at most
+constexpr int RTT = 8;       // tokens per thread
 __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ y,
                                                      const int8_t* __restrict__ rq,
                                                      const uint16_t* __restrict__ rd, int32_t n,
@@ -396,38 +399,53 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ y
                                                      float* __restrict__ logits,
                                                      int32_t* __restrict__ idx,
                                                      float* __restrict__ wout) {
-  __shared__ float sy[RT][256];
+  __shared__ float4 sy4[RT][64];
   __shared__ float slog[RT][256];
   const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * RT;
-  float acc[RT];
+  const int groups = E <= 128 ? 2 : 1;
+  const int EP = 256 / groups;
+  const int e = tid % EP, grp = tid / EP;
+  const int RTW = RTT * groups;
+  const int t0 = blockIdx.x * RTW;
+  float acc[RTT];
 #pragma unroll
-  for (int tt = 0; tt < RT; ++tt) acc[tt] = 0.0f;
+  for (int tt = 0; tt < RTT; ++tt) acc[tt] = 0.0f;
   for (int c0 = 0; c0 < d; c0 += 256) {
     __syncthreads();
-    for (int e = tid; e < RT * 256; e += 256) {
-      const int tt = e / 256, j = e % 256;
-      const int t = t0 + tt;
-      sy[tt][j] = (t < n && c0 + j < d) ? y[(int64_t)t * d + c0 + j] : 0.0f;
+    for (int u = tid; u < RTW * 64; u += 256) {
+      const int tt = u / 64, j4 = u % 64;
+      const int t = t0 + tt, col = c0 + 4 * j4;
+      sy4[tt][j4] = (t < n && col < d) ? *reinterpret_cast<const float4*>(y + (int64_t)t * d + col)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
-    if (tid < E) {
+    if (e < E) {
       for (int b = 0; b < 8; ++b) {
         const int col = c0 + b * QK;
         if (col >= d) break;
         const int blk = col / QK;
-        const uint4* qp = reinterpret_cast<const uint4*>(rq + (int64_t)tid * d + col);
+        const uint4* qp = reinterpret_cast<const uint4*>(rq + (int64_t)e * d + col);
         const uint4 qa = qp[0], qb = qp[1];
         const uint32_t w[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-        const float ds = half_bits_to_float(rd[(int64_t)tid * (d / QK) + blk]);
+        float qf[QK];
 #pragma unroll
-        for (int tt = 0; tt < RT; ++tt) {
-          const float* ys = &sy[tt][b * QK];
-          float P = __fmul_rn((float)(int8_t)(w[0] & 0xFF), ys[0]);
+        for (int j = 0; j < QK; ++j) qf[j] = (float)(int8_t)((w[j >> 2] >> (8 * (j & 3))) & 0xFF);
+        const float ds = half_bits_to_float(rd[(int64_t)e * (d / QK) + blk]);
 #pragma unroll
-          for (int j = 1; j < QK; ++j) {
-            const float qj = (float)(int8_t)((w[j >> 2] >> (8 * (j & 3))) & 0xFF);
-            P = __fadd_rn(P, __fmul_rn(qj, ys[j]));
+        for (int tt = 0; tt < RTT; ++tt) {
+          const float4* ys = &sy4[grp * RTT + tt][b * (QK / 4)];
+          float4 yv = ys[0];
+          float P = __fmul_rn(qf[0], yv.x);
+          P = __fadd_rn(P, __fmul_rn(qf[1], yv.y));
+          P = __fadd_rn(P, __fmul_rn(qf[2], yv.z));
+          P = __fadd_rn(P, __fmul_rn(qf[3], yv.w));
+#pragma unroll
+          for (int j4 = 1; j4 < QK / 4; ++j4) {
+            yv = ys[j4];
+            P = __fadd_rn(P, __fmul_rn(qf[4 * j4 + 0], yv.x));
+            P = __fadd_rn(P, __fmul_rn(qf[4 * j4 + 1], yv.y));
+            P = __fadd_rn(P, __fmul_rn(qf[4 * j4 + 2], yv.z));
+            P = __fadd_rn(P, __fmul_rn(qf[4 * j4 + 3], yv.w));
           }
           const float term = __fmul_rn(ds, P);
           acc[tt] = (blk == 0) ? term : __fadd_rn(acc[tt], term);
@@ -436,16 +454,17 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ y
     }
   }
   __syncthreads();
-  if (tid < E) {
+  if (e < E) {
 #pragma unroll
-    for (int tt = 0; tt < RT; ++tt) {
-      slog[tt][tid] = acc[tt];
-      if (t0 + tt < n) logits[(int64_t)(t0 + tt) * E + tid] = acc[tt];
+    for (int tt = 0; tt < RTT; ++tt) {
+      const int tw = grp * RTT + tt;
+      slog[tw][e] = acc[tt];
+      if (t0 + tw < n) logits[(int64_t)(t0 + tw) * E + e] = acc[tt];
     }
   }
   __syncthreads();
   const int lane = tid & 63, wave = tid >> 6;
-  for (int tt = wave; tt < RT; tt += 4) {
+  for (int tt = wave; tt < RTW; tt += 4) {
     const int t = t0 + tt;
     if (t >= n) break;
     float v[4];
@@ -494,7 +513,8 @@ hipError_t launch_router(const float* y, const int8_t* rq, const uint16_t* rd, i
                          int32_t E, int32_t k, float* logits, int32_t* idx, float* w,
                          hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(router_kernel, dim3((unsigned)ceil_div(n, RT)), dim3(256), 0, s, y, rq, rd, n,
+  const int rtw = RTT * (E <= 128 ? 2 : 1);
+  hipLaunchKernelGGL(router_kernel, dim3((unsigned)ceil_div(n, rtw)), dim3(256), 0, s, y, rq, rd, n,
                      d, E, k, logits, idx, w);
   return hipGetLastError();
 }

@@ -162,6 +162,14 @@ def cp_quantize_q8_0(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> tor
     return out
 
 
+def cp_plan_chunk(n_tokens: int, cap: int, stages: int, b_over_a: float) -> int:
+    """Pipeline chunk size from the fitted b/a (host code of the library)."""
+    c = lib().cp_plan_chunk(int(n_tokens), int(cap), int(stages), float(b_over_a))
+    if c < 0:
+        raise PrefillError(c, "cp_plan_chunk: invalid arguments")
+    return c
+
+
 def cp_measure_peaks(read_bytes: int = 2 << 30, device="cuda"):
     """(MFMA fp16 TFLOP/s, HBM read GB/s) measured on the device by the library's own
     MFMA-only and streaming-read kernels (the buffers are allocated here)."""

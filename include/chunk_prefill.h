@@ -185,6 +185,17 @@ void prefill_free(cp_ctx* ctx);   /* releases host-side state only; buffers stay
 int cp_kernel_timing(cp_ctx* ctx, const char* classes);
 int cp_kernel_times(cp_ctx* ctx, const char* kernel_class, float* total_ms, int32_t* launches);
 
+/* Chunk size for an n_tokens prompt read over `stages` layer-split pipeline stages, from a
+ * layer's fitted cost per chunk b and per token a (as b/a, in tokens): "Prompt chunks sized
+ * for a layer split's pipeline", sections "Summary" and "What changed".  A prompt in chunks
+ * of C over S stages takes (S - 1 + n/C) chunk-steps of (b + a*C), least at
+ * C0 = sqrt(n * (b/a) / (S - 1)); C0 is rounded up to a multiple of 256 and kept within
+ * [512, cap], then evened over the k = ceil(n / C0) chunks it takes:
+ * C = min(cap, roundup_256(ceil(n / k))).  A prompt that fits one chunk, and a single stage
+ * (S = 1), take min(n, cap).  Host only.  Returns the chunk (0 for n = 0), or CP_E_INVALID
+ * for n < 0, cap < 1, stages < 1 or a b/a that is not a positive finite number. */
+int32_t cp_plan_chunk(int32_t n_tokens, int32_t cap, int32_t stages, double b_over_a);
+
 /* The roofline's denominators, measured on this device (bench reports against both these
  * and the published 2.5 PFLOP/s dense fp16 / 8 TB/s HBM figures).  Runs, on hip_stream and
  * synchronising it:

@@ -79,3 +79,24 @@ def test_state_header_check_matches_oracle_blobs(cpa):
     assert L.cp_state_check(ctypes.byref(cfg), blob[:-2], len(blob) - 2) == -3
     small = cpa.make_config(w, 8, 8)      # capacity below the blob's 9 tokens
     assert L.cp_state_check(ctypes.byref(small), blob, len(blob)) == -3
+
+
+def test_plan_chunk_matches_the_oracle_rule_and_the_page_table(cpa):
+    """The library's pipeline chunk rule (host code) against the oracle's restatement over
+    a grid of prompt lengths, capacities, stage counts and cost ratios, and against the
+    chunks the page prints for four stages."""
+    import os
+    golden = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "pipeline_chunks.txt")
+    rows = [l.split() for l in open(golden) if l.strip() and not l.startswith("#")]
+    for n, stages, chunk in ((int(a), int(b), int(c)) for a, b, c in rows):
+        assert cpa.cp_plan_chunk(n, 8192, stages, 1024.0) == chunk
+    for n in (0, 1, 300, 511, 512, 513, 2013, 3865, 10041, 17055, 28998, 58300, 100000):
+        for cap in (128, 512, 2048, 3328, 8192):
+            for stages in (1, 2, 3, 4, 8):
+                for ba in (50.0, 183.0, 1000.0, 1024.0, 1820.0, 5000.0):
+                    assert cpa.cp_plan_chunk(n, cap, stages, ba) == oracle.pipeline_chunk(n, cap, stages, ba), \
+                        (n, cap, stages, ba)
+    for bad in ((-1, 8192, 4, 1024.0), (100, 0, 4, 1024.0), (100, 8192, 0, 1024.0),
+                (100, 8192, 4, 0.0), (100, 8192, 4, float("nan")), (100, 8192, 4, float("inf"))):
+        with pytest.raises(Exception):
+            cpa.cp_plan_chunk(*bad)

@@ -160,3 +160,58 @@ def test_determinism_truncate_and_error_paths(torch):
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     assert ctx.kv_cache_get_state() == s1
+
+
+@pytest.mark.parametrize("kv", ["f16", "q8_0"])
+def test_prefix_resume_equals_full_prefill(torch, kv):
+    """A prompt-cache hit: the state of a 64-token prefix restored into a fresh context (or
+    the cache truncated back to it), then only the suffix prefilled.  With the same chunk
+    boundaries the suffix outputs and the final state are bitwise those of the full
+    prefill; with other boundaries they agree to the tolerance, and with the oracle."""
+    import chunked_prompt_prefill_amd as cpa
+    w = GPU_DENSE.with_(kv_type=kv)
+    ql = q8_layers(w)
+    x = synth.prompt_inputs(w, 150)
+    dev = [cpa.to_device(l) for l in ql]
+    cfg = cpa.make_config(w, 160, 64)
+    xt = torch.from_numpy(x).cuda()
+    bounds = [(0, 64), (64, 128), (128, 150)]
+    full = cpa.PrefillContext(cfg, dev)
+    y_full = torch.empty_like(xt)
+    for s, e in bounds:
+        full.prefill_chunk(xt[s:e], y_full[s:e])
+    state_full = full.kv_cache_get_state()
+    pre = cpa.PrefillContext(cfg, dev)
+    y_pre = torch.empty_like(xt)
+    pre.prefill_chunk(xt[:64], y_pre[:64])
+    blob = pre.kv_cache_get_state()
+    # restored prefix, same boundaries: bitwise
+    hit = cpa.PrefillContext(cfg, dev)
+    assert hit.kv_cache_set_state(blob) == 0 and hit.n_past == 64
+    y_hit = torch.empty_like(xt)
+    for s, e in bounds[1:]:
+        hit.prefill_chunk(xt[s:e], y_hit[s:e])
+    torch.cuda.synchronize()
+    assert torch.equal(y_hit[64:], y_full[64:])
+    assert hit.kv_cache_get_state() == state_full
+    # truncation back to the prefix, same boundaries: bitwise
+    assert full.kv_cache_truncate(64) == 0
+    y_tr = torch.empty_like(xt)
+    for s, e in bounds[1:]:
+        full.prefill_chunk(xt[s:e], y_tr[s:e])
+    torch.cuda.synchronize()
+    assert torch.equal(y_tr[64:], y_full[64:])
+    assert full.kv_cache_get_state() == state_full
+    # restored prefix, the suffix in other chunks (40, 40, 6): within tolerance
+    other = cpa.PrefillContext(cpa.make_config(w, 160, 40), dev)
+    y_other = torch.empty_like(xt)
+    assert other.kv_cache_set_state(blob) == 0
+    for s, e in ((64, 104), (104, 144), (144, 150)):
+        other.prefill_chunk(xt[s:e], y_other[s:e])
+    torch.cuda.synchronize()
+    ref = oracle.OracleModel(w, ql).prefill_layer_major(x)
+    got = y_other.cpu().numpy()[64:]
+    e1 = rel_err(got, y_full.cpu().numpy()[64:])
+    e2 = rel_err(got, ref[64:])
+    log(f"  prefix resume kv={kv}: other chunking vs full {e1:.3e}, vs oracle {e2:.3e}")
+    assert e1 < TOL and e2 < TOL
