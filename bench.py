@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_F16_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 MFMA (same rate)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+DECODE_ROOM = 128           # cache positions past the prompt for the decode-sized chunks
 
 
 def note(msg: str):
@@ -168,7 +169,7 @@ def run_main(args, torch, cpa, synth):
     note(f"workload {w.name}: {w.n_layer} layers, {n} tokens in {C}-token chunks, {w.kv_type} cache")
     t = time.time()
     layers = gpu_layers(w, torch, cpa, synth)
-    ctx = cpa.PrefillContext(cpa.make_config(w, n, C), layers)
+    ctx = cpa.PrefillContext(cpa.make_config(w, n + DECODE_ROOM, C), layers)
     del layers
     torch.cuda.empty_cache()
     x = synth.prompt_inputs(w, backend="torch", device="cuda")
@@ -209,6 +210,22 @@ def run_main(args, torch, cpa, synth):
     expect = per_launch["launches"] * w.n_layer * args.steps
     if dom_launches != expect:
         raise RuntimeError(f"timed {dom_launches} launches of {dom}, expected {expect}")
+    # Decode-sized chunks at the end of the prompt (the pages' "pp3" / "tg32" regime, run on
+    # the same kernels): 32 chunks of 1 token, then 32 of 3, each series from depth n.
+    decode = {}
+    for dc in (1, 3):
+        ctx.kv_cache_truncate(n)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for i in range(32):
+            rc = ctx.prefill_chunk_raw(x[i * dc:(i + 1) * dc].data_ptr(), out[i * dc:(i + 1) * dc].data_ptr(), dc)
+            if rc != 0:
+                raise RuntimeError(f"prefill_chunk failed: {rc} {ctx.last_error()}")
+        torch.cuda.synchronize()
+        dt2 = time.perf_counter() - t2
+        decode[f"chunk_{dc}"] = {"tokens_per_s": 32 * dc / dt2, "ms_per_chunk": dt2 / 32 * 1e3,
+                                 "depth": n,
+                                 "hbm_roofline_ms_per_chunk": roofline_s(w, dc, n) * w.n_layer * 1e3}
     # whole-prompt roofline: sum of per-chunk-layer bounds
     bound = sum(roofline_s(w, e - s, s) for s, e in chunks) * w.n_layer
     res = {
@@ -223,6 +240,7 @@ def run_main(args, torch, cpa, synth):
                      "algorithmic_bytes_per_launch": per_launch["bytes"]},
         "prompt_roofline": {"bound_ms_per_step": bound * 1e3,
                             "frac": bound / (total / args.steps)},
+        "decode_regime": decode,
     }
     ctx.close()
     del x, out
@@ -460,6 +478,7 @@ def main():
                    "kv_type": w.kv_type},
         "roofline": res["roofline"],
         "prompt_roofline": res["prompt_roofline"],
+        "decode_regime": res["decode_regime"],
         "measured_peaks": {"mfma_f16_tflops": mf_tflops, "hbm_read_gbs": hbm_gbs,
                            "published": {"mfma_f16_tflops": PEAK_F16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}},
         "cpu_baseline": cpu,

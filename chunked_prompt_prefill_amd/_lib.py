@@ -62,6 +62,7 @@ SIGNATURES = {
                                        ctypes.POINTER(c_i32)]),
     "cp_quantize_q8_0": (ctypes.c_int, [c_vp, c_i64, c_i32, c_i64, c_vp, c_vp]),
     "cp_plan_chunk": (c_i32, [c_i32, c_i32, c_i32, ctypes.c_double]),
+    "cp_last_logits": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32, c_i32, c_f, c_vp, c_vp]),
     "cp_peak_sink_bytes": (c_sz, []),
     "cp_measure_peaks": (ctypes.c_int, [c_vp, c_sz, c_vp, c_sz, c_vp, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_double)]),

@@ -832,6 +832,15 @@ int cp_quantize_q8_0(const float* x, int64_t rows, int32_t k, int64_t ldx, void*
   return launch_quantize_q8_0(x, rows, k, ldx, out, (hipStream_t)stream) == hipSuccess ? CP_OK : CP_E_DEVICE;
 }
 
+int cp_last_logits(const float* x_row, const float* norm_gain, const void* lm_head, int32_t vocab,
+                   int32_t d_model, float eps, float* logits, void* hip_stream) {
+  if (!x_row || !norm_gain || !lm_head || !logits || vocab < 1 || d_model < QK || d_model % QK ||
+      d_model > 32768 || !(eps > 0.0f) || ((uintptr_t)lm_head % 2))
+    return CP_E_INVALID;
+  return launch_last_logits(x_row, norm_gain, lm_head, vocab, d_model, eps, logits,
+                            (hipStream_t)hip_stream) == hipSuccess ? CP_OK : CP_E_DEVICE;
+}
+
 int32_t cp_plan_chunk(int32_t n_tokens, int32_t cap, int32_t stages, double b_over_a) {
   if (n_tokens < 0 || cap < 1 || stages < 1 || !(b_over_a > 0.0) || !std::isfinite(b_over_a))
     return CP_E_INVALID;

@@ -142,4 +142,8 @@ size_t peak_sink_bytes();
 hipError_t launch_mfma_peak(int32_t iters, float* sink, hipStream_t s, double* flops);
 hipError_t launch_stream_read(const void* buf, int64_t n_bytes, uint32_t* sink, hipStream_t s);
 
+// Last-position logits (k_elem.hip).
+hipError_t launch_last_logits(const float* x, const float* gamma, const void* head, int32_t vocab,
+                              int32_t d, float eps, float* logits, hipStream_t s);
+
 }  // namespace cp

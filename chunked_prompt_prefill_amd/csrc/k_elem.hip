@@ -645,3 +645,70 @@ hipError_t launch_moe_unpermute(const float* y_perm, const MoeBuffers& b, int32_
 }
 
 }  // namespace cp
+
+namespace cp {
+
+// ======================================================================================
+// Last-position logits: RMSNorm of one row, then logits[v] = sum_b d_vb * sum_j q_vbj * y_j
+// over the q8_0 LM head in its interchange layout (rows of d/32 blocks of 34 bytes).
+// HBM-bound: every head byte is read once.  The normed row is staged in LDS (float32);
+// a wave takes one vocabulary row at a time, its lanes consecutive blocks (so a load
+// instruction covers 64 adjacent blocks), each lane reading its block as 17 halfwords;
+// the per-lane partial dot products are summed across the wave.
+// ======================================================================================
+constexpr int LMW = 4;   // waves per workgroup
+
+__global__ __launch_bounds__(LMW * 64) void last_logits_kernel(const float* __restrict__ x,
+                                                               const float* __restrict__ gamma,
+                                                               const uint8_t* __restrict__ head,
+                                                               int32_t vocab, int32_t d, float eps,
+                                                               float* __restrict__ logits) {
+  extern __shared__ float sy[];
+  __shared__ float red[LMW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // RMSNorm of the row (every workgroup recomputes it: d values, negligible next to the head)
+  float ss = 0.0f;
+  for (int i = tid; i < d; i += LMW * 64) ss += x[i] * x[i];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < LMW; ++w) tot += red[w];
+  const float scale = 1.0f / sqrtf(tot / (float)d + eps);
+  for (int i = tid; i < d; i += LMW * 64) sy[i] = x[i] * scale * gamma[i];
+  __syncthreads();
+  const int nb = d / QK;
+  const int64_t row_bytes = (int64_t)nb * 34;
+  for (int64_t v = (int64_t)blockIdx.x * LMW + wave; v < vocab; v += (int64_t)gridDim.x * LMW) {
+    const uint16_t* row = reinterpret_cast<const uint16_t*>(head + v * row_bytes);
+    float part = 0.0f;
+    for (int b = lane; b < nb; b += 64) {
+      const uint16_t* blk = row + b * 17;           // 34 bytes = 17 halfwords
+      const float db = half_bits_to_float(blk[0]);
+      const float* ys = sy + b * QK;
+      float p = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint16_t two = blk[1 + j];
+        p = fmaf((float)(int8_t)(two & 0xFF), ys[2 * j], p);
+        p = fmaf((float)(int8_t)(two >> 8), ys[2 * j + 1], p);
+      }
+      part = fmaf(db, p, part);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+    if (lane == 0) logits[v] = part;
+  }
+}
+
+hipError_t launch_last_logits(const float* x, const float* gamma, const void* head, int32_t vocab,
+                              int32_t d, float eps, float* logits, hipStream_t s) {
+  const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(vocab, LMW), 2048);
+  hipLaunchKernelGGL(last_logits_kernel, dim3(grid), dim3(LMW * 64), (size_t)d * sizeof(float), s,
+                     x, gamma, (const uint8_t*)head, vocab, d, eps, logits);
+  return hipGetLastError();
+}
+
+}  // namespace cp

@@ -162,6 +162,19 @@ def cp_quantize_q8_0(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> tor
     return out
 
 
+def cp_last_logits(x_row: torch.Tensor, norm_gain: torch.Tensor, lm_head: torch.Tensor,
+                   vocab: int, eps: float, logits: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Logits of one residual row: RMSNorm then the q8_0 LM head (interchange bytes)."""
+    d = x_row.numel()
+    if logits is None:
+        logits = torch.empty(vocab, dtype=torch.float32, device=x_row.device)
+    rc = lib().cp_last_logits(ptr(x_row), ptr(norm_gain), ptr(lm_head), int(vocab), int(d), float(eps),
+                              ptr(logits), stream_ptr())
+    if rc != CP_OK:
+        raise PrefillError(rc, "cp_last_logits failed")
+    return logits
+
+
 def cp_plan_chunk(n_tokens: int, cap: int, stages: int, b_over_a: float) -> int:
     """Pipeline chunk size from the fitted b/a (host code of the library)."""
     c = lib().cp_plan_chunk(int(n_tokens), int(cap), int(stages), float(b_over_a))

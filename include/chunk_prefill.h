@@ -185,6 +185,21 @@ void prefill_free(cp_ctx* ctx);   /* releases host-side state only; buffers stay
 int cp_kernel_timing(cp_ctx* ctx, const char* classes);
 int cp_kernel_times(cp_ctx* ctx, const char* kernel_class, float* total_ms, int32_t* launches);
 
+/* Logits of the last prompt position, the step after prefill: y = RMSNorm(x_row) * gain
+ * (float32, eps inside the square root), logits[v] = sum_b d_vb * sum_j q_vbj * y_32b+j
+ * over a q8_0 LM head (float32 accumulation).  The prefill planner page checks chunked
+ * against unchunked prefill by the logits at the last prompt position ("refactor: one
+ * prefill planner and one pad-trim hook for CLI and server", sections "Current Behavior"
+ * and "Acceptance Criteria").
+ *   x_row: dev float32 [d_model] (e.g. the last row of prefill_chunk's x_out);
+ *   norm_gain: dev float32 [d_model];
+ *   lm_head: dev q8_0 interchange [vocab][d_model/32 x 34 bytes], 2-byte aligned;
+ *   logits: dev float32 [vocab].
+ * d_model % 32 == 0 and <= 32768.  Enqueued on hip_stream.  Returns CP_OK, CP_E_INVALID
+ * for bad arguments, CP_E_DEVICE if the launch fails.  No allocation, no state. */
+int cp_last_logits(const float* x_row, const float* norm_gain, const void* lm_head, int32_t vocab,
+                   int32_t d_model, float eps, float* logits, void* hip_stream);
+
 /* Chunk size for an n_tokens prompt read over `stages` layer-split pipeline stages, from a
  * layer's fitted cost per chunk b and per token a (as b/a, in tokens): "Prompt chunks sized
  * for a layer split's pipeline", sections "Summary" and "What changed".  A prompt in chunks

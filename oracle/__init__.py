@@ -39,5 +39,6 @@ from .state import (state_bytes, state_size, parse_state, load_state, row_bytes,
                     STATE_MAGIC, STATE_VERSION)
 from .costfit import fit_linear, fit_quadratic
 from .planner import pipeline_chunk
+from .logits import last_logits
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -278,3 +278,20 @@ def test_router_bit_exact(torch, cpa, n, d, E, k):
     assert np.array_equal(logits.cpu().numpy().view(np.uint32), r.view(np.uint32))
     assert np.array_equal(idx.cpu().numpy(), ridx)
     assert np.allclose(wt.cpu().numpy(), rw, rtol=1e-5, atol=1e-7)
+
+
+# --------------------------------------------------------------------------- last logits
+@pytest.mark.parametrize("vocab,d", [(4096, 5120), (1000, 256), (33, 2048)])
+def test_last_logits_matches_oracle(torch, cpa, vocab, d):
+    """RMSNorm + q8_0 LM head on one row: float32 accumulation against the float64
+    definition, to 1e-4 of the largest logit."""
+    log(f"last logits vocab={vocab} d={d}")
+    x = synth.normal(synth.tensor_seed("xrow", d), (d,), scale=1.0)
+    gamma = (1.0 + synth.normal(synth.tensor_seed("g", d), (d,))).astype(np.float32)
+    head = oracle.q8_0_encode_bytes(synth.normal(synth.tensor_seed("head", vocab, d), (vocab, d)))
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    got = cpa.cp_last_logits(T(x), T(gamma), T(head), vocab, 1e-6).cpu().numpy()
+    ref = oracle.last_logits(x, gamma, head, d, 1e-6)
+    e = rel_err(got, ref)
+    log(f"  max rel err {e:.3e}")
+    assert e < 1e-4

@@ -215,3 +215,30 @@ def test_prefix_resume_equals_full_prefill(torch, kv):
     e2 = rel_err(got, ref[64:])
     log(f"  prefix resume kv={kv}: other chunking vs full {e1:.3e}, vs oracle {e2:.3e}")
     assert e1 < TOL and e2 < TOL
+
+
+def test_last_position_logits_chunked_and_unchunked(torch):
+    """The tiny dense decoder's 512-token prompt read in chunks of 1, 7, 128 and 512: the
+    last-position logits (RMSNorm + a q8_0 head of 4096 rows) agree with each other and with
+    the oracle's."""
+    import chunked_prompt_prefill_amd as cpa
+    w = synth.WORKLOADS["tiny_dense"]
+    ql = q8_layers(w, gains="ones")
+    x = synth.prompt_inputs(w)
+    head = oracle.q8_0_encode_bytes(synth.normal(synth.tensor_seed("lm_head", w.vocab, w.d_model),
+                                                 (w.vocab, w.d_model)))
+    gamma = np.ones(w.d_model, np.float32)
+    ref = oracle.last_logits(oracle.OracleModel(w, ql).prefill_layer_major(x)[-1], gamma, head,
+                             w.d_model, w.rms_eps)
+    hd, gd = torch.from_numpy(head).cuda(), torch.from_numpy(gamma).cuda()
+    outs = {}
+    for chunk in (1, 7, 128, 512):
+        out, ctx = run_prefill(torch, w, ql, x, chunk)
+        row = torch.from_numpy(np.ascontiguousarray(out[-1])).cuda()
+        outs[chunk] = cpa.cp_last_logits(row, gd, hd, w.vocab, w.rms_eps).cpu().numpy()
+        e = rel_err(outs[chunk], ref)
+        log(f"  chunk {chunk}: last logits max rel err {e:.3e}, argmax {int(np.argmax(outs[chunk]))} "
+            f"(oracle {int(np.argmax(ref))})")
+        assert e < TOL
+    for c in (1, 7, 512):
+        assert rel_err(outs[c], outs[128]) < TOL

@@ -58,3 +58,34 @@ def test_synth_numpy_and_torch_paths_are_bit_identical():
     assert abs(x.mean()) < 0.01 and abs(x.std() - 1.0) < 0.01
     assert np.array_equal(synth.normal(5, (10,)), synth.normal(5, (10,)))
     assert not np.array_equal(synth.normal(5, (10,)), synth.normal(6, (10,)))
+
+
+def test_last_logits_by_hand():
+    """Two head rows of 32 values each: row 0 holds 127 in column 3 and zeros elsewhere, so
+    its block scale is exactly 1 and its logit is y_3 * 127; row 1 holds -2 in column 0 and 2
+    in column 31 (scale 2/127 after fp16 rounding).  x is constant, so RMSNorm gives 1 * gamma."""
+    d = 32
+    W = np.zeros((2, d), np.float32)
+    W[0, 3] = 127.0
+    W[1, 0], W[1, 31] = -2.0, 2.0
+    head = oracle.q8_0_encode_bytes(W)
+    gamma = np.arange(1, d + 1, dtype=np.float32) / 16.0
+    x = np.full(d, 0.5, np.float32)
+    got = oracle.last_logits(x, gamma, head, d, 1e-6)
+    y = 0.5 / np.sqrt(0.25 + 1e-6) * gamma.astype(np.float64)
+    s1 = float(np.float16(np.float32(2.0) / np.float32(127.0)))   # stored scale of row 1
+    assert abs(got[0] - 127.0 * y[3]) < 1e-12
+    assert abs(got[1] - s1 * 127.0 * (y[31] - y[0])) < 1e-12
+
+
+def test_last_logits_chunk_invariant():
+    """The last-position logits of a chunked prefill equal those of the whole prompt at once."""
+    from model_inputs import TINY_DENSE, q8_layers
+    w = TINY_DENSE
+    m = oracle.OracleModel(w, q8_layers(w))
+    x = synth.prompt_inputs(w)
+    head = oracle.q8_0_encode_bytes(synth.normal(synth.tensor_seed("head", 97, w.d_model), (97, w.d_model)))
+    gamma = np.ones(w.d_model, np.float32)
+    full = oracle.last_logits(m.prefill_layer_major(x)[-1], gamma, head, w.d_model, 1e-6)
+    chunked = oracle.last_logits(m.prefill(x, 3)[-1], gamma, head, w.d_model, 1e-6)
+    assert np.max(np.abs(full - chunked)) <= 1e-12 * np.max(np.abs(full))
