@@ -298,6 +298,8 @@ def run_pmc_probe(args, torch, cpa, synth):
     the benchmark times (the GEMM plans and tiles depend on the chunk size, not the
     depth), with few enough dispatches for per-dispatch counter collection."""
     w = synth.WORKLOADS[args.workload].with_(n_layer=1)
+    if args.pmc_chunk:
+        w = w.with_(chunk=args.pmc_chunk)
     C, D = w.chunk, args.pmc_depth
     layers = gpu_layers(w, torch, cpa, synth)
     ctx = cpa.PrefillContext(cpa.make_config(w, D + C, C), layers)
@@ -422,6 +424,8 @@ def main():
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for rocprofv3 --pmc: the copy probe, then one chunk of the workload's "
                          "chunk size through one of its layers (no timing events), and exit")
+    ap.add_argument("--pmc-chunk", type=int, default=0,
+                    help="with --pmc-probe: chunk size instead of the workload's own")
     ap.add_argument("--pmc-depth", type=int, default=0,
                     help="with --pmc-probe: first prefill this many positions (in chunks of the "
                          "workload's chunk size), so the probed chunk attends at that depth")
