@@ -341,9 +341,13 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
       // keep the buffer valid, and the result is unused) interleave with tile t's
       // exponentials, so the MFMAs of one tile run under the softmax of the other; V^T P^T
       // of tile t follows.
-      f32x16 sc[2], sn[2];
-      auto step = [&](auto J, int t) __attribute__((always_inline)) {
+      // Two score sets alternate between "this tile" and "the next" (P selects which holds
+      // this tile), so no scores are copied: six steps cover both buffer and set cycles.
+      f32x16 sa[2], sb[2];
+      auto step = [&](auto J, auto P, int t) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value;
+        f32x16 (&sc)[2] = decltype(P)::value ? sb : sa;
+        f32x16 (&sn)[2] = decltype(P)::value ? sa : sb;
         attn_wait_vm_lgkm<0>();
         __builtin_amdgcn_s_barrier();
         attn_cfence();
@@ -371,20 +375,23 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (i < 13) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
-#pragma unroll
-          for (int jb = 0; jb < 2; ++jb) sc[jb] = sn[jb];
         }
       };
+      using P0 = std::false_type;
+      using P1 = std::true_type;
       issue_f16(I0{}, jt0);
       issue_f16(I1{}, min(jt0 + 1, last));
       attn_wait_vm_lgkm<NLOAD>();      // tile jt0 landed (own loads)
       __builtin_amdgcn_s_barrier();    // everyone's
       attn_cfence();
-      qk(bufK(I0{}), sc);
-      for (int t = jt0; t < jt1; t += 3) {
-        step(I0{}, t);
-        step(I1{}, t + 1);
-        step(I2{}, t + 2);
+      qk(bufK(I0{}), sa);
+      for (int t = jt0; t < jt1; t += 6) {
+        step(I0{}, P0{}, t);
+        step(I1{}, P1{}, t + 1);
+        step(I2{}, P0{}, t + 2);
+        step(I0{}, P1{}, t + 3);
+        step(I1{}, P0{}, t + 4);
+        step(I2{}, P1{}, t + 5);
       }
       attn_wait_vm0();
     } else {
