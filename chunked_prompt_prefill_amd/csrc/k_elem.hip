@@ -384,14 +384,88 @@ hipError_t launch_unpack_router(const void* src, int32_t E, int32_t d, int8_t* q
   return hipGetLastError();
 }
 
+// Top-k of one token's E logits (descending logit, ties to the lower expert index) and
+// the softmax over the k selected ones, by one wave: lane l holds experts l, l+64, l+128
+// and l+192.  lg may point to LDS or to global memory.
+__device__ void route_topk(const float* lg, int32_t E, int32_t k, int lane, int32_t* idx_row,
+                           float* w_row) {
+  float v[4];
+  bool used[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? lg[e] : -INFINITY;
+    used[j] = e >= E;
+  }
+  float selv[16];
+  int sele[16];
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      if (!used[j] && (v[j] > bv || (v[j] == bv && e < be))) { bv = v[j]; be = e; }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oe = __shfl_xor(be, o, 64);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j == be) used[j] = true;
+    selv[r] = bv;
+    sele[r] = be;
+  }
+  if (lane == 0) {
+    float z = 0.0f;
+    float ex[16];
+    for (int r = 0; r < k; ++r) { ex[r] = expf(selv[r] - selv[0]); z += ex[r]; }
+    for (int r = 0; r < k; ++r) {
+      idx_row[r] = sele[r];
+      w_row[r] = ex[r] / z;
+    }
+  }
+}
+
+// One router block product in the fixed float32 order: P = sum_j q_j * y_j, products
+// rounded, then added in ascending j.
+__device__ __forceinline__ float router_block_dot(const float* qf, const float4* ys) {
+  float4 yv = ys[0];
+  float P = __fmul_rn(qf[0], yv.x);
+  P = __fadd_rn(P, __fmul_rn(qf[1], yv.y));
+  P = __fadd_rn(P, __fmul_rn(qf[2], yv.z));
+  P = __fadd_rn(P, __fmul_rn(qf[3], yv.w));
+#pragma unroll
+  for (int j4 = 1; j4 < QK / 4; ++j4) {
+    yv = ys[j4];
+    P = __fadd_rn(P, __fmul_rn(qf[4 * j4 + 0], yv.x));
+    P = __fadd_rn(P, __fmul_rn(qf[4 * j4 + 1], yv.y));
+    P = __fadd_rn(P, __fmul_rn(qf[4 * j4 + 2], yv.z));
+    P = __fadd_rn(P, __fmul_rn(qf[4 * j4 + 3], yv.w));
+  }
+  return P;
+}
+
+__device__ __forceinline__ void router_block_weights(const int8_t* rq_blk, float* qf) {
+  const uint4* qp = reinterpret_cast<const uint4*>(rq_blk);
+  const uint4 qa = qp[0], qb = qp[1];
+  const uint32_t w[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+  for (int j = 0; j < QK; ++j) qf[j] = (float)(int8_t)((w[j >> 2] >> (8 * (j & 3))) & 0xFF);
+}
+
 // Router logits in the fixed float32 order (per block: products and sums ascending,
-// then acc += d_b * P_b over blocks ascending), then top-k (descending logit, ties to
-// the lower expert index) and softmax over the k selected logits.  Threads are (expert,
-// token group): with E <= 128 two groups of 128 threads each take 8 of the workgroup's 16
-// tokens, otherwise one group of 256 takes 8.  Each thread converts a block's 32 weights
-// to float once and applies them to its 8 tokens; y is staged 256 columns at a time.
-constexpr int RT = 16;       // tokens per workgroup, at most
-constexpr int RTT = 8;       // tokens per thread
+// then acc += d_b * P_b over blocks ascending), then top-k and softmax (route_topk).
+// Threads are (expert, token group): with E <= 128 two groups of 128 threads each take 4
+// of the workgroup's 8 tokens, otherwise one group of 256 takes 4 (small workgroups: many
+// of them in flight, since each thread's sums are serial chains).  Each thread converts a
+// block's 32 weights to float once and applies them to its 4 tokens; y is staged 256
+// columns at a time and read from LDS as a broadcast.
+constexpr int RT = 8;        // tokens per workgroup, at most
+constexpr int RTT = 4;       // tokens per thread
 __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ y,
                                                      const int8_t* __restrict__ rq,
                                                      const uint16_t* __restrict__ rd, int32_t n,
@@ -424,30 +498,12 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ y
         const int col = c0 + b * QK;
         if (col >= d) break;
         const int blk = col / QK;
-        const uint4* qp = reinterpret_cast<const uint4*>(rq + (int64_t)e * d + col);
-        const uint4 qa = qp[0], qb = qp[1];
-        const uint32_t w[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
         float qf[QK];
-#pragma unroll
-        for (int j = 0; j < QK; ++j) qf[j] = (float)(int8_t)((w[j >> 2] >> (8 * (j & 3))) & 0xFF);
+        router_block_weights(rq + (int64_t)e * d + col, qf);
         const float ds = half_bits_to_float(rd[(int64_t)e * (d / QK) + blk]);
 #pragma unroll
         for (int tt = 0; tt < RTT; ++tt) {
-          const float4* ys = &sy4[grp * RTT + tt][b * (QK / 4)];
-          float4 yv = ys[0];
-          float P = __fmul_rn(qf[0], yv.x);
-          P = __fadd_rn(P, __fmul_rn(qf[1], yv.y));
-          P = __fadd_rn(P, __fmul_rn(qf[2], yv.z));
-          P = __fadd_rn(P, __fmul_rn(qf[3], yv.w));
-#pragma unroll
-          for (int j4 = 1; j4 < QK / 4; ++j4) {
-            yv = ys[j4];
-            P = __fadd_rn(P, __fmul_rn(qf[4 * j4 + 0], yv.x));
-            P = __fadd_rn(P, __fmul_rn(qf[4 * j4 + 1], yv.y));
-            P = __fadd_rn(P, __fmul_rn(qf[4 * j4 + 2], yv.z));
-            P = __fadd_rn(P, __fmul_rn(qf[4 * j4 + 3], yv.w));
-          }
-          const float term = __fmul_rn(ds, P);
+          const float term = __fmul_rn(ds, router_block_dot(qf, &sy4[grp * RTT + tt][b * (QK / 4)]));
           acc[tt] = (blk == 0) ? term : __fadd_rn(acc[tt], term);
         }
       }
@@ -467,52 +523,71 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ y
   for (int tt = wave; tt < RTW; tt += 4) {
     const int t = t0 + tt;
     if (t >= n) break;
-    float v[4];
-    bool used[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      v[j] = e < E ? slog[tt][e] : -INFINITY;
-      used[j] = e >= E;
-    }
-    float selv[16];
-    int sele[16];
-    for (int r = 0; r < k; ++r) {
-      float bv = -INFINITY;
-      int be = 0x7FFFFFFF;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = lane + 64 * j;
-        if (!used[j] && (v[j] > bv || (v[j] == bv && e < be))) { bv = v[j]; be = e; }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oe = __shfl_xor(be, o, 64);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (lane + 64 * j == be) used[j] = true;
-      selv[r] = bv;
-      sele[r] = be;
-    }
-    if (lane == 0) {
-      float z = 0.0f;
-      float ex[16];
-      for (int r = 0; r < k; ++r) { ex[r] = expf(selv[r] - selv[0]); z += ex[r]; }
-      for (int r = 0; r < k; ++r) {
-        idx[(int64_t)t * k + r] = sele[r];
-        wout[(int64_t)t * k + r] = ex[r] / z;
-      }
-    }
+    route_topk(slog[tt], E, k, lane, idx + (int64_t)t * k, wout + (int64_t)t * k);
   }
 }
+
+// Few tokens (decode-sized chunks): the per-token work of the kernel above is one serial
+// chain per expert, too long for a handful of workgroups.  Here a wave owns one expert and
+// RSN tokens; lane b computes the block products d_b * P_b of blocks b, b+64, ... (same
+// float32 order), parks them in LDS, and lane t then adds them in ascending block order.
+// Top-k follows in router_topk_kernel, over the logits written here.
+constexpr int RSN = 4;          // tokens per wave
+constexpr int kRouterSmallMaxBlocks = 256;   // d <= 8192
+__global__ __launch_bounds__(64) void router_small_kernel(const float* __restrict__ y,
+                                                          const int8_t* __restrict__ rq,
+                                                          const uint16_t* __restrict__ rd,
+                                                          int32_t n, int32_t d, int32_t E,
+                                                          float* __restrict__ logits) {
+  __shared__ float sterm[RSN][kRouterSmallMaxBlocks];
+  const int lane = threadIdx.x;
+  const int e = blockIdx.x;
+  const int t0 = blockIdx.y * RSN;
+  const int nt = min(RSN, n - t0);
+  const int nb = d / QK;
+  for (int blk = lane; blk < nb; blk += 64) {
+    float qf[QK];
+    router_block_weights(rq + (int64_t)e * d + blk * QK, qf);
+    const float ds = half_bits_to_float(rd[(int64_t)e * nb + blk]);
+    for (int tt = 0; tt < nt; ++tt) {
+      const float4* ys = reinterpret_cast<const float4*>(y + (int64_t)(t0 + tt) * d + blk * QK);
+      sterm[tt][blk] = __fmul_rn(ds, router_block_dot(qf, ys));
+    }
+  }
+  __syncthreads();
+  if (lane < nt) {
+    float acc = sterm[lane][0];
+    for (int blk = 1; blk < nb; ++blk) acc = __fadd_rn(acc, sterm[lane][blk]);
+    logits[(int64_t)(t0 + lane) * E + e] = acc;
+  }
+}
+
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
+                                                          int32_t n, int32_t E, int32_t k,
+                                                          int32_t* __restrict__ idx,
+                                                          float* __restrict__ wout) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= n) return;
+  route_topk(logits + (int64_t)t * E, E, k, threadIdx.x & 63, idx + (int64_t)t * k,
+             wout + (int64_t)t * k);
+}
+
+// token count up to which the wave-per-expert router runs
+constexpr int32_t kRouterSmallN = 16;
 
 hipError_t launch_router(const float* y, const int8_t* rq, const uint16_t* rd, int32_t n, int32_t d,
                          int32_t E, int32_t k, float* logits, int32_t* idx, float* w,
                          hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  if (n <= kRouterSmallN && d / QK <= kRouterSmallMaxBlocks) {
+    hipLaunchKernelGGL(router_small_kernel, dim3((unsigned)E, (unsigned)ceil_div(n, RSN)), dim3(64), 0, s,
+                       y, rq, rd, n, d, E, logits);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)ceil_div(n, 4)), dim3(256), 0, s, logits, n, E,
+                       k, idx, w);
+    return hipGetLastError();
+  }
   const int rtw = RTT * (E <= 128 ? 2 : 1);
   hipLaunchKernelGGL(router_kernel, dim3((unsigned)ceil_div(n, rtw)), dim3(256), 0, s, y, rq, rd, n,
                      d, E, k, logits, idx, w);
@@ -546,6 +621,9 @@ __global__ __launch_bounds__(256) void moe_rank_kernel(const int32_t* __restrict
   for (int e = tid; e < E; e += 256) chunk_cnt[(int64_t)blockIdx.x * E + e] = scnt[e];
 }
 
+// per-chunk counts staged in LDS by the scan when they fit (16K counts = 64 KiB)
+constexpr int64_t kMoeScanLds = 16384;
+
 __global__ __launch_bounds__(256) void moe_scan_kernel(int32_t n_chunks, int32_t E, int32_t mt,
                                                        int32_t max_tiles,
                                                        int32_t* __restrict__ chunk_cnt,
@@ -554,33 +632,77 @@ __global__ __launch_bounds__(256) void moe_scan_kernel(int32_t n_chunks, int32_t
                                                        int32_t* __restrict__ n_tiles) {
   __shared__ int32_t stot[256];
   __shared__ int32_t soff[257];
+  extern __shared__ int32_t scnt[];     // [n_chunks][E] when it fits (see the launch)
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 256) {
-    int total = 0;
-    for (int c = 0; c < n_chunks; ++c) {
-      const int v = chunk_cnt[(int64_t)c * E + e];
-      chunk_cnt[(int64_t)c * E + e] = total;
-      total += v;
-    }
-    stot[e] = total;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int off = 0, nt = 0;
-    for (int e = 0; e < E; ++e) {
-      soff[e] = off;
-      offsets[e] = off;
-      for (int m = 0; m < stot[e] && nt < max_tiles; m += mt) {
-        reinterpret_cast<int4*>(tiles)[nt++] = make_int4(e, off + m, off + min(m + mt, stot[e]), 0);
+  const int64_t ncnt = (int64_t)n_chunks * E;
+  const bool staged = ncnt <= kMoeScanLds;
+  if (staged) {
+    // coalesced loads into LDS, the per-expert running sums there, coalesced stores back
+    for (int64_t u = tid; u < ncnt; u += 256) scnt[u] = chunk_cnt[u];
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) {
+      int total = 0;
+      for (int c = 0; c < n_chunks; ++c) {
+        const int v = scnt[c * E + e];
+        scnt[c * E + e] = total;
+        total += v;
       }
-      off += stot[e];
+      stot[e] = total;
     }
-    offsets[E] = off;
-    *n_tiles = nt;
+  } else {
+    for (int e = tid; e < E; e += 256) {
+      int total = 0;
+      for (int c = 0; c < n_chunks; ++c) {
+        const int v = chunk_cnt[(int64_t)c * E + e];
+        chunk_cnt[(int64_t)c * E + e] = total;
+        total += v;
+      }
+      stot[e] = total;
+    }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256)
-    for (int c = 0; c < n_chunks; ++c) chunk_cnt[(int64_t)c * E + e] += soff[e];
+  // expert offsets and tile-table offsets: exclusive prefix sums over the experts (E <= 256,
+  // one thread each; a log-step scan in LDS)
+  __shared__ int32_t ssum[2][256];
+  __shared__ int32_t tsum[2][256];
+  {
+    const int cnt = tid < E ? stot[tid] : 0;
+    const int ntl = tid < E ? (cnt + mt - 1) / mt : 0;
+    ssum[0][tid] = cnt;
+    tsum[0][tid] = ntl;
+    __syncthreads();
+    int src = 0;
+    for (int o = 1; o < 256; o <<= 1) {
+      const int v = ssum[src][tid] + (tid >= o ? ssum[src][tid - o] : 0);
+      const int u = tsum[src][tid] + (tid >= o ? tsum[src][tid - o] : 0);
+      ssum[src ^ 1][tid] = v;
+      tsum[src ^ 1][tid] = u;
+      __syncthreads();
+      src ^= 1;
+    }
+    const int off = ssum[src][tid] - cnt;            // exclusive sums
+    const int t0 = tsum[src][tid] - ntl;
+    if (tid < E) {
+      soff[tid] = off;
+      offsets[tid] = off;
+      for (int i = 0; i < ntl; ++i) {
+        const int m = i * mt;
+        if (t0 + i < max_tiles)
+          reinterpret_cast<int4*>(tiles)[t0 + i] = make_int4(tid, off + m, off + min(m + mt, cnt), 0);
+      }
+    }
+    if (tid == 255) {
+      offsets[E] = ssum[src][255];
+      *n_tiles = min(tsum[src][255], max_tiles);
+    }
+  }
+  __syncthreads();
+  if (staged) {
+    for (int64_t u = tid; u < ncnt; u += 256) chunk_cnt[u] = scnt[u] + soff[u % E];
+  } else {
+    for (int e = tid; e < E; e += 256)
+      for (int c = 0; c < n_chunks; ++c) chunk_cnt[(int64_t)c * E + e] += soff[e];
+  }
 }
 
 __global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restrict__ idx, int32_t n_slots,
@@ -604,7 +726,8 @@ hipError_t launch_moe_permute(const MoeBuffers& b, int32_t n, int32_t E, int32_t
                      b.rank, b.chunk_cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(256), 0, s, n_chunks, E, mt, max_tiles,
+  const size_t scan_lds = (int64_t)n_chunks * E <= kMoeScanLds ? (size_t)n_chunks * E * 4 : 0;
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(256), scan_lds, s, n_chunks, E, mt, max_tiles,
                      b.chunk_cnt, b.offsets, b.tiles, b.n_tiles);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

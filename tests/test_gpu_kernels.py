@@ -261,7 +261,11 @@ def test_attention_keys_of_one_lane_half_dominate(torch, cpa, kv):
 
 
 # --------------------------------------------------------------------------- router
-@pytest.mark.parametrize("n,d,E,k", [(37, 2048, 128, 8), (5, 256, 8, 2), (64, 512, 256, 16)])
+# n <= 16 takes the wave-per-expert kernel (decode-sized chunks), larger n the
+# token-tiled one; d = 8224 (257 blocks) sends a small n to the tiled kernel too.
+@pytest.mark.parametrize("n,d,E,k", [(37, 2048, 128, 8), (5, 256, 8, 2), (64, 512, 256, 16),
+                                     (1, 2048, 128, 8), (3, 2048, 128, 8), (16, 4096, 64, 4),
+                                     (17, 4096, 64, 4), (2, 8224, 16, 2)])
 def test_router_bit_exact(torch, cpa, n, d, E, k):
     log(f"router n={n} d={d} E={E} k={k}")
     y = synth.normal(synth.tensor_seed("y", n, d), (n, d), scale=1.0)
