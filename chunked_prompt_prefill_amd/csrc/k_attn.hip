@@ -444,26 +444,64 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
 }
 
 // Merge split-KV partials: o = sum_s 2^(m_s - m*) O_s / sum_s 2^(m_s - m*) l_s.
+// A row's hd/4 column quads times SL "split lanes" share the work: split lane j takes the
+// splits j, j+SL, ..., so the partial loads of one row are in flight together; the lanes'
+// maxima, weights and sums meet in LDS and are added in lane order (a fixed order).  SL
+// grows (up to 8, and not past the split count) only while rows x quads alone would leave
+// the chip short of threads, as with decode-sized chunks.
+__host__ __device__ constexpr int combine_split_lanes(int splits, int64_t row_quads) {
+  int sl = 1;
+  while (sl < 8 && sl < splits && row_quads * sl < (int64_t(1) << 18)) sl *= 2;
+  return sl;
+}
+
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float red[5][256];
   const int G = a.n_head / a.n_kv_head;
   const int64_t R = (int64_t)a.n * G;
   const int64_t rows_total = (int64_t)a.n_kv_head * R;
   const int hd = a.head_dim;
-  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (u >= rows_total * (hd / 4)) return;
-  const int64_t rg = u / (hd / 4);
-  const int d0 = (int)(u % (hd / 4)) * 4;
+  const int Q = hd / 4;
+  const int SL = combine_split_lanes(a.splits, rows_total * Q);
+  const int per_row = Q * SL;
+  const int tid = threadIdx.x;
+  const int rl = tid / per_row, sl = (tid % per_row) / Q, q = tid % Q;
+  const int64_t rg = (int64_t)blockIdx.x * (256 / per_row) + rl;
+  const bool live = rl < 256 / per_row && rg < rows_total;
+  const int d0 = q * 4;
+  float m = -INFINITY;
+  if (live) {
+#pragma unroll 4
+    for (int s = sl; s < a.splits; s += SL) m = fmaxf(m, a.part_ml[((int64_t)s * rows_total + rg) * 2]);
+  }
+  red[0][tid] = m;
+  __syncthreads();
   float mstar = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) mstar = fmaxf(mstar, a.part_ml[((int64_t)s * rows_total + rg) * 2]);
+  const int base = rl * per_row + q;
+  if (live)
+    for (int j = 0; j < SL; ++j) mstar = fmaxf(mstar, red[0][base + j * Q]);
   float den = 0.0f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < a.splits; ++s) {
-    const float ms = a.part_ml[((int64_t)s * rows_total + rg) * 2];
-    if (ms == -INFINITY) continue;
-    const float w = __builtin_amdgcn_exp2f(ms - mstar);
-    den += w * a.part_ml[((int64_t)s * rows_total + rg) * 2 + 1];
-    const float4 po = *reinterpret_cast<const float4*>(a.part_o + ((int64_t)s * rows_total + rg) * hd + d0);
-    num.x += w * po.x; num.y += w * po.y; num.z += w * po.z; num.w += w * po.w;
+  if (live) {
+#pragma unroll 4
+    for (int s = sl; s < a.splits; s += SL) {
+      const float ms = a.part_ml[((int64_t)s * rows_total + rg) * 2];
+      if (ms == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(ms - mstar);
+      den += w * a.part_ml[((int64_t)s * rows_total + rg) * 2 + 1];
+      const float4 po = *reinterpret_cast<const float4*>(a.part_o + ((int64_t)s * rows_total + rg) * hd + d0);
+      num.x += w * po.x; num.y += w * po.y; num.z += w * po.z; num.w += w * po.w;
+    }
+  }
+  __syncthreads();
+  red[0][tid] = den;
+  red[1][tid] = num.x; red[2][tid] = num.y; red[3][tid] = num.z; red[4][tid] = num.w;
+  __syncthreads();
+  if (!live || sl != 0) return;
+  for (int j = 1; j < SL; ++j) {
+    const int o = base + j * Q;
+    den += red[0][o];
+    num.x += red[1][o]; num.y += red[2][o]; num.z += red[3][o]; num.w += red[4][o];
   }
   const float inv = 1.0f / den;
   const int64_t g = rg / R, i = rg % R;
@@ -488,8 +526,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;
-  const int64_t work = (int64_t)a.n_kv_head * R * (a.head_dim / 4);
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)ceil_div(work, 256)), dim3(256), 0, s, a);
+  const int64_t rows_total = (int64_t)a.n_kv_head * R;
+  const int rows_per_wg = 256 / (a.head_dim / 4 * combine_split_lanes(a.splits, rows_total * (a.head_dim / 4)));
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)ceil_div(rows_total, rows_per_wg)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -221,7 +221,7 @@ def build_cache(torch, cpa, Hq, Hkv, hd, kv, T, seed, k_gain=None):
 @pytest.mark.parametrize("hd,Hq,Hkv,n,start,splits", [
     (64, 4, 2, 40, 0, 0), (64, 4, 2, 33, 100, 0), (128, 40, 8, 70, 300, 0),
     (128, 40, 8, 128, 700, 5), (128, 32, 4, 200, 0, 0), (128, 8, 8, 1, 250, 0),
-    (128, 40, 8, 300, 1234, 1)])
+    (128, 40, 8, 300, 1234, 1), (128, 40, 8, 256, 1000, 3), (64, 8, 2, 3, 900, 6)])
 def test_attention_matches_oracle(torch, cpa, kv, hd, Hq, Hkv, n, start, splits):
     log(f"attention kv={kv} hd={hd} Hq={Hq} Hkv={Hkv} n={n} start={start} splits={splits}")
     T = start + n
