@@ -163,6 +163,53 @@ def measured_traffic(kernel, per_launch):
     return r.get("hbm_bytes_per_launch")
 
 
+# sources whose text defines the dominant kernel's code: a change to any of them makes the
+# stored counter readings stale (measured_traffic then reports None)
+PMC_SOURCES = ["chunked_prompt_prefill_amd/csrc/k_gemm_big.hip",
+               "chunked_prompt_prefill_amd/csrc/k_common.h",
+               "chunked_prompt_prefill_amd/csrc/cp_internal.h"]
+
+
+def pmc_digest(fetch_csv, write_csv, copy_mib):
+    """Fold two rocprofv3 --pmc counter files of the --pmc-probe run (FETCH_SIZE, then
+    WRITE_SIZE) into profiles/pmc_traffic.json: the unsplit gate/up launch's readings,
+    each scaled by what the same counter reads for the plain copy of copy_mib MiB that the
+    probe runs first (the copy reads and writes exactly that many bytes)."""
+    import csv
+    import hashlib
+
+    def readings(path, grid_wg):
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+        copy = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")]
+        k = [float(r["Counter_Value"]) for r in rows
+             if "gemm_q8_big_kernel<2>" in r["Kernel_Name"]
+             and int(r["Grid_Size"]) // int(r["Workgroup_Size"]) == grid_wg]
+        if not copy or len(k) != 1:
+            raise SystemExit(f"{path}: expected the copy and one unsplit gate/up launch, got {len(copy)} / {len(k)}")
+        return copy[0], k[0]
+
+    cf, kf = readings(fetch_csv, 256)
+    cw, kw = readings(write_csv, 256)
+    probe_kib = copy_mib * 1024
+    ff, fw = probe_kib / cf, probe_kib / cw
+    h = hashlib.sha256()
+    for src in PMC_SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    rec = {"gemm_gate_up/full": {
+        "kernel": "gemm_q8_big_kernel<GM_SWIGLU> (256 workgroups, 256x256 tiles)",
+        "rows": 512, "fetch_size_kib": kf, "write_size_kib": kw,
+        "copy_probe_bytes": probe_kib * 1024, "copy_fetch_size_kib": cf, "copy_write_size_kib": cw,
+        "fetch_factor": ff, "write_factor": fw,
+        "hbm_read_bytes_per_launch": kf * 1024 * ff, "hbm_write_bytes_per_launch": kw * 1024 * fw,
+        "hbm_bytes_per_launch": kf * 1024 * ff + kw * 1024 * fw,
+        "sources": PMC_SOURCES, "sources_sha256": h.hexdigest()}}
+    with open(os.path.join(ROOT, "profiles", "pmc_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def run_main(args, torch, cpa, synth):
     w = synth.WORKLOADS[args.workload]
     n, C = w.n_prompt, w.chunk
@@ -432,7 +479,13 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB: the "
                          "reference reading that scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--pmc-digest", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: fold the counter files of the two --pmc-probe runs "
+                         "(taken with --copy-probe-mib 1024) into profiles/pmc_traffic.json")
     args = ap.parse_args()
+    if args.pmc_digest:
+        pmc_digest(*args.pmc_digest, copy_mib=1024)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               "(the multi-GPU layer split is a design note, not part of this build)", flush=True)
