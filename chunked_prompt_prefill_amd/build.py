@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libchunkprefill.so")
-SOURCES = ["cp_api.cpp", "k_gemm.hip", "k_gemm_big.hip", "k_elem.hip", "k_attn.hip", "k_peak.hip"]
+SOURCES = ["cp_api.cpp", "k_gemm.hip", "k_gemm_big.hip", "k_gemv.hip", "k_elem.hip", "k_attn.hip",
+           "k_peak.hip"]
 
 
 def hipcc() -> str:

@@ -153,9 +153,31 @@ GemmPlan plan_gemm_mt(int M, int N, int K, int mt, int force_splits) {
   return p;
 }
 
-// force_mt > 0 pins the row tile (tests); force_splits > 0 forces one launch with that
+// A few rows (decode-sized chunks): the weight-streaming kernel, "row tile" 1, one
+// workgroup per 64 columns and K split S ways.  Measured on the 27B-class shapes, the
+// stream runs near the HBM rate once about 600-900 workgroups are in flight, and each
+// split costs a reduction launch (about 4 us plus the gap between launches), so S brings
+// the workgroup count near 768 and no further (at most one 4-stage share per split).
+GemmPlan plan_gemm_skinny(int M, int N, int K, int force_splits) {
+  GemmPlan p;
+  p.mt = 1;
+  p.nparts = 1;
+  const int KQ = K / 128, P = N / 64;
+  int S;
+  if (force_splits > 0) S = std::min(force_splits, KQ);
+  else S = std::max(1, std::min((768 + P / 2) / P, std::max(1, KQ / 4)));
+  p.part[0] = {0, N, S};
+  p.partial_bytes = S > 1 ? (size_t)S * M * N * 4 : 0;
+  return p;
+}
+
+bool skinny_fits(int M, int N) { return M <= kSkinnyMaxRows && N % 64 == 0; }
+
+// force_mt > 0 pins the row tile (tests; 1 = the weight-streaming kernel, which needs
+// M <= kSkinnyMaxRows and N % 64 == 0); force_splits > 0 forces one launch with that
 // split-K factor.
 GemmPlan plan_gemm(int M, int N, int K, int force_splits = 0, int force_mt = 0) {
+  if (force_mt == 1 || (force_mt == 0 && skinny_fits(M, N))) return plan_gemm_skinny(M, N, K, force_splits);
   if (force_mt > 0) return plan_gemm_mt(M, N, K, force_mt, force_splits);
   if (M <= 64) return plan_gemm_mt(M, N, K, 64, force_splits);
   GemmPlan best = plan_gemm_mt(M, N, K, 128, force_splits);
@@ -436,8 +458,9 @@ hipError_t gemm(cp_ctx* c, const char* cls, const _Float16* A, int lda, int M, c
       g.splits = p.part[i].splits;
       g.partial = c->wsp<float>(c->WS.partial);
       // each launch is also timed on its own: "<class>/full" for an unsplit column range
-      // (one kernel), "<class>/split" for a split-K range (partial GEMM + ordered reduce)
-      const std::string sub = std::string(cls) + (g.splits > 1 ? "/split" : "/full");
+      // (one kernel), "<class>/split" for a split-K range (partial GEMM + ordered reduce),
+      // "<class>/skinny" for the weight-streaming kernel of a few rows
+      const std::string sub = std::string(cls) + (p.mt == 1 ? "/skinny" : g.splits > 1 ? "/split" : "/full");
       const hipError_t e = timed(c, sub.c_str(), [&] { return launch_gemm(g, 0, p.mt, c->stream); });
       if (e != hipSuccess) return e;
     }
@@ -941,9 +964,14 @@ int cp_test_router(const float* y, const void* w_router, int32_t n, int32_t d, i
   return launch_router(y, q, dd, n, d, E, k, logits, idx, weight, s) == hipSuccess ? CP_OK : CP_E_DEVICE;
 }
 
+bool test_row_tile_ok(int32_t M, int32_t N, int32_t row_tile) {
+  if (row_tile == 1) return skinny_fits(M, N);
+  return row_tile == 0 || row_tile == 64 || row_tile == 128 || row_tile == 256;
+}
+
 size_t cp_test_gemm_scratch_bytes_ex(int32_t M, int32_t N, int32_t K, int32_t splits, int32_t row_tile) {
   if (M < 1 || N < 32 || N % 32 || K < 128 || K % 128 || splits < 0) return 0;
-  if (row_tile != 0 && row_tile != 64 && row_tile != 128 && row_tile != 256) return 0;
+  if (!test_row_tile_ok(M, N, row_tile)) return 0;
   const GemmPlan p = plan_gemm(M, N, K, splits, row_tile);
   return align_up(QMat::q_bytes(N, K)) + align_up(QMat::d_bytes(N, K)) + align_up(p.partial_bytes + 4);
 }
@@ -957,7 +985,7 @@ int cp_test_gemm_ex(const void* A, const void* W, int32_t M, int32_t N, int32_t 
   if (!A || !W || !out || !scratch || M < 1 || N < 32 || N % 32 || K < 128 || K % 128 || mode < 0 ||
       mode > 2 || splits < 0)
     return CP_E_INVALID;
-  if (row_tile != 0 && row_tile != 64 && row_tile != 128 && row_tile != 256) return CP_E_INVALID;
+  if (!test_row_tile_ok(M, N, row_tile)) return CP_E_INVALID;
   if (mode == GM_SWIGLU && N % 64) return CP_E_INVALID;
   hipStream_t s = (hipStream_t)stream;
   QMat q;
@@ -965,6 +993,7 @@ int cp_test_gemm_ex(const void* A, const void* W, int32_t M, int32_t N, int32_t 
   q.d = (uint32_t*)((uint8_t*)scratch + align_up(QMat::q_bytes(N, K)));
   q.N = N; q.K = K;
   float* partial = (float*)((uint8_t*)q.d + align_up(QMat::d_bytes(N, K)));
+  const GemmPlan p = plan_gemm(M, N, K, splits, row_tile);
   hipError_t e;
   if (mode == GM_SWIGLU) {
     const int F = N / 2;
@@ -974,7 +1003,6 @@ int cp_test_gemm_ex(const void* A, const void* W, int32_t M, int32_t N, int32_t 
     e = launch_repack_q8_0(W, nullptr, N, K, 0, N, 0, q, s);
   }
   if (e != hipSuccess) return CP_E_DEVICE;
-  const GemmPlan p = plan_gemm(M, N, K, splits, row_tile);
   for (int i = 0; i < p.nparts; ++i) {
     GemmArgs g;
     g.A = (const _Float16*)A; g.lda = K; g.M = M; g.N = p.part[i].n1; g.K = K; g.n0 = p.part[i].n0;

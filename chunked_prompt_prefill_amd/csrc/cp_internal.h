@@ -53,11 +53,18 @@ struct GemmArgs {
   int32_t splits = 1;
 };
 
+// Rows up to which the weight-streaming kernel (k_gemv.hip) takes a GEMM.
+constexpr int kSkinnyMaxRows = 4;
+
 // Kernel launchers (return hipError_t of the launch).
 hipError_t launch_gemm(const GemmArgs& a, int grid_m_tiles, int mt, hipStream_t s);
 // 256-row tiles, one workgroup per CU (non-grouped only); the partial-sum reduction of a
 // split launch is left to the caller.
 hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t s);
+// M <= kSkinnyMaxRows, N % 64 == 0, whole column range; splits = K splits.  With one
+// split it applies the epilogue itself; with more it writes partial [S][M][N] and the
+// caller runs the split-K reduction (launch_gemm does).
+hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* partial, int32_t splits, int32_t M, int32_t n0,
                                 int32_t N, int32_t mode, void* out, int32_t ldo, hipStream_t s);
 // Repack interchange q8_0 rows into a QMat.  mode 0: destination rows dst_row0 ..

@@ -180,8 +180,10 @@ void prefill_free(cp_ctx* ctx);   /* releases host-side state only; buffers stay
  * "rope_kv_append", "rmsnorm", "moe_route", "moe_permute", "moe_gemm_gate_up",
  * "moe_gemm_down", "moe_unpermute".  A dense GEMM class runs as one or two launches over
  * column ranges; each launch is also its own class, "<gemm class>/full" for an unsplit
- * range (one kernel launch) and "<gemm class>/split" for a split-K range (the partial
- * GEMM and its ordered reduce), e.g. "gemm_gate_up/full". */
+ * range (one kernel launch), "<gemm class>/split" for a split-K range (the partial
+ * GEMM and its ordered reduce), e.g. "gemm_gate_up/full", and "<gemm class>/skinny" for
+ * the weight-streaming kernel that takes chunks of at most 4 tokens (with its reduce
+ * when it splits K). */
 int cp_kernel_timing(cp_ctx* ctx, const char* classes);
 int cp_kernel_times(cp_ctx* ctx, const char* kernel_class, float* total_ms, int32_t* launches);
 

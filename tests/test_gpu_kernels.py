@@ -157,6 +157,49 @@ def test_gemm_q8_0_row_tiles(torch, cpa, M, N, K, splits, mode, row_tile):
     assert np.all(err <= bound + 1e-30)
 
 
+# The weight-streaming kernel (row tile 1) of chunks of 1-4 tokens: every row count it
+# templates (1, 2, and 3-4), K with fewer stages than waves and with many, the planned
+# split count, one split, an uneven split and one stage per workgroup (idle waves), in the
+# three epilogues.  Two calls must agree bit for bit (fixed summation order).
+@pytest.mark.parametrize("M,N,K,splits", [(1, 64, 128, 0), (2, 5120, 640, 0), (3, 6144, 5120, 0),
+                                          (4, 5120, 17408, 0), (1, 34816, 5120, 0), (3, 1024, 5120, 1),
+                                          (4, 512, 2048, 3), (2, 256, 1024, 8)])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_gemm_skinny(torch, cpa, M, N, K, splits, mode):
+    log(f"gemm skinny M={M} N={N} K={K} splits={splits} mode={mode}")
+    A = f16_round(synth.normal(synth.tensor_seed("As", M, K), (M, K), scale=1.0))
+    W = synth.normal(synth.tensor_seed("Ws", N, K), (N, K))
+    Wb = oracle.q8_0_encode_bytes(W)
+    Wd = oracle.q8_0_decode_bytes(Wb, K).astype(np.float64)
+    At = torch.from_numpy(A).cuda().to(torch.float16)
+    Wt = torch.from_numpy(Wb).cuda()
+    F = N // 2
+    X0 = synth.normal(synth.tensor_seed("X0s", M, N), (M, N), scale=1.0)
+    outs = []
+    for _ in range(2):
+        if mode == 2:
+            out = torch.zeros((M, F), dtype=torch.float16, device="cuda")
+        else:
+            out = torch.from_numpy(X0.copy() if mode == 1 else np.zeros((M, N), np.float32)).cuda()
+        cpa.cp_test_gemm(At, Wt, M, N, K, mode, splits, out, row_tile=1)
+        outs.append(out.float().cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    got = outs[0].astype(np.float64)
+    if mode == 2:
+        g = A.astype(np.float64) @ Wd[:F].T
+        u = A.astype(np.float64) @ Wd[F:].T
+        ref = g / (1 + np.exp(-g)) * u
+        e = rel_err(got, ref)
+        log(f"  max rel err {e:.3e}")
+        assert e < 1e-2
+        return
+    ref = A.astype(np.float64) @ Wd.T + (X0.astype(np.float64) if mode == 1 else 0.0)
+    bound = gemm_bound(A, Wd, ref, K, mode)
+    err = np.abs(got - ref)
+    log(f"  max rel err {rel_err(got, ref):.3e}, worst err/bound {np.max(err / (bound + 1e-30)):.3f}")
+    assert np.all(err <= bound + 1e-30)
+
+
 @pytest.mark.parametrize("M,F,K,splits,row_tile", [(130, 128, 256, 0, 0), (77, 704, 256, 0, 0),
                                                    (512, 1024, 2048, 2, 0), (512, 17408, 5120, 0, 0),
                                                    (159, 17408, 5120, 0, 0), (300, 1024, 2048, 0, 256),

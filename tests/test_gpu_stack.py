@@ -76,20 +76,22 @@ def test_stack_end_to_end_and_per_layer(torch, base, kv):
 
 
 def test_tiny_dense_workload_chunk_sizes(torch):
-    """The 2-layer d=256 workload: 512 token ids read in chunks of 1, 7, 128 and 512."""
+    """The 2-layer d=256 workload: 512 token ids read in chunks of 1, 3, 7, 128 and 512
+    (1 and 3: every GEMM on the weight-streaming kernel, its counters reused launch after
+    launch)."""
     w = synth.WORKLOADS["tiny_dense"]
     ql = q8_layers(w, gains="ones")
     x = synth.prompt_inputs(w)
     ref = oracle.OracleModel(w, ql).prefill_layer_major(x)
     outs = {}
-    for chunk in (128, 1, 7, 512):
+    for chunk in (128, 1, 3, 7, 512):
         log(f"tiny_dense chunk={chunk}")
         out, ctx = run_prefill(torch, w, ql, x, chunk)
         outs[chunk] = out
         e = rel_err(out, ref)
         log(f"  max rel err {e:.3e}")
         assert e < TOL
-    for c in (1, 7, 512):
+    for c in (1, 3, 7, 512):
         assert rel_err(outs[c], outs[128]) < TOL
 
 
