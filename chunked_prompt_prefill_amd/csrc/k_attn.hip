@@ -279,19 +279,16 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
     }
     return (m == -INFINITY) ? 0.0f : m;
   };
-  // ---- probabilities p = 2^(s*scale - m) (every one below 2^8: safe in fp16), their row
-  // sum, and the fp16 B operands of O^T += V^T P^T (keys 16*ks + 8h .. +7 per lane).
+  // ---- probabilities p = 2^(s*scale - m) (every one below 2^8: safe in fp16), the fp16
+  // B operands of O^T += V^T P^T (keys 16*ks + 8h .. +7 per lane), and the row sum of
+  // those fp16 values (the weights the product applies), two per v_dot2 against (1, 1).
   auto probs = [&](f32x16 (&s)[2], float msafe, uint4 (&pb)[4]) __attribute__((always_inline)) {
-    float ls = 0.0f;
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][e], scale, -msafe));
-        s[jb][e] = p;
-        ls += p;
-      }
-    l += ls;                           // lane half; halves are combined at the end
+      for (int e = 0; e < 16; ++e) s[jb][e] = __builtin_amdgcn_exp2f(fmaf(s[jb][e], scale, -msafe));
+    const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+    float ls = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int jb = ks >> 1, kk = ks & 1;
@@ -299,7 +296,11 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
                           pack_f16x2(s[jb][8 * kk + 2], s[jb][8 * kk + 3]),
                           pack_f16x2(s[jb][8 * kk + 4], s[jb][8 * kk + 5]),
                           pack_f16x2(s[jb][8 * kk + 6], s[jb][8 * kk + 7]));
+      const uint32_t w[4] = {pb[ks].x, pb[ks].y, pb[ks].z, pb[ks].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ls = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[c]), one2, ls, false);
     }
+    l += ls;                           // lane half; halves are combined at the end
   };
   // ---- O^T += V^T P^T (16 MFMAs)
   auto pv = [&](const uint4* vb, const uint4 (&pb)[4]) __attribute__((always_inline)) {
