@@ -87,6 +87,9 @@ __device__ __forceinline__ float warp_max32(float v) {   // max over aligned gro
   return v;
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g), with the hardware reciprocal (1 ulp) in place of an IEEE
+// division: the product is rounded to fp16 afterwards.  e^-g overflows to +inf for
+// g < about -88, and then the reciprocal gives 0 and silu gives -0.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 }  // namespace cp
