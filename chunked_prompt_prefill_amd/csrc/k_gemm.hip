@@ -208,36 +208,43 @@ __global__ __launch_bounds__(256, MinBlocks<MI>::v) void gemm_q8_kernel(GemmArgs
   }
 
   // Epilogue.  acc[mi][ni][e]: row mi*32 + 8*(e/4) + 4*h + e%4, column n_wave + 32*ni + l32.
+  // A lane's rows are 4h plus constants, so each store address is a per-lane base plus a
+  // constant times the (uniform) row stride; whole tiles skip the row check.
   const int pn = g.N - g.n0;
+  const bool full = rows >= MT;
+  auto each = [&](auto&& st) __attribute__((always_inline)) {
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int r = mi * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-      if (r >= rows) continue;
-      const int64_t row = m0 + r;
-      if constexpr (MODE == GM_SWIGLU) {
-        if (!col_ok0) continue;
-        const int f = (n_wave >> 1) + l32;
-        const float gte = acc[mi][0][e], up = acc[mi][1][e];
-        reinterpret_cast<_Float16*>(g.out)[row * g.ldo + f] = f16_sat(silu(gte) * up);
-      } else {
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          if (!(ni ? col_ok1 : col_ok0)) continue;
-          const int64_t col = n_wave + 32 * ni + l32;
-          const float v = acc[mi][ni][e];
-          if constexpr (MODE == GM_F32) {
-            reinterpret_cast<float*>(g.out)[row * g.ldo + col] = v;
-          } else if constexpr (MODE == GM_F32_ADD) {
-            float* p = reinterpret_cast<float*>(g.out) + row * g.ldo + col;
-            *p = *p + v;
-          } else {
-            g.partial[((int64_t)split * g.M + row) * pn + (col - g.n0)] = v;
-          }
-        }
+      for (int e = 0; e < 16; ++e) {
+        const int rc = mi * 32 + 8 * (e >> 2) + (e & 3);   // row minus 4h
+        if (full || rc + 4 * h < rows) st(mi, e, rc);
       }
+  };
+  if constexpr (MODE == GM_SWIGLU) {
+    if (col_ok0) {
+      _Float16* ob = reinterpret_cast<_Float16*>(g.out) + ((int64_t)m0 + 4 * h) * g.ldo + (n_wave >> 1) + l32;
+      each([&](int mi, int e, int rc) {
+        ob[(int64_t)rc * g.ldo] = f16_sat(silu(acc[mi][0][e]) * acc[mi][1][e]);
+      });
     }
+  } else if constexpr (MODE == GM_PARTIAL) {
+    float* pb = g.partial + ((int64_t)split * g.M + m0 + 4 * h) * pn + (n_wave - g.n0) + l32;
+    each([&](int mi, int e, int rc) {
+      if (col_ok0) pb[(int64_t)rc * pn] = acc[mi][0][e];
+      if (col_ok1) pb[(int64_t)rc * pn + 32] = acc[mi][1][e];
+    });
+  } else {
+    float* ob = reinterpret_cast<float*>(g.out) + ((int64_t)m0 + 4 * h) * g.ldo + n_wave + l32;
+    each([&](int mi, int e, int rc) {
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        if (!(ni ? col_ok1 : col_ok0)) continue;
+        float* p = ob + (int64_t)rc * g.ldo + 32 * ni;
+        if constexpr (MODE == GM_F32) *p = acc[mi][ni][e];
+        else *p = *p + acc[mi][ni][e];
+      }
+    });
   }
 }
 
