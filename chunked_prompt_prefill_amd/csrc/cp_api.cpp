@@ -389,6 +389,7 @@ struct cp_ctx {
   WLayout WL;
   WsLayout WS;
   hipStream_t stream = nullptr;
+  PendingSum pend_x;            // split-K sums into the chunk's x not yet added
   uint8_t* warena = nullptr;
   uint8_t* kv = nullptr;
   uint8_t* ws = nullptr;
@@ -447,11 +448,20 @@ hipError_t timed(cp_ctx* c, const char* cls, F&& launch) {
   return e;
 }
 
+// defer (optional): a split launch covering the last column range leaves its partial
+// sums pending and describes them there (PendingSum) for the kernel that reads the
+// result, instead of running the reduction pass; *defer is cleared otherwise.  Only for
+// chunks of kDeferMinRows rows or more: the reading kernel (RMSNorm, one workgroup per
+// row) then has rows enough to spread the partial reads over the chip.
+constexpr int kDeferMinRows = 64;
 hipError_t gemm(cp_ctx* c, const char* cls, const _Float16* A, int lda, int M, const QMat& W,
-                int mode, void* out, int ldo) {
+                int mode, void* out, int ldo, PendingSum* defer = nullptr) {
   const GemmPlan p = plan_gemm(M, W.N, W.K);
+  if (defer) *defer = PendingSum();
   return timed(c, cls, [&] {
     for (int i = 0; i < p.nparts; ++i) {
+      const bool leave = defer && p.part[i].splits > 1 && i == p.nparts - 1 && mode != GM_SWIGLU &&
+                         M >= kDeferMinRows;
       GemmArgs g;
       g.A = A; g.lda = lda; g.M = M; g.N = p.part[i].n1; g.K = W.K; g.n0 = p.part[i].n0;
       g.wq = W.q; g.wd = W.d; g.mode = mode; g.out = out; g.ldo = ldo;
@@ -461,14 +471,22 @@ hipError_t gemm(cp_ctx* c, const char* cls, const _Float16* A, int lda, int M, c
       // (one kernel), "<class>/split" for a split-K range (partial GEMM + ordered reduce),
       // "<class>/skinny" for the weight-streaming kernel of a few rows
       const std::string sub = std::string(cls) + (p.mt == 1 ? "/skinny" : g.splits > 1 ? "/split" : "/full");
-      const hipError_t e = timed(c, sub.c_str(), [&] { return launch_gemm(g, 0, p.mt, c->stream); });
+      const hipError_t e = timed(c, sub.c_str(), [&] { return launch_gemm(g, 0, p.mt, c->stream, !leave); });
       if (e != hipSuccess) return e;
+      if (leave) {
+        defer->partial = g.partial;
+        defer->splits = g.splits; defer->M = M; defer->n0 = g.n0; defer->N = g.N;
+        defer->add = mode == GM_F32_ADD;
+      }
     }
     return hipSuccess;
   });
 }
 
-int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int start) {
+// One layer of one chunk.  The split-K sums of the output projection are taken by the FFN
+// RMSNorm, and those of the down projection by the next layer's first RMSNorm
+// (c->pend_x), or, with flush_end, by a reduction pass at the end of the layer.
+int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int start, bool flush_end) {
   const Dims& D = c->D;
   const LayerW& L = c->layers[li];
   hipStream_t s = c->stream;
@@ -479,7 +497,14 @@ int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int sta
   const float* cos_t = c->wsp<float>(c->WS.cos);
   const float* sin_t = c->wsp<float>(c->WS.sin);
 
-  CP_HIP(c, timed(c, "rmsnorm", [&] { return launch_rmsnorm(x_res_in, L.attn_norm, n, D.d, c->cfg.rms_eps, xn, nullptr, s); }), "rmsnorm");
+  // pending sums into x exist only from the previous layer, which wrote x itself
+  const PendingSum px = c->pend_x;
+  c->pend_x = PendingSum();
+  if (px.partial && x_res_in != x) return fail(c, CP_E_DEVICE, "pending sums on the chunk input");
+  // (x_res_in is written only when sums are pending, and then it is x)
+  CP_HIP(c, timed(c, "rmsnorm", [&] { return launch_rmsnorm(const_cast<float*>(x_res_in), L.attn_norm, n, D.d, c->cfg.rms_eps, xn, nullptr, s, px); }), "rmsnorm");
+  // (the QKV sums are reduced in their own pass: RoPE reads each q/k value twice, as a
+  // value and as its rotation partner, so it would read the partials twice)
   CP_HIP(c, gemm(c, "gemm_qkv", xn, D.d, n, L.qkv, GM_F32, qkv, D.Nqkv), "gemm_qkv");
   CP_HIP(c, timed(c, "rope_kv_append", [&] {
     hipError_t e = launch_rope_qk(qkv, cos_t, sin_t, n, start, D.Hq, D.Hkv, D.hd, D.kv_type, D.n_ctx, q, L.kv, s);
@@ -499,17 +524,25 @@ int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int sta
   CP_HIP(c, timed(c, "attention", [&] { return launch_attention(aa, s); }), "attention");
   if (x != x_res_in)
     CP_HIP(c, hipMemcpyAsync(x, x_res_in, (size_t)n * D.d * 4, hipMemcpyDeviceToDevice, s), "residual copy");
-  CP_HIP(c, gemm(c, "gemm_o", attn, D.Dq, n, L.o, GM_F32_ADD, x, D.d), "gemm_o");
+  PendingSum po;
+  CP_HIP(c, gemm(c, "gemm_o", attn, D.Dq, n, L.o, GM_F32_ADD, x, D.d, &po), "gemm_o");
 
   if (!D.moe) {
-    CP_HIP(c, timed(c, "rmsnorm", [&] { return launch_rmsnorm(x, L.ffn_norm, n, D.d, c->cfg.rms_eps, xn, nullptr, s); }), "rmsnorm");
+    CP_HIP(c, timed(c, "rmsnorm", [&] { return launch_rmsnorm(x, L.ffn_norm, n, D.d, c->cfg.rms_eps, xn, nullptr, s, po); }), "rmsnorm");
     _Float16* hbuf = c->wsp<_Float16>(c->WS.h);
     CP_HIP(c, gemm(c, "gemm_gate_up", xn, D.d, n, L.gu, GM_SWIGLU, hbuf, D.Fp), "gemm_gate_up");
-    CP_HIP(c, gemm(c, "gemm_down", hbuf, D.Fp, n, L.dn, GM_F32_ADD, x, D.d), "gemm_down");
+    CP_HIP(c, gemm(c, "gemm_down", hbuf, D.Fp, n, L.dn, GM_F32_ADD, x, D.d, &c->pend_x), "gemm_down");
+    if (flush_end && c->pend_x.partial) {
+      const PendingSum& pd = c->pend_x;
+      CP_HIP(c, timed(c, "gemm_down", [&] {
+        return launch_splitk_reduce(pd.partial, pd.splits, pd.M, pd.n0, pd.N, GM_F32_ADD, x, D.d, s);
+      }), "gemm_down reduce");
+      c->pend_x = PendingSum();
+    }
     return CP_OK;
   }
   float* xn32 = c->wsp<float>(c->WS.xn32);
-  CP_HIP(c, timed(c, "rmsnorm", [&] { return launch_rmsnorm(x, L.ffn_norm, n, D.d, c->cfg.rms_eps, xn, xn32, s); }), "rmsnorm");
+  CP_HIP(c, timed(c, "rmsnorm", [&] { return launch_rmsnorm(x, L.ffn_norm, n, D.d, c->cfg.rms_eps, xn, xn32, s, po); }), "rmsnorm");
   MoeBuffers mb;
   mb.logits = c->wsp<float>(c->WS.logits); mb.idx = c->wsp<int32_t>(c->WS.idx);
   mb.w = c->wsp<float>(c->WS.w); mb.rank = c->wsp<int32_t>(c->WS.rank);
@@ -687,8 +720,9 @@ int prefill_chunk(cp_ctx* c, const float* x_in, float* x_out, int32_t n) {
   if (n < 1 || n > c->cfg.n_chunk_max) return fail(c, CP_E_CAPACITY, "n_tokens outside [1, n_chunk_max]");
   if ((int64_t)c->n_past + n > c->cfg.n_ctx_max) return fail(c, CP_E_CAPACITY, "n_past + n_tokens > n_ctx_max");
   const int start = c->n_past;
+  c->pend_x = PendingSum();
   for (int l = 0; l < c->D.L; ++l) {
-    const int r = run_layer(c, l, l == 0 ? x_in : x_out, x_out, n, start);
+    const int r = run_layer(c, l, l == 0 ? x_in : x_out, x_out, n, start, l == c->D.L - 1);
     if (r != CP_OK) return r;
   }
   c->n_past = start + n;
@@ -705,8 +739,9 @@ int prefill_chunk_trace(cp_ctx* c, const float* x_in, float* x_out, int32_t n, f
   if (route_idx && (!c->D.moe || route_stride < (int64_t)n * c->D.k))
     return fail(c, CP_E_INVALID, "route_idx needs routed experts and route_stride >= n * n_expert_used");
   const int start = c->n_past;
+  c->pend_x = PendingSum();
   for (int l = 0; l < c->D.L; ++l) {
-    const int r = run_layer(c, l, l == 0 ? x_in : x_out, x_out, n, start);
+    const int r = run_layer(c, l, l == 0 ? x_in : x_out, x_out, n, start, true);
     if (r != CP_OK) return r;
     if (layer_out)
       CP_HIP(c, hipMemcpyAsync(layer_out + layer_stride * l, x_out, (size_t)n * c->D.d * 4,
@@ -731,8 +766,9 @@ int prefill_chunk_timed(cp_ctx* c, const float* x_in, float* x_out, int32_t n, f
   const int start = c->n_past;
   int rc = CP_OK;
   if (hipEventRecord(ev[0], c->stream) != hipSuccess) rc = fail(c, CP_E_DEVICE, "event record");
+  c->pend_x = PendingSum();
   for (int l = 0; l < L && rc == CP_OK; ++l) {
-    rc = run_layer(c, l, l == 0 ? x_in : x_out, x_out, n, start);
+    rc = run_layer(c, l, l == 0 ? x_in : x_out, x_out, n, start, l == L - 1);
     if (rc == CP_OK && hipEventRecord(ev[l + 1], c->stream) != hipSuccess) rc = fail(c, CP_E_DEVICE, "event record");
   }
   if (rc == CP_OK) {

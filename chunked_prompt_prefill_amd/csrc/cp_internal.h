@@ -56,8 +56,20 @@ struct GemmArgs {
 // Rows up to which the weight-streaming kernel (k_gemv.hip) takes a GEMM.
 constexpr int kSkinnyMaxRows = 4;
 
-// Kernel launchers (return hipError_t of the launch).
-hipError_t launch_gemm(const GemmArgs& a, int grid_m_tiles, int mt, hipStream_t s);
+// A split-K GEMM result whose partial sums have not been added yet.  Column c >= n0 of
+// row m of the result is partial[0][m][c-n0] + ... + partial[splits-1][m][c-n0] (added in
+// split order), then, when add is set, base[m][c] + that sum; columns below n0 are final
+// in the base matrix.  A consumer kernel that reads the result through this description
+// replaces the separate reduction pass (same arithmetic, same order).
+struct PendingSum {
+  const float* partial = nullptr;   // nullptr: nothing pending
+  int32_t splits = 0, M = 0, n0 = 0, N = 0;
+  bool add = false;
+};
+
+// Kernel launchers (return hipError_t of the launch).  With reduce = false a split launch
+// leaves its partial sums for the caller (who describes them with a PendingSum).
+hipError_t launch_gemm(const GemmArgs& a, int grid_m_tiles, int mt, hipStream_t s, bool reduce = true);
 // 256-row tiles, one workgroup per CU (non-grouped only); the partial-sum reduction of a
 // split launch is left to the caller.
 hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t s);
@@ -77,8 +89,11 @@ hipError_t launch_repack_q8_0(const void* src0, const void* src1, int64_t src_ro
                               hipStream_t s);
 hipError_t launch_quantize_q8_0(const float* x, int64_t rows, int32_t k, int64_t ldx,
                                 void* out, hipStream_t s);
-hipError_t launch_rmsnorm(const float* x, const float* gamma, int32_t n, int32_t d, float eps,
-                          _Float16* y, float* y32, hipStream_t s);
+// y = RMSNorm(x) * gamma (fp16; y32: the same in float32, or nullptr).  With ps pending,
+// x first takes its pending sums (see PendingSum; x is the base matrix) and the result is
+// written back to x.
+hipError_t launch_rmsnorm(float* x, const float* gamma, int32_t n, int32_t d, float eps,
+                          _Float16* y, float* y32, hipStream_t s, const PendingSum& ps = PendingSum());
 
 struct KvLayer {          // one layer's cache (device pointers), capacity n_ctx
   void* k = nullptr;      // f16 [Hkv][n_ctx][hd]  | int8 [Hkv][n_ctx][hd]

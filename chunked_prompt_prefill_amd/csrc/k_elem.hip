@@ -108,16 +108,35 @@ hipError_t launch_quantize_q8_0(const float* x, int64_t rows, int32_t k, int64_t
 // ======================================================================================
 // RMSNorm: y = x / sqrt(mean(x^2) + eps) * gamma  -> fp16 (and optionally float32)
 // ======================================================================================
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
-                                                      const float* __restrict__ gamma, int32_t d,
-                                                      float eps, _Float16* __restrict__ y,
-                                                      float* __restrict__ y32) {
+// Four consecutive elements (col % 4 == 0; n0 % 4 == 0) of row `row` of a matrix [rows][ld]
+// whose split-K sums may still be pending (PendingSum).
+__device__ __forceinline__ float4 pend_load4(const float* base, int64_t ld, const PendingSum& ps,
+                                             int64_t row, int col) {
+  const float4 b = *reinterpret_cast<const float4*>(base + row * ld + col);
+  if (!ps.partial || col < ps.n0) return b;
+  const int64_t pn = ps.N - ps.n0, plane = (int64_t)ps.M * pn;
+  const float* p = ps.partial + row * pn + (col - ps.n0);
+  float4 acc = *reinterpret_cast<const float4*>(p);
+  for (int sp = 1; sp < ps.splits; ++sp) {
+    const float4 a = *reinterpret_cast<const float4*>(p + sp * plane);
+    acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
+  }
+  if (ps.add) { acc.x = b.x + acc.x; acc.y = b.y + acc.y; acc.z = b.z + acc.z; acc.w = b.w + acc.w; }
+  return acc;
+}
+// One row per workgroup.  Pass 1 takes the pending sums into x (written back) and forms
+// the sum of squares; pass 2 re-reads the row (this thread's own writes) and scales it.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(float* x, const float* __restrict__ gamma,
+                                                      int32_t d, float eps, _Float16* __restrict__ y,
+                                                      float* __restrict__ y32, PendingSum ps) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
-  const float* xr = x + row * d;
+  float* xr = x + row * d;
+  const bool pend = ps.partial != nullptr;
   float ss = 0.0f;
   for (int i = threadIdx.x * 4; i < d; i += 1024) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + i);
+    const float4 v = pend ? pend_load4(x, d, ps, row, i) : *reinterpret_cast<const float4*>(xr + i);
+    if (pend && i >= ps.n0) *reinterpret_cast<float4*>(xr + i) = v;
     ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
 #pragma unroll
@@ -137,10 +156,10 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_rmsnorm(const float* x, const float* gamma, int32_t n, int32_t d, float eps,
-                          _Float16* y, float* y32, hipStream_t s) {
+hipError_t launch_rmsnorm(float* x, const float* gamma, int32_t n, int32_t d, float eps,
+                          _Float16* y, float* y32, hipStream_t s, const PendingSum& ps) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(n), dim3(256), 0, s, x, gamma, d, eps, y, y32);
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(n), dim3(256), 0, s, x, gamma, d, eps, y, y32, ps);
   return hipGetLastError();
 }
 
@@ -193,10 +212,10 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(const float* __restrict__ 
   const int64_t p = start + t;
   const int half = hd / 2;
   const int64_t Nqkv = (int64_t)(Hq + 2 * Hkv) * hd;
-  const float* row = qkv + t * Nqkv;
   const int head = e0 / hd, i0 = e0 % hd;
   const bool lo = i0 < half;
   const int ic0 = lo ? i0 : i0 - half;
+  const float* row = qkv + t * Nqkv;
   const float4 x = *reinterpret_cast<const float4*>(row + e0);
   const float4 y = *reinterpret_cast<const float4*>(row + head * hd + (lo ? i0 + half : i0 - half));
   const float4 c = *reinterpret_cast<const float4*>(cos_t + p * half + ic0);

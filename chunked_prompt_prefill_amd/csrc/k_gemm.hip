@@ -311,7 +311,7 @@ static hipError_t launch_mode(const GemmArgs& a, int grid_m_tiles, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs& a, int grid_m_tiles, int mt, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& a, int grid_m_tiles, int mt, hipStream_t s, bool reduce) {
   if (a.M <= 0 || a.N <= a.n0) return hipSuccess;
   const bool grouped = a.tiles != nullptr;
   hipError_t e;
@@ -320,7 +320,7 @@ hipError_t launch_gemm(const GemmArgs& a, int grid_m_tiles, int mt, hipStream_t 
   else if (mt == 64) e = launch_mode<2, false>(a, 0, s);
   else if (mt == 128) e = launch_mode<4, false>(a, 0, s);
   else e = launch_gemm_big(a, s);
-  if (e != hipSuccess || a.splits <= 1) return e;
+  if (e != hipSuccess || a.splits <= 1 || !reduce) return e;
   return launch_splitk_reduce(a.partial, a.splits, a.M, a.n0, a.N, a.mode, a.out, a.ldo, s);
 }
 

@@ -95,6 +95,33 @@ def test_tiny_dense_workload_chunk_sizes(torch):
         assert rel_err(outs[c], outs[128]) < TOL
 
 
+def test_deferred_split_sums_bitwise_equal_reduction_pass(torch):
+    """Chunks of 64+ rows leave the split-K sums of the output and down projections to the
+    RMSNorm that reads them (the down sums cross into the next layer).  The traced entry
+    point adds each layer's down sums in the reduction pass instead; the arithmetic and
+    its order are the same, so outputs and cache state must agree bit for bit."""
+    import chunked_prompt_prefill_amd as cpa
+    w = synth.WORKLOADS["tiny_dense"]
+    ql = q8_layers(w)
+    x = torch.from_numpy(synth.prompt_inputs(w)).cuda()
+    n = x.shape[0]
+    dev = [cpa.to_device(l) for l in ql]
+    for chunk in (128, 512):
+        log(f"deferred sums tiny_dense chunk={chunk} plan(O)={cpa.cp_test_gemm_plan(chunk, w.d_model, w.n_head * w.head_dim)}")
+        a = cpa.PrefillContext(cpa.make_config(w, n, chunk), dev)
+        b = cpa.PrefillContext(cpa.make_config(w, n, chunk), dev)
+        ya, yb = torch.empty_like(x), torch.empty_like(x)
+        lo = torch.empty((w.n_layer, chunk, w.d_model), dtype=torch.float32, device="cuda")
+        for s0 in range(0, n, chunk):
+            e0 = min(n, s0 + chunk)
+            a.prefill_chunk(x[s0:e0], ya[s0:e0])
+            b.prefill_chunk_trace(x[s0:e0], yb[s0:e0], lo[:, :e0 - s0], chunk * w.d_model)
+        torch.cuda.synchronize()
+        assert torch.equal(ya, yb)
+        assert torch.equal(lo[-1, :n - (n - 1) // chunk * chunk], yb[(n - 1) // chunk * chunk:])
+        assert a.kv_cache_get_state() == b.kv_cache_get_state()
+
+
 def test_state_round_trip_restore_and_continuation(torch):
     import chunked_prompt_prefill_amd as cpa
     for kv in ("f16", "q8_0"):
