@@ -550,7 +550,9 @@ int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int sta
   mb.perm = c->wsp<int32_t>(c->WS.perm); mb.inv = c->wsp<int32_t>(c->WS.inv);
   mb.tiles = c->wsp<int32_t>(c->WS.tiles); mb.n_tiles = c->wsp<int32_t>(c->WS.ntiles);
   CP_HIP(c, timed(c, "moe_route", [&] { return launch_router(xn32, L.rq, L.rd, n, D.d, D.E, D.k, mb.logits, mb.idx, mb.w, s); }), "moe_route");
-  const int mt = 128;
+  // expert row tiles of 256 (the one-workgroup-per-CU kernel) once the experts average
+  // 128 token-slots or more, else 128
+  const int mt = (int64_t)n * D.k >= 128LL * D.E ? 256 : 128;
   const int max_tiles = (int)(ceil_div((int64_t)n * D.k, mt) + D.E);
   CP_HIP(c, timed(c, "moe_permute", [&] { return launch_moe_permute(mb, n, D.E, D.k, mt, max_tiles, s); }), "moe_permute");
   _Float16* hperm = c->wsp<_Float16>(c->WS.h);

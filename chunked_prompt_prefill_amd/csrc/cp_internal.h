@@ -70,9 +70,9 @@ struct PendingSum {
 // Kernel launchers (return hipError_t of the launch).  With reduce = false a split launch
 // leaves its partial sums for the caller (who describes them with a PendingSum).
 hipError_t launch_gemm(const GemmArgs& a, int grid_m_tiles, int mt, hipStream_t s, bool reduce = true);
-// 256-row tiles, one workgroup per CU (non-grouped only); the partial-sum reduction of a
-// split launch is left to the caller.
-hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t s);
+// 256-row tiles, one workgroup per CU; the partial-sum reduction of a split launch is left
+// to the caller.  Grouped (a.tiles set): grid_m_tiles is the tile table's capacity.
+hipError_t launch_gemm_big(const GemmArgs& a, int grid_m_tiles, hipStream_t s);
 // M <= kSkinnyMaxRows, N % 64 == 0, whole column range; splits = K splits.  With one
 // split it applies the epilogue itself; with more it writes partial [S][M][N] and the
 // caller runs the split-K reduction (launch_gemm does).

@@ -315,11 +315,14 @@ hipError_t launch_gemm(const GemmArgs& a, int grid_m_tiles, int mt, hipStream_t 
   if (a.M <= 0 || a.N <= a.n0) return hipSuccess;
   const bool grouped = a.tiles != nullptr;
   hipError_t e;
-  if (grouped) return mt == 64 ? launch_mode<2, true>(a, grid_m_tiles, s) : launch_mode<4, true>(a, grid_m_tiles, s);
+  if (grouped) {
+    if (mt == 256) return launch_gemm_big(a, grid_m_tiles, s);
+    return mt == 64 ? launch_mode<2, true>(a, grid_m_tiles, s) : launch_mode<4, true>(a, grid_m_tiles, s);
+  }
   if (mt == 1) e = launch_gemm_skinny(a, s);
   else if (mt == 64) e = launch_mode<2, false>(a, 0, s);
   else if (mt == 128) e = launch_mode<4, false>(a, 0, s);
-  else e = launch_gemm_big(a, s);
+  else e = launch_gemm_big(a, 0, s);
   if (e != hipSuccess || a.splits <= 1 || !reduce) return e;
   return launch_splitk_reduce(a.partial, a.splits, a.M, a.n0, a.N, a.mode, a.out, a.ldo, s);
 }

@@ -80,7 +80,7 @@ __device__ __forceinline__ void sfor(F&& f) {
   sfor_impl(f, std::make_integer_sequence<int, N>());
 }
 
-template <int MODE>
+template <int MODE, bool GROUPED>
 __global__ __launch_bounds__(256, 1) void gemm_q8_big_kernel(GemmArgs g) {
   __shared__ uint4 sA0[BNCH], sA1[BNCH], sA2[BNCH], sA3[BNCH];
 
@@ -90,30 +90,50 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_big_kernel(GemmArgs g) {
   const int h = lane >> 5, l32 = lane & 31;
   const int KS = g.K / BK;
 
-  // Tile order.  Workgroup i runs on XCD i % 8 and each XCD gets a contiguous range of
-  // logical tiles, so the ~32 workgroups an XCD runs at once are consecutive logical
-  // tiles.  Those are laid out in groups of up to 8 row tiles: 32 consecutive tiles form an
-  // 8 x 4 block (rows x columns) that shares 8 A row panels and 4 weight column panels
-  // in the XCD's L2, instead of 32 A panels for one weight panel.
-  const int mtiles = (int)ceil_div(g.M, BMT);
+  int m0, rows, split, ntile, expert = 0;
   const int ntiles = (int)ceil_div(g.N - g.n0, BNT);
-  const int per_split = mtiles * ntiles;
-  const int total = per_split * g.splits;
-  const int i = blockIdx.x;
-  const int xcd = i & 7, idx = i >> 3;
-  const int q8 = total >> 3, r8 = total & 7;
-  const int logical = (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
-  const int split = logical / per_split;
-  const int lt = logical % per_split;
-  constexpr int GM = 8;
-  const int group = lt / (GM * ntiles);
-  const int first_m = group * GM;
-  const int gm = min(GM, mtiles - first_m);
-  const int within = lt - group * GM * ntiles;
-  const int mt = first_m + within % gm;
-  const int ntile = within / gm;
-  const int m0 = mt * BMT;
-  const int rows = min(BMT, g.M - m0);
+  if constexpr (GROUPED) {
+    // Routed experts: row tiles come from the device tile table {expert, m0, m1}, whose
+    // length is known only on the device; the grid covers the table's capacity.  The
+    // valid (tile, column tile) pairs, column tile fastest, are dealt to the eight XCDs in
+    // contiguous ranges (so a row tile's A rows stay in one L2), and the rest exit.
+    const int valid = *g.n_tiles * ntiles;
+    const int per_xcd = (valid + 7) >> 3;
+    const int i = blockIdx.x;
+    const int xcd = i & 7, idx = i >> 3;
+    const int logical = xcd * per_xcd + idx;
+    if (idx >= per_xcd || logical >= valid) return;
+    const int4 tile = reinterpret_cast<const int4*>(g.tiles)[logical / ntiles];
+    expert = tile.x;
+    m0 = tile.y;
+    rows = tile.z - tile.y;
+    ntile = logical % ntiles;
+    split = 0;
+  } else {
+    // Tile order.  Workgroup i runs on XCD i % 8 and each XCD gets a contiguous range of
+    // logical tiles, so the ~32 workgroups an XCD runs at once are consecutive logical
+    // tiles.  Those are laid out in groups of up to 8 row tiles: 32 consecutive tiles form
+    // an 8 x 4 block (rows x columns) that shares 8 A row panels and 4 weight column
+    // panels in the XCD's L2, instead of 32 A panels for one weight panel.
+    const int mtiles = (int)ceil_div(g.M, BMT);
+    const int per_split = mtiles * ntiles;
+    const int total = per_split * g.splits;
+    const int i = blockIdx.x;
+    const int xcd = i & 7, idx = i >> 3;
+    const int q8 = total >> 3, r8 = total & 7;
+    const int logical = (xcd < r8) ? xcd * (q8 + 1) + idx : r8 * (q8 + 1) + (xcd - r8) * q8 + idx;
+    split = logical / per_split;
+    const int lt = logical % per_split;
+    constexpr int GM = 8;
+    const int group = lt / (GM * ntiles);
+    const int first_m = group * GM;
+    const int gm = min(GM, mtiles - first_m);
+    const int within = lt - group * GM * ntiles;
+    const int mt = first_m + within % gm;
+    ntile = within / gm;
+    m0 = mt * BMT;
+    rows = min(BMT, g.M - m0);
+  }
 
   const int ks0 = (int)((int64_t)split * KS / g.splits);
   const int ks1 = (int)((int64_t)(split + 1) * KS / g.splits);
@@ -136,7 +156,11 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_big_kernel(GemmArgs g) {
       (void*)g.A, (short)0, (int)min((int64_t)g.M * g.lda * 2, (int64_t)0x7FFFFFFF), 0x00020000);
   int32_t aoff[BJPW];   // byte offset of each lane's 16-byte chunk at K stage 0
 #pragma unroll
-  for (int j = 0; j < BJPW; ++j) aoff[j] = ((m0 + min(32 * j + rsub, rows - 1)) * g.lda + lchunk * 8) * 2;
+  for (int j = 0; j < BJPW; ++j) {
+    int32_t pr = m0 + min(32 * j + rsub, rows - 1);
+    if (GROUPED && g.a_rows) pr = g.a_rows[pr] / g.a_row_div;   // gathered A rows
+    aoff[j] = (pr * g.lda + lchunk * 8) * 2;
+  }
 
   const int KB = g.K / QK, KQ = g.K / 128;
   const int last32 = g.N / 32 - 1;
@@ -145,9 +169,9 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_big_kernel(GemmArgs g) {
 #pragma unroll
   for (int ni = 0; ni < 2; ++ni) {
     const int64_t n32 = min((n_wave >> 5) + ni, last32);
-    bsrc[ni] = reinterpret_cast<const uint4*>(g.wq) + n32 * KB * 64 + lane;
+    bsrc[ni] = reinterpret_cast<const uint4*>(g.wq + expert * g.wq_estride) + n32 * KB * 64 + lane;
     // scales: four fp16 per row per 128 columns; a stage takes one 32-bit pair
-    ssrc[ni] = reinterpret_cast<const uint32_t*>(g.wd) + (n32 * KQ * 32 + l32) * 2;
+    ssrc[ni] = reinterpret_cast<const uint32_t*>(g.wd + expert * g.wd_estride) + (n32 * KQ * 32 + l32) * 2;
   }
 
   auto bufA = [&](auto J) __attribute__((always_inline)) -> uint4* {
@@ -365,15 +389,26 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_big_kernel(GemmArgs g) {
 
 }  // namespace
 
-hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm_big(const GemmArgs& a, int grid_m_tiles, hipStream_t s) {
   if (a.M <= 0 || a.N <= a.n0) return hipSuccess;
+  if (a.tiles) {
+    // grouped: one workgroup per (tile table capacity x column tile), unsplit, rounded up
+    // to a multiple of 8 so that every XCD's range of the valid pairs is covered
+    const unsigned grid = (unsigned)(ceil_div((int64_t)grid_m_tiles * ceil_div(a.N - a.n0, BNT), 8) * 8);
+    switch (a.mode) {
+      case GM_F32: hipLaunchKernelGGL((gemm_q8_big_kernel<GM_F32, true>), dim3(grid), dim3(256), 0, s, a); break;
+      case GM_F32_ADD: hipLaunchKernelGGL((gemm_q8_big_kernel<GM_F32_ADD, true>), dim3(grid), dim3(256), 0, s, a); break;
+      default: hipLaunchKernelGGL((gemm_q8_big_kernel<GM_SWIGLU, true>), dim3(grid), dim3(256), 0, s, a); break;
+    }
+    return hipGetLastError();
+  }
   const unsigned grid = (unsigned)(ceil_div(a.M, BMT) * ceil_div(a.N - a.n0, BNT) * a.splits);
   const int mode = a.splits > 1 ? GM_PARTIAL : a.mode;
   switch (mode) {
-    case GM_F32: hipLaunchKernelGGL(gemm_q8_big_kernel<GM_F32>, dim3(grid), dim3(256), 0, s, a); break;
-    case GM_F32_ADD: hipLaunchKernelGGL(gemm_q8_big_kernel<GM_F32_ADD>, dim3(grid), dim3(256), 0, s, a); break;
-    case GM_SWIGLU: hipLaunchKernelGGL(gemm_q8_big_kernel<GM_SWIGLU>, dim3(grid), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(gemm_q8_big_kernel<GM_PARTIAL>, dim3(grid), dim3(256), 0, s, a); break;
+    case GM_F32: hipLaunchKernelGGL((gemm_q8_big_kernel<GM_F32, false>), dim3(grid), dim3(256), 0, s, a); break;
+    case GM_F32_ADD: hipLaunchKernelGGL((gemm_q8_big_kernel<GM_F32_ADD, false>), dim3(grid), dim3(256), 0, s, a); break;
+    case GM_SWIGLU: hipLaunchKernelGGL((gemm_q8_big_kernel<GM_SWIGLU, false>), dim3(grid), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((gemm_q8_big_kernel<GM_PARTIAL, false>), dim3(grid), dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
 }

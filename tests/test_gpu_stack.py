@@ -75,6 +75,26 @@ def test_stack_end_to_end_and_per_layer(torch, base, kv):
     assert e < TOL
 
 
+# Few experts and long chunks: 4 experts, top-2, chunks of 700 tokens (1400 token-slots,
+# about 350 per expert), so the expert GEMMs run in 256-row tiles, several per expert,
+# with a ragged last tile.
+GPU_MOE_WIDE = synth.Workload("gpu_moe_wide", 2, 128, 4, 2, 64, 0, n_expert=4, n_expert_used=2,
+                              expert_ffn_dim=96, kv_type="f16", n_prompt=1000, chunk=700)
+
+
+def test_stack_routed_experts_in_256_row_tiles(torch):
+    w = GPU_MOE_WIDE
+    log(f"stack {w.name} n={w.n_prompt} chunk={w.chunk}")
+    ql = q8_layers(w)
+    x = synth.prompt_inputs(w)
+    out, ctx, lo, ro = run_prefill(torch, w, ql, x, w.chunk, trace=True)
+    assert np.all(np.isfinite(out))
+    ref = check_layers(w, ql, x, lo, ro)
+    e = rel_err(out, ref)
+    log(f"  end-to-end max rel err {e:.3e}")
+    assert e < TOL
+
+
 def test_tiny_dense_workload_chunk_sizes(torch):
     """The 2-layer d=256 workload: 512 token ids read in chunks of 1, 3, 7, 128 and 512
     (1 and 3: every GEMM on the weight-streaming kernel, its counters reused launch after
