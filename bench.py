@@ -183,7 +183,7 @@ def pmc_digest(fetch_csv, write_csv, copy_mib):
             rows = list(csv.DictReader(f))
         copy = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")]
         k = [float(r["Counter_Value"]) for r in rows
-             if "gemm_q8_big_kernel<2>" in r["Kernel_Name"]
+             if "gemm_q8_big_kernel<2, false>" in r["Kernel_Name"]
              and int(r["Grid_Size"]) // int(r["Workgroup_Size"]) == grid_wg]
         if not copy or len(k) != 1:
             raise SystemExit(f"{path}: expected the copy and one unsplit gate/up launch, got {len(copy)} / {len(k)}")
