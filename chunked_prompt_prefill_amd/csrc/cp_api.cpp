@@ -185,6 +185,12 @@ GemmPlan plan_gemm(int M, int N, int K, int force_splits = 0, int force_mt = 0) 
   if (force_mt > 0) return plan_gemm_mt(M, N, K, force_mt, force_splits);
   if (M <= 64) return plan_gemm_mt(M, N, K, 64, force_splits);
   GemmPlan best = plan_gemm_mt(M, N, K, 128, force_splits);
+  if (M <= 128) {
+    // (measured at 128 rows: two 64-row tiles with more workgroups in flight beat one
+    // 128-row tile on every weight stream but the widest)
+    const GemmPlan small = plan_gemm_mt(M, N, K, 64, force_splits);
+    if (small.cost < best.cost) best = small;
+  }
   if (M > 128) {
     const GemmPlan big = plan_gemm_mt(M, N, K, 256, force_splits);
     if (big.cost < best.cost) best = big;
