@@ -100,3 +100,29 @@ def test_plan_chunk_matches_the_oracle_rule_and_the_page_table(cpa):
                 (100, 8192, 4, 0.0), (100, 8192, 4, float("nan")), (100, 8192, 4, float("inf"))):
         with pytest.raises(Exception):
             cpa.cp_plan_chunk(*bad)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 37, 64, 65, 128, 159, 300, 512, 956, 2048, 3328, 8192])
+@pytest.mark.parametrize("N,K", [(34816, 5120), (5120, 17408), (7168, 5120), (5120, 5120), (5120, 2048),
+                                 (2048, 4096), (1536, 2048), (256, 256), (96, 768)])
+def test_gemm_launch_plans_cover_the_columns(cpa, M, N, K):
+    """Every launch plan the layers use (host only): one or two launches covering [0, N) in
+    order, the first starting at column 0 and the second at a whole 256-column tile; split
+    factors within [1, 16] and the K stages; the weight-streaming kernel (row tile 1) only
+    for 1-4 rows with N a multiple of 64; 256-row tiles only above 128 rows."""
+    mt, parts = cpa.cp_test_gemm_plan(M, N, K)
+    assert 1 <= len(parts) <= 2
+    assert parts[0][0] == 0
+    for i, (n0, splits) in enumerate(parts):
+        assert 1 <= splits <= max(16, K // 128)
+        assert splits <= K // 128
+        if i:
+            assert n0 % 256 == 0 and 0 < n0 < N
+            assert parts[0][1] == 1          # the whole rounds run unsplit
+    if mt == 1:
+        assert M <= 4 and N % 64 == 0 and len(parts) == 1
+    else:
+        assert mt in (64, 128, 256)
+        assert not (M <= 4 and N % 64 == 0)
+        assert mt != 256 or M > 128
+        assert mt != 128 or M > 64
