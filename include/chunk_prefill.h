@@ -280,15 +280,16 @@ int cp_test_router(const float* y, const void* w_router, int32_t n, int32_t d, i
  * buffer of cp_test_gemm_scratch_bytes(M, N, K, splits) bytes (repacked weights and
  * partial sums). */
 size_t cp_test_gemm_scratch_bytes(int32_t M, int32_t N, int32_t K, int32_t splits);
-/* The launch plan the layer uses for an M x N x K GEMM (host only): out6 = {row tile,
- * number of launches, first column of launch 0, its split-K factor, first column of
- * launch 1, its split-K factor}. */
+/* The launch plan the layer uses for an M x N x K GEMM (host only): out6 = {row tile (1 =
+ * the weight-streaming kernel), number of launches, first column of launch 0, its split-K
+ * factor, first column of launch 1, its split-K factor}. */
 int cp_test_gemm_plan(int32_t M, int32_t N, int32_t K, int32_t* out6);
 int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
                  int32_t splits, void* out, void* scratch, void* hip_stream);
 /* Same with the row tile pinned: row_tile 64 or 128 runs the kernel that keeps two
  * workgroups per CU, 256 the one-workgroup-per-CU kernel with the three-stage LDS
- * pipeline; 0 = the layer's own choice.  Scratch: cp_test_gemm_scratch_bytes_ex. */
+ * pipeline, 1 the weight-streaming kernel of 1-4 rows (M <= 4 and N % 64 == 0, else
+ * CP_E_INVALID); 0 = the layer's own choice.  Scratch: cp_test_gemm_scratch_bytes_ex. */
 size_t cp_test_gemm_scratch_bytes_ex(int32_t M, int32_t N, int32_t K, int32_t splits,
                                      int32_t row_tile);
 int cp_test_gemm_ex(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
