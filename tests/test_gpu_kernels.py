@@ -109,10 +109,13 @@ def gemm_bound(A, Wd, ref, K, mode):
             (np.abs(ref) * 2.0 ** -23 if mode == 1 else 0))
 
 
+# The planned launches; the last two shapes plan 256-row tiles with an unsplit column range
+# and a split-K tail (ragged rows; a one-tile tail).
 @pytest.mark.parametrize("M,N,K,splits", [(1, 256, 256, 0), (57, 512, 256, 0), (128, 5120, 512, 0),
                                           (300, 768, 2048, 1), (300, 768, 2048, 3), (513, 1024, 768, 0),
                                           (64, 7168, 5120, 0), (1000, 256, 17408, 0),
-                                          (512, 7168, 5120, 0), (2048, 5120, 5120, 0)])
+                                          (512, 7168, 5120, 0), (2048, 5120, 5120, 0),
+                                          (300, 34816, 1024, 0), (512, 33024, 1280, 0)])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_gemm_q8_0_within_f16_bound(torch, cpa, M, N, K, splits, mode):
     log(f"gemm M={M} N={N} K={K} splits={splits} mode={mode} plan={cpa.cp_test_gemm_plan(M, N, K)}")
@@ -202,7 +205,8 @@ def test_gemm_skinny(torch, cpa, M, N, K, splits, mode):
 
 @pytest.mark.parametrize("M,F,K,splits,row_tile", [(130, 128, 256, 0, 0), (77, 704, 256, 0, 0),
                                                    (512, 1024, 2048, 2, 0), (512, 17408, 5120, 0, 0),
-                                                   (159, 17408, 5120, 0, 0), (300, 1024, 2048, 0, 256),
+                                                   (159, 17408, 5120, 0, 0), (300, 17408, 1024, 0, 0),
+                                                   (300, 1024, 2048, 0, 256),
                                                    (2048, 2048, 1280, 0, 256), (600, 1536, 768, 4, 256)])
 def test_gemm_swiglu(torch, cpa, M, F, K, splits, row_tile):
     log(f"gemm swiglu M={M} F={F} K={K} row_tile={row_tile} plan={cpa.cp_test_gemm_plan(M, 2 * F, K)}")
