@@ -114,19 +114,27 @@ GemmPlan plan_gemm_mt(int M, int N, int K, int mt, int force_splits) {
   // unsplit on 160 of the 256 CUs, 25% slower than three splits)
   auto epi = [&](int64_t cols) { return (double)M * cols * 4 / 5e12; };
   auto rounds = [&](int64_t wgs) { return (double)ceil_div(wgs, slots); };
+  // 128-wide K stages a workgroup runs for S splits.  The 256-row kernel runs 64-wide
+  // stages in groups of four: a split's count is padded to a multiple of four with
+  // zero-weight stages, which take as long as real ones (80 stages in 6 splits run 16
+  // each, as in 5 splits).
+  auto kst = [&](int64_t S) {
+    if (p.mt < 256) return (double)ceil_div(KS, S);
+    return (double)(ceil_div(ceil_div(K / 64, S), 4) * 4) / 2.0;
+  };
   if (force_splits > 0) {
     const int S = (int)std::min<int64_t>(force_splits, KS);
     p.nparts = 1;
     p.part[0] = {0, N, S};
     p.partial_bytes = S > 1 ? (size_t)S * M * N * 4 : 0;
-    p.cost = rounds(T * S) * ceil_div(KS, S) * t_stage;
+    p.cost = rounds(T * S) * kst(S) * t_stage;
     return p;
   }
-  double best = rounds(T) * KS * t_stage + epi(N);
+  double best = rounds(T) * kst(1) * t_stage + epi(N);
   p.nparts = 1;
   p.part[0] = {0, N, 1};
   for (int64_t S = 2; S <= std::min<int64_t>(16, KS); ++S) {
-    const double c = rounds(T * S) * ceil_div(KS, S) * t_stage + red(S, N);
+    const double c = rounds(T * S) * kst(S) * t_stage + red(S, N);
     if (c < best) {
       best = c;
       p.nparts = 1;
@@ -139,8 +147,8 @@ GemmPlan plan_gemm_mt(int M, int N, int K, int mt, int force_splits) {
       const int64_t R = Mt * (Nt - Nf);
       const int64_t cols = N - Nf * 256;
       for (int64_t S = 2; S <= std::min<int64_t>(16, KS); ++S) {
-        const double c = rounds(Mt * Nf) * KS * t_stage + epi(Nf * 256) +
-                         rounds(R * S) * ceil_div(KS, S) * t_stage + red(S, cols);
+        const double c = rounds(Mt * Nf) * kst(1) * t_stage + epi(Nf * 256) +
+                         rounds(R * S) * kst(S) * t_stage + red(S, cols);
         if (c < best) {
           best = c;
           p.nparts = 2;
