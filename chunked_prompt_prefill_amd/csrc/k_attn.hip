@@ -484,13 +484,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   float den = 0.0f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   if (live) {
+    // A split without keys for this row left m = -inf, l = 0 and O = 0: its weight is
+    // exp2(-inf) = 0 and it adds exact zeros, so no branch holds back the loads.
 #pragma unroll 4
     for (int s = sl; s < a.splits; s += SL) {
-      const float ms = a.part_ml[((int64_t)s * rows_total + rg) * 2];
-      if (ms == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(ms - mstar);
-      den += w * a.part_ml[((int64_t)s * rows_total + rg) * 2 + 1];
+      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + ((int64_t)s * rows_total + rg) * 2);
       const float4 po = *reinterpret_cast<const float4*>(a.part_o + ((int64_t)s * rows_total + rg) * hd + d0);
+      const float w = __builtin_amdgcn_exp2f(ml.x - mstar);
+      den += w * ml.y;
       num.x += w * po.x; num.y += w * po.y; num.z += w * po.z; num.w += w * po.w;
     }
   }
