@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 PEAK_F16_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 MFMA (same rate)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 DECODE_ROOM = 128           # cache positions past the prompt for the decode-sized chunks
+LOGITS_VOCAB = 152064       # rows of the synthetic LM head of the last-logits measurement
 
 
 def note(msg: str):
@@ -273,6 +274,33 @@ def run_main(args, torch, cpa, synth):
         decode[f"chunk_{dc}"] = {"tokens_per_s": 32 * dc / dt2, "ms_per_chunk": dt2 / 32 * 1e3,
                                  "depth": n,
                                  "hbm_roofline_ms_per_chunk": roofline_s(w, dc, n) * w.n_layer * 1e3}
+    # The step after the prompt: logits of the last position over a q8_0 LM head of
+    # LOGITS_VOCAB rows (seeded synthetic bytes with a fixed scale), HBM-bound: every head
+    # byte is read once.
+    last_logits = None
+    if not w.n_expert:
+        nb = w.d_model // 32
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        head = torch.randint(0, 256, (LOGITS_VOCAB, nb, 34), dtype=torch.uint8, device="cuda", generator=gen)
+        head[:, :, 0] = 0x00
+        head[:, :, 1] = 0x20
+        head = head.reshape(-1)
+        gain = torch.ones(w.d_model, device="cuda")
+        lg = torch.empty(LOGITS_VOCAB, device="cuda")
+        xr = out[n - 1]
+        for _ in range(3):
+            cpa.cp_last_logits(xr, gain, head, LOGITS_VOCAB, 1e-6, lg)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(20):
+            cpa.cp_last_logits(xr, gain, head, LOGITS_VOCAB, 1e-6, lg)
+        ev1.record()
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) / 20 * 1e3
+        last_logits = {"vocab": LOGITS_VOCAB, "d_model": w.d_model, "head_bytes": head.numel(),
+                       "us": us, "tb_per_s": head.numel() / us / 1e6,
+                       "frac_of_hbm": head.numel() / us / 1e6 / (PEAK_HBM_GBS / 1e3)}
+        del head, lg
     # whole-prompt roofline: sum of per-chunk-layer bounds
     bound = sum(roofline_s(w, e - s, s) for s, e in chunks) * w.n_layer
     res = {
@@ -288,6 +316,7 @@ def run_main(args, torch, cpa, synth):
         "prompt_roofline": {"bound_ms_per_step": bound * 1e3,
                             "frac": bound / (total / args.steps)},
         "decode_regime": decode,
+        "last_logits": last_logits,
     }
     ctx.close()
     del x, out
@@ -536,6 +565,7 @@ def main():
         "roofline": res["roofline"],
         "prompt_roofline": res["prompt_roofline"],
         "decode_regime": res["decode_regime"],
+        "last_logits": res["last_logits"],
         "measured_peaks": {"mfma_f16_tflops": mf_tflops, "hbm_read_gbs": hbm_gbs,
                            "published": {"mfma_f16_tflops": PEAK_F16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}},
         "cpu_baseline": cpu,

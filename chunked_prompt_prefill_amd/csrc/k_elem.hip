@@ -793,7 +793,9 @@ namespace cp {
 // ======================================================================================
 // Last-position logits: RMSNorm of one row, then logits[v] = sum_b d_vb * sum_j q_vbj * y_j
 // over the q8_0 LM head in its interchange layout (rows of d/32 blocks of 34 bytes).
-// HBM-bound: every head byte is read once.  The normed row is staged in LDS (float32);
+// HBM-bound: every head byte is read once.  The normed row is staged in LDS (float32,
+// 33 floats per block: lanes on consecutive blocks then read distinct banks, where a
+// stride of 32 floats would put every lane of the wave on one bank);
 // a wave takes one vocabulary row at a time, its lanes consecutive blocks (so a load
 // instruction covers 64 adjacent blocks), each lane reading its block as 17 halfwords;
 // the per-lane partial dot products are summed across the wave.
@@ -819,7 +821,7 @@ __global__ __launch_bounds__(LMW * 64) void last_logits_kernel(const float* __re
 #pragma unroll
   for (int w = 0; w < LMW; ++w) tot += red[w];
   const float scale = 1.0f / sqrtf(tot / (float)d + eps);
-  for (int i = tid; i < d; i += LMW * 64) sy[i] = x[i] * scale * gamma[i];
+  for (int i = tid; i < d; i += LMW * 64) sy[i + i / QK] = x[i] * scale * gamma[i];
   __syncthreads();
   const int nb = d / QK;
   const int64_t row_bytes = (int64_t)nb * 34;
@@ -829,7 +831,7 @@ __global__ __launch_bounds__(LMW * 64) void last_logits_kernel(const float* __re
     for (int b = lane; b < nb; b += 64) {
       const uint16_t* blk = row + b * 17;           // 34 bytes = 17 halfwords
       const float db = half_bits_to_float(blk[0]);
-      const float* ys = sy + b * QK;
+      const float* ys = sy + b * (QK + 1);
       float p = 0.0f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -845,10 +847,133 @@ __global__ __launch_bounds__(LMW * 64) void last_logits_kernel(const float* __re
   }
 }
 
+// Streaming form for rows that are whole 16-byte chunks (d % 256 == 0, head 16-byte
+// aligned): a wave reads its rows segment by segment (LL_SEGB blocks, 4352 bytes) with
+// coalesced 16-byte loads, keeping the next segment's loads in flight while the current
+// one is staged in the wave's LDS slot and decoded there (lane b takes blocks b, b + 64;
+// a block is 17 halfwords).  The halfword-per-lane global reads of the form above make
+// each load touch 34 cache lines, which caps that form far below the HBM rate.
+constexpr int LL_SEGB = 128;                      // q8_0 blocks per segment
+constexpr int LL_SEGBYTES = LL_SEGB * 34;         // 4352 bytes = 272 chunks of 16
+constexpr int LL_CHL = (LL_SEGBYTES / 16 + 63) / 64;   // chunks per lane per segment
+
+__global__ __launch_bounds__(LMW * 64) void last_logits_stream_kernel(const float* __restrict__ x,
+                                                                      const float* __restrict__ gamma,
+                                                                      const uint8_t* __restrict__ head,
+                                                                      int32_t vocab, int32_t d, float eps,
+                                                                      float* __restrict__ logits) {
+  extern __shared__ float sy[];                   // y (swizzled, see below), then LMW segment slots
+  __shared__ float red[LMW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float ss = 0.0f;
+  for (int i = tid; i < d; i += LMW * 64) ss += x[i] * x[i];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < LMW; ++w) tot += red[w];
+  const float scale = 1.0f / sqrtf(tot / (float)d + eps);
+  // float4 group g of block b sits at group (g + b) % 8 of the block's 32 floats: lanes on
+  // consecutive blocks reading the same group then hit distinct banks, and every read is
+  // an aligned 16-byte one
+  for (int i = tid; i < d; i += LMW * 64) {
+    const int b = i / QK, g = (i % QK) / 4;
+    sy[b * QK + 4 * ((g + b) & 7) + (i & 3)] = x[i] * scale * gamma[i];
+  }
+  __syncthreads();
+
+  uint8_t* slot = reinterpret_cast<uint8_t*>(sy + d) + wave * LL_SEGBYTES;
+  const int nb = d / QK, nseg = (nb + LL_SEGB - 1) / LL_SEGB;
+  const int64_t row_bytes = (int64_t)nb * 34;
+  const int64_t v0 = (int64_t)blockIdx.x * LMW + wave, vstep = (int64_t)gridDim.x * LMW;
+  const int64_t items = v0 < vocab ? ((vocab - 1 - v0) / vstep + 1) * nseg : 0;
+  auto seg_blocks = [&](int sg) { return min(LL_SEGB, nb - sg * LL_SEGB); };
+  auto load = [&](int64_t it, uint4 (&r)[LL_CHL]) {
+    const int64_t v = v0 + (it / nseg) * vstep;
+    const int sg = (int)(it % nseg);
+    const int nc = seg_blocks(sg) * 34 / 16;
+    const uint4* src = reinterpret_cast<const uint4*>(head + v * row_bytes + (int64_t)sg * LL_SEGBYTES);
+#pragma unroll
+    for (int c = 0; c < LL_CHL; ++c) {
+      const int ch = lane + 64 * c;
+      r[c] = ch < nc ? src[ch] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 cur[LL_CHL], nxt[LL_CHL];
+  if (items > 0) load(0, cur);
+  float part = 0.0f;
+  for (int64_t it = 0; it < items; ++it) {
+    if (it + 1 < items) load(it + 1, nxt);
+    const int sg = (int)(it % nseg);
+    const int nbs = seg_blocks(sg), nc = nbs * 34 / 16;
+    // The slot belongs to this wave alone, and a wave's LDS operations take effect in
+    // program order: the reads below see these writes, and the next item's writes come
+    // after these reads.
+#pragma unroll
+    for (int c = 0; c < LL_CHL; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nc) reinterpret_cast<uint4*>(slot)[ch] = cur[c];
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int b = lane; b < nbs; b += 64) {
+      // the block's 34 bytes from nine aligned words of the slot: block b starts at byte
+      // 34b, which is 0 or 2 past a word boundary; byte shifts realign them
+      const int a = (34 * b) >> 2, r = (34 * b) & 3;
+      const uint32_t* sw = reinterpret_cast<const uint32_t*>(slot) + a;
+      uint32_t u[9];
+#pragma unroll
+      for (int i = 0; i < 9; ++i) u[i] = sw[i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) u[i] = __builtin_amdgcn_alignbyte(u[i + 1], u[i], r);
+      u[8] = __builtin_amdgcn_alignbyte(0u, u[8], r);
+      const float db = half_bits_to_float(u[0] & 0xFFFFu);
+      const int blk = sg * LL_SEGB + b;
+      const float4* ys = reinterpret_cast<const float4*>(sy + blk * QK);
+      float p = 0.0f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const float4 yv = ys[(g + blk) & 7];
+        const float yy[4] = {yv.x, yv.y, yv.z, yv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 4 * g + e, byte = j + 2;        // q_j is byte j + 2 of the block
+          const int q = __builtin_amdgcn_sbfe((int)u[byte >> 2], 8 * (byte & 3), 8);
+          p = fmaf((float)q, yy[e], p);
+        }
+      }
+      part = fmaf(db, p, part);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (sg == nseg - 1) {
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+      if (lane == 0) logits[v0 + (it / nseg) * vstep] = part;
+      part = 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < LL_CHL; ++c) cur[c] = nxt[c];
+  }
+}
+
 hipError_t launch_last_logits(const float* x, const float* gamma, const void* head, int32_t vocab,
                               int32_t d, float eps, float* logits, hipStream_t s) {
   const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(vocab, LMW), 2048);
-  hipLaunchKernelGGL(last_logits_kernel, dim3(grid), dim3(LMW * 64), (size_t)d * sizeof(float), s,
+  if (d % 256 == 0 && (uintptr_t)head % 16 == 0) {
+    const size_t lds = (size_t)d * sizeof(float) + (size_t)LMW * LL_SEGBYTES;
+    hipError_t e = hipFuncSetAttribute((const void*)last_logits_stream_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(last_logits_stream_kernel, dim3(grid), dim3(LMW * 64), lds, s, x, gamma,
+                       (const uint8_t*)head, vocab, d, eps, logits);
+    return hipGetLastError();
+  }
+  const size_t lds = (size_t)(d + d / QK) * sizeof(float);
+  hipError_t e = hipFuncSetAttribute((const void*)last_logits_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(last_logits_kernel, dim3(grid), dim3(LMW * 64), lds, s,
                      x, gamma, (const uint8_t*)head, vocab, d, eps, logits);
   return hipGetLastError();
 }

@@ -197,8 +197,11 @@ int cp_kernel_times(cp_ctx* ctx, const char* kernel_class, float* total_ms, int3
  *   norm_gain: dev float32 [d_model];
  *   lm_head: dev q8_0 interchange [vocab][d_model/32 x 34 bytes], 2-byte aligned;
  *   logits: dev float32 [vocab].
- * d_model % 32 == 0 and <= 32768.  Enqueued on hip_stream.  Returns CP_OK, CP_E_INVALID
- * for bad arguments, CP_E_DEVICE if the launch fails.  No allocation, no state. */
+ * d_model % 32 == 0 and <= 32768.  The head streams at close to the HBM rate when
+ * d_model % 256 == 0 and lm_head is 16-byte aligned (rows are then whole 16-byte chunks);
+ * other heads take a slower per-block path with the same result to float32 rounding.
+ * Enqueued on hip_stream.  Returns CP_OK, CP_E_INVALID for bad arguments, CP_E_DEVICE if
+ * the launch fails.  No allocation, no state. */
 int cp_last_logits(const float* x_row, const float* norm_gain, const void* lm_head, int32_t vocab,
                    int32_t d_model, float eps, float* logits, void* hip_stream);
 

@@ -332,16 +332,22 @@ def test_router_bit_exact(torch, cpa, n, d, E, k):
 
 
 # --------------------------------------------------------------------------- last logits
-@pytest.mark.parametrize("vocab,d", [(4096, 5120), (1000, 256), (33, 2048)])
-def test_last_logits_matches_oracle(torch, cpa, vocab, d):
+# d % 256 == 0 with an aligned head takes the streaming kernel (one partial segment, one
+# and a half, four and eight segments of 128 blocks); d = 2080 and a head at an odd
+# halfword offset take the per-block kernel.
+@pytest.mark.parametrize("vocab,d,offset", [(4096, 5120, 0), (1000, 256, 0), (33, 2048, 0), (77, 2080, 0),
+                                            (129, 16384, 0), (40, 32768, 0), (300, 5120, 2)])
+def test_last_logits_matches_oracle(torch, cpa, vocab, d, offset):
     """RMSNorm + q8_0 LM head on one row: float32 accumulation against the float64
     definition, to 1e-4 of the largest logit."""
-    log(f"last logits vocab={vocab} d={d}")
+    log(f"last logits vocab={vocab} d={d} head offset={offset}")
     x = synth.normal(synth.tensor_seed("xrow", d), (d,), scale=1.0)
     gamma = (1.0 + synth.normal(synth.tensor_seed("g", d), (d,))).astype(np.float32)
     head = oracle.q8_0_encode_bytes(synth.normal(synth.tensor_seed("head", vocab, d), (vocab, d)))
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    got = cpa.cp_last_logits(T(x), T(gamma), T(head), vocab, 1e-6).cpu().numpy()
+    hbuf = torch.zeros(head.size + offset, dtype=torch.uint8, device="cuda")
+    hbuf[offset:] = T(head.reshape(-1))
+    got = cpa.cp_last_logits(T(x), T(gamma), hbuf[offset:], vocab, 1e-6).cpu().numpy()
     ref = oracle.last_logits(x, gamma, head, d, 1e-6)
     e = rel_err(got, ref)
     log(f"  max rel err {e:.3e}")
