@@ -124,17 +124,20 @@ __device__ __forceinline__ float4 pend_load4(const float* base, int64_t ld, cons
   if (ps.add) { acc.x = b.x + acc.x; acc.y = b.y + acc.y; acc.z = b.z + acc.z; acc.w = b.w + acc.w; }
   return acc;
 }
-// One row per workgroup.  Pass 1 takes the pending sums into x (written back) and forms
-// the sum of squares; pass 2 re-reads the row (this thread's own writes) and scales it.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(float* x, const float* __restrict__ gamma,
-                                                      int32_t d, float eps, _Float16* __restrict__ y,
-                                                      float* __restrict__ y32, PendingSum ps) {
-  __shared__ float red[4];
+// One row per workgroup of nthr threads (a multiple of 64, at most 1024; about two float4
+// columns per thread, so that a row's loads are spread over many waves).  Pass 1 takes the
+// pending sums into x (written back) and forms the sum of squares; pass 2 re-reads the row
+// (this thread's own writes) and scales it.
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(float* x, const float* __restrict__ gamma,
+                                                       int32_t d, float eps, _Float16* __restrict__ y,
+                                                       float* __restrict__ y32, PendingSum ps) {
+  __shared__ float red[16];
+  const int nthr = blockDim.x;
   const int64_t row = blockIdx.x;
   float* xr = x + row * d;
   const bool pend = ps.partial != nullptr;
   float ss = 0.0f;
-  for (int i = threadIdx.x * 4; i < d; i += 1024) {
+  for (int i = threadIdx.x * 4; i < d; i += 4 * nthr) {
     const float4 v = pend ? pend_load4(x, d, ps, row, i) : *reinterpret_cast<const float4*>(xr + i);
     if (pend && i >= ps.n0) *reinterpret_cast<float4*>(xr + i) = v;
     ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
@@ -143,9 +146,10 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* x, const float* __r
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  ss = red[0] + red[1] + red[2] + red[3];
+  ss = red[0];
+  for (int w = 1; w < nthr / 64; ++w) ss += red[w];
   const float scale = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int i = threadIdx.x * 4; i < d; i += 1024) {
+  for (int i = threadIdx.x * 4; i < d; i += 4 * nthr) {
     const float4 v = *reinterpret_cast<const float4*>(xr + i);
     const float4 gm = *reinterpret_cast<const float4*>(gamma + i);
     const float a = v.x * scale * gm.x, b = v.y * scale * gm.y;
@@ -159,7 +163,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* x, const float* __r
 hipError_t launch_rmsnorm(float* x, const float* gamma, int32_t n, int32_t d, float eps,
                           _Float16* y, float* y32, hipStream_t s, const PendingSum& ps) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(n), dim3(256), 0, s, x, gamma, d, eps, y, y32, ps);
+  if (d <= 0 || d % 4) return hipErrorInvalidValue;
+  const int nthr = (int)std::min<int64_t>(1024, std::max<int64_t>(64, ceil_div(ceil_div(d, 8), 64) * 64));
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(n), dim3(nthr), 0, s, x, gamma, d, eps, y, y32, ps);
   return hipGetLastError();
 }
 
