@@ -4,5 +4,5 @@
 """
 from ._lib import lib, LIB_PATH, PrefillError, cp_config, cp_layer_weights  # noqa: F401
 from .prefill import (PrefillContext, make_config, arena_sizes, validate_config,  # noqa: F401
-                      to_device, cp_quantize_q8_0, cp_test_gemm_plan,
+                      to_device, chunk_check, cp_quantize_q8_0, cp_test_gemm_plan,
                       cp_measure_peaks, cp_plan_chunk, cp_last_logits)

@@ -53,6 +53,7 @@ SIGNATURES = {
     "kv_cache_set_state": (ctypes.c_int, [c_vp, c_vp, c_sz]),
     "cp_state_check": (ctypes.c_int, [ctypes.POINTER(cp_config), c_vp, c_sz]),
     "cp_state_bytes": (c_sz, [ctypes.POINTER(cp_config), c_i32]),
+    "cp_chunk_check": (ctypes.c_int, [ctypes.POINTER(cp_config), c_i32, c_vp, c_vp, c_i32]),
     "kv_cache_truncate": (ctypes.c_int, [c_vp, c_i32]),
     "prefill_n_past": (c_i32, [c_vp]),
     "prefill_last_error": (ctypes.c_char_p, [c_vp]),

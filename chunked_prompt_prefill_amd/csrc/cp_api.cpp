@@ -62,7 +62,29 @@ std::string validate(const cp_config* c) {
   if ((int64_t)(c->n_ctx_max + 63) * c->head_dim * 2 >= (1LL << 31)) return "n_ctx_max * head_dim too large";
   if (c->n_chunk_max < 1 || c->n_chunk_max > c->n_ctx_max) return "n_chunk_max must be in [1, n_ctx_max]";
   if ((int64_t)c->n_chunk_max * c->n_head * c->head_dim > (1LL << 31)) return "n_chunk_max too large";
+  // The GEMMs address their fp16 A operand (n_chunk_max rows of the normed input, the
+  // attention output, the FFN intermediate, or the routed slots' intermediate) with 32-bit
+  // byte offsets from the buffer's base, so the largest such operand stays below 2 GiB.
+  {
+    const int64_t Fp = round_up(c->ffn_dim, 128), Fep = round_up(c->expert_ffn_dim, 128);
+    const int64_t widest = std::max<int64_t>({(int64_t)c->d_model, (int64_t)c->n_head * c->head_dim, Fp});
+    const int64_t a_bytes = std::max<int64_t>((int64_t)c->n_chunk_max * widest * 2,
+                                              moe ? (int64_t)c->n_chunk_max * c->n_expert_used * Fep * 2 : 0);
+    if (a_bytes >= (1LL << 31))
+      return "n_chunk_max rows of the widest fp16 GEMM operand must stay below 2 GiB";
+  }
   return "";
+}
+
+// The checks prefill_chunk makes before enqueuing anything: pointers, their 16-byte
+// alignment (the row kernels move x in float4 units), and the chunk's bounds.
+int chunk_check(const cp_config* c, int64_t n_past, const float* x_in, const float* x_out, int32_t n,
+                std::string& err) {
+  if (!x_in || !x_out) { err = "x_in / x_out is NULL"; return CP_E_INVALID; }
+  if ((uintptr_t)x_in % 16 || (uintptr_t)x_out % 16) { err = "x_in / x_out must be 16-byte aligned"; return CP_E_INVALID; }
+  if (n < 1 || n > c->n_chunk_max) { err = "n_tokens outside [1, n_chunk_max]"; return CP_E_CAPACITY; }
+  if (n_past + n > c->n_ctx_max) { err = "n_past + n_tokens > n_ctx_max"; return CP_E_CAPACITY; }
+  return CP_OK;
 }
 
 Dims dims_of(const cp_config* c) {
@@ -635,6 +657,13 @@ int cp_state_check(const cp_config* cfg, const void* src, size_t n_bytes) {
   return check_state(cfg, src, n_bytes, err, nullptr);
 }
 
+int cp_chunk_check(const cp_config* cfg, int32_t n_past, const float* x_in, const float* x_out,
+                   int32_t n_tokens) {
+  if (!validate(cfg).empty() || n_past < 0) return CP_E_INVALID;
+  std::string err;
+  return chunk_check(cfg, n_past, x_in, x_out, n_tokens, err);
+}
+
 int prefill_init(const cp_config* cfg, const cp_layer_weights* layers, void* weights_arena,
                  void* kv_buf, void* workspace, void* hip_stream, cp_ctx** out) {
   if (!out) return CP_E_INVALID;
@@ -736,9 +765,7 @@ int prefill_init(const cp_config* cfg, const cp_layer_weights* layers, void* wei
 
 int prefill_chunk(cp_ctx* c, const float* x_in, float* x_out, int32_t n) {
   if (!c) return CP_E_INVALID;
-  if (!x_in || !x_out) return fail(c, CP_E_INVALID, "x_in / x_out is NULL");
-  if (n < 1 || n > c->cfg.n_chunk_max) return fail(c, CP_E_CAPACITY, "n_tokens outside [1, n_chunk_max]");
-  if ((int64_t)c->n_past + n > c->cfg.n_ctx_max) return fail(c, CP_E_CAPACITY, "n_past + n_tokens > n_ctx_max");
+  if (const int r = chunk_check(&c->cfg, c->n_past, x_in, x_out, n, c->err); r != CP_OK) return r;
   const int start = c->n_past;
   c->pend_x = PendingSum();
   for (int l = 0; l < c->D.L; ++l) {
@@ -752,9 +779,7 @@ int prefill_chunk(cp_ctx* c, const float* x_in, float* x_out, int32_t n) {
 int prefill_chunk_trace(cp_ctx* c, const float* x_in, float* x_out, int32_t n, float* layer_out,
                         int64_t layer_stride, int32_t* route_idx, int64_t route_stride) {
   if (!c) return CP_E_INVALID;
-  if (!x_in || !x_out) return fail(c, CP_E_INVALID, "x_in / x_out is NULL");
-  if (n < 1 || n > c->cfg.n_chunk_max) return fail(c, CP_E_CAPACITY, "n_tokens outside [1, n_chunk_max]");
-  if ((int64_t)c->n_past + n > c->cfg.n_ctx_max) return fail(c, CP_E_CAPACITY, "n_past + n_tokens > n_ctx_max");
+  if (const int r = chunk_check(&c->cfg, c->n_past, x_in, x_out, n, c->err); r != CP_OK) return r;
   if (layer_out && layer_stride < (int64_t)n * c->D.d) return fail(c, CP_E_INVALID, "layer_stride too small");
   if (route_idx && (!c->D.moe || route_stride < (int64_t)n * c->D.k))
     return fail(c, CP_E_INVALID, "route_idx needs routed experts and route_stride >= n * n_expert_used");
@@ -777,9 +802,7 @@ int prefill_chunk_trace(cp_ctx* c, const float* x_in, float* x_out, int32_t n, f
 int prefill_chunk_timed(cp_ctx* c, const float* x_in, float* x_out, int32_t n, float* layer_ms) {
   if (!c) return CP_E_INVALID;
   if (!layer_ms) return fail(c, CP_E_INVALID, "layer_ms is NULL");
-  if (!x_in || !x_out) return fail(c, CP_E_INVALID, "x_in / x_out is NULL");
-  if (n < 1 || n > c->cfg.n_chunk_max) return fail(c, CP_E_CAPACITY, "n_tokens outside [1, n_chunk_max]");
-  if ((int64_t)c->n_past + n > c->cfg.n_ctx_max) return fail(c, CP_E_CAPACITY, "n_past + n_tokens > n_ctx_max");
+  if (const int r = chunk_check(&c->cfg, c->n_past, x_in, x_out, n, c->err); r != CP_OK) return r;
   const int L = c->D.L;
   std::vector<hipEvent_t> ev(L + 1, nullptr);
   for (auto& e : ev) CP_HIP(c, hipEventCreate(&e), "event create");

@@ -44,6 +44,11 @@ def validate_config(cfg: cp_config) -> str:
     return L.cp_config_error(ctypes.byref(cfg)).decode()
 
 
+def chunk_check(cfg: cp_config, n_past: int, x_in_ptr: int, x_out_ptr: int, n_tokens: int) -> int:
+    """The host-side checks prefill_chunk makes for a context of cfg at n_past (status code)."""
+    return lib().cp_chunk_check(ctypes.byref(cfg), int(n_past), x_in_ptr, x_out_ptr, int(n_tokens))
+
+
 def to_device(layer: Dict[str, np.ndarray], device="cuda") -> Dict[str, torch.Tensor]:
     """Copy one layer's interchange bytes / gains to device memory."""
     out = {}

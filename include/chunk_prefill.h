@@ -66,9 +66,17 @@ enum cp_status {
 enum cp_kv_type { CP_KV_F16 = 0, CP_KV_Q8_0 = 1 };
 
 /* Model geometry and capacities.  Supported shapes: head_dim in {64, 128};
- * n_head % n_kv_head == 0; d_model % 64 == 0; (n_head * head_dim) % 64 == 0;
- * dense ffn_dim > 0 with n_expert == 0, or routed experts with ffn_dim == 0,
- * n_expert in [1, 256], 1 <= n_expert_used <= min(n_expert, 16), expert_ffn_dim > 0. */
+ * n_head % n_kv_head == 0 and n_head / n_kv_head <= 64; d_model % 128 == 0;
+ * (n_head * head_dim) % 128 == 0; dense ffn_dim > 0 with n_expert == 0, or routed
+ * experts with ffn_dim == 0, n_expert in [1, 256], 1 <= n_expert_used <=
+ * min(n_expert, 16), expert_ffn_dim > 0.  Capacities: 1 <= n_ctx_max <= 2^24 with
+ * (n_ctx_max rounded up to 64) * head_dim * 2 < 2^31 (one kv head's cache is addressed
+ * with 32-bit byte offsets); 1 <= n_chunk_max <= n_ctx_max, with n_chunk_max * n_head *
+ * head_dim <= 2^31 and, because the GEMMs address their fp16 input with 32-bit byte
+ * offsets, n_chunk_max * W * 2 < 2^31 for the widest GEMM input row W = max(d_model,
+ * n_head*head_dim, ffn_dim rounded up to 128) (and n_expert_used * expert_ffn_dim
+ * rounded up to 128 for routed experts).  Anything else is rejected with CP_E_INVALID
+ * (cp_validate_config, cp_config_error). */
 typedef struct cp_config {
   int32_t n_layer, d_model, n_head, n_kv_head, head_dim;
   int32_t ffn_dim;                                 /* dense FFN width; 0 for experts  */
@@ -116,7 +124,8 @@ int prefill_init(const cp_config* cfg, const cp_layer_weights* layers, void* wei
                  void* kv_buf, void* workspace, void* hip_stream, cp_ctx** out);
 
 /* Process one chunk of n_tokens rows at positions n_past .. n_past+n_tokens-1.
- * x_in, x_out: dev float32 [n_tokens][d_model] row-major; x_out may equal x_in.
+ * x_in, x_out: dev float32 [n_tokens][d_model] row-major, 16-byte aligned (else
+ * CP_E_INVALID, nothing enqueued); x_out may equal x_in.
  * Every layer appends the chunk's K/V (post-RoPE K) to its cache, then attends to cache
  * rows 0 .. n_past+n_tokens-1 ("append, then attend").  Requires 1 <= n_tokens <=
  * n_chunk_max and n_past + n_tokens <= n_ctx_max (else CP_E_CAPACITY, nothing
@@ -158,6 +167,14 @@ int kv_cache_get_state(cp_ctx* ctx, void* dst, size_t cap, size_t* n_bytes);
  * previous cache and n_past are untouched.  On success n_past = n_tokens.  The bytes a
  * following kv_cache_get_state returns are identical to src.  Synchronises the stream. */
 int kv_cache_set_state(cp_ctx* ctx, const void* src, size_t n_bytes);
+
+/* Host-only: the argument checks prefill_chunk (and its _timed / _trace forms) makes
+ * before enqueuing anything, for a context of configuration cfg at n_past: CP_E_INVALID
+ * for a NULL or not 16-byte aligned x_in / x_out (or an invalid cfg, n_past < 0),
+ * CP_E_CAPACITY for n_tokens outside [1, n_chunk_max] or n_past + n_tokens > n_ctx_max,
+ * else CP_OK.  The pointers are only inspected, never dereferenced. */
+int cp_chunk_check(const cp_config* cfg, int32_t n_past, const float* x_in, const float* x_out,
+                   int32_t n_tokens);
 
 /* Host-only header check of a blob against a configuration (the same validation
  * kv_cache_set_state does before touching the cache). */

@@ -126,3 +126,51 @@ def test_gemm_launch_plans_cover_the_columns(cpa, M, N, K):
         assert not (M <= 4 and N % 64 == 0)
         assert mt != 256 or M > 128
         assert mt != 128 or M > 64
+
+
+def test_chunk_limit_of_the_gemm_operand_offsets(cpa):
+    """The GEMMs address their fp16 input with 32-bit byte offsets: a chunk whose widest
+    operand (the dense FFN intermediate, 17,408 columns at the 27B-class shapes) reaches
+    2 GiB is refused at configuration time instead of reading zeros past 2 GiB."""
+    w = synth.WORKLOADS["dense27b_f16"]
+    limit = (1 << 31) // (2 * 17408)          # 61,680 rows of the FFN intermediate
+    ok = cpa.make_config(w, limit, limit)
+    assert cpa.validate_config(ok) == ""
+    bad = cpa.make_config(w, limit + 1, limit + 1)
+    assert "2 GiB" in cpa.validate_config(bad)
+    assert cpa.arena_sizes(bad) == (0, 0, 0)
+    # routed experts: the slots' intermediate (n * n_expert_used rows) counts
+    m = synth.WORKLOADS["moe_a3b"]
+    lim_m = (1 << 31) // (2 * 8 * 768)
+    assert cpa.validate_config(cpa.make_config(m, lim_m, lim_m)) == ""
+    assert cpa.validate_config(cpa.make_config(m, lim_m + 1, lim_m + 1)) != ""
+
+
+@pytest.mark.parametrize("field,value", [("d_model", 5120 + 64), ("n_head", 41)])
+def test_shape_multiples_of_128(cpa, field, value):
+    """d_model and n_head*head_dim must be multiples of 128, as the header documents."""
+    cfg = cpa.make_config(synth.WORKLOADS["dense27b_f16"], 1024, 512)
+    setattr(cfg, field, value)
+    if field == "n_head":
+        cfg.n_kv_head, cfg.head_dim = 41, 64   # 41 x 64 = 2624: only the 128 rule fails
+    assert "128" in cpa.validate_config(cfg)
+
+
+def test_chunk_argument_checks(cpa):
+    """prefill_chunk's host-side checks (run before anything is enqueued): NULL and
+    misaligned x_in / x_out are CP_E_INVALID, a chunk outside [1, n_chunk_max] or past
+    n_ctx_max is CP_E_CAPACITY.  The addresses are never dereferenced."""
+    cfg = cpa.make_config(synth.WORKLOADS["dense27b_f16"], 1024, 512)
+    base = 1 << 20
+    assert cpa.chunk_check(cfg, 0, base, base + 4096, 512) == 0
+    assert cpa.chunk_check(cfg, 0, base, base, 1) == 0                 # in place
+    assert cpa.chunk_check(cfg, 0, None, base, 1) == -1
+    assert cpa.chunk_check(cfg, 0, base, None, 1) == -1
+    for off in (4, 8, 12):
+        assert cpa.chunk_check(cfg, 0, base + off, base, 1) == -1
+        assert cpa.chunk_check(cfg, 0, base, base + off, 1) == -1
+    assert cpa.chunk_check(cfg, 0, base, base, 0) == -2
+    assert cpa.chunk_check(cfg, 0, base, base, 513) == -2
+    assert cpa.chunk_check(cfg, 600, base, base, 425) == -2            # 600 + 425 > 1024
+    assert cpa.chunk_check(cfg, 600, base, base, 424) == 0
+    assert cpa.chunk_check(cfg, -1, base, base, 1) == -1

@@ -118,3 +118,63 @@ def test_state_sizes_at_workload_geometry():
     assert oracle.state_size(16, 8, 128, 17055, "f16") == 1_117_716_512
     assert oracle.state_size(16, 8, 128, 58300, "q8_0") == 2_029_772_832
     assert HEADER.size == 32
+
+
+@pytest.mark.parametrize("kv", ["f16", "q8_0"])
+def test_state_byte_order_at_explicit_offsets(kv):
+    """The blob's body order, pinned by hand: for every layer, all K rows and then all V
+    rows; within each, rows in token-major order (t, h).  A cache of 2 layers, 3 tokens,
+    2 kv heads and head_dim 32 (one q8_0 block per row) is filled with a marker that names
+    (layer, K/V, token, head, element), and every row is looked up at the offset
+        32 + l*2*T*H*rb + which*T*H*rb + (t*H + h)*rb
+    written out here rather than taken from the serializer.  Swapping K and V, t and h, or
+    two layers moves some marker off its offset.  The form is the pages' layout-independent
+    sequence state ("completion : allow the prompt to be processed under its own split
+    mode", section "What this does"; "llama : switch the split mode of a live context",
+    section "What this adds")."""
+    L, T, H, hd = 2, 3, 2, 32
+    rb = hd * 2 if kv == "f16" else 34
+    cache = oracle.OracleCache(L, 8, H, hd, kv)
+
+    def code(l, which, t, h):            # 0 .. 23, distinct for every row of the blob
+        return ((l * 2 + which) * T + t) * H + h
+
+    for l in range(L):
+        for which in range(2):
+            if kv == "f16":
+                # row values code*32 + i: integers below 2048, exact in binary16
+                rows = np.array([[[code(l, which, t, h) * 32 + i for i in range(hd)]
+                                  for h in range(H)] for t in range(T)], dtype=np.float16)
+            else:
+                d16 = np.array([[[1.0 + code(l, which, t, h)] for h in range(H)]
+                                for t in range(T)], dtype=np.float16)
+                q = np.array([[[[(code(l, which, t, h) * 5 + i) % 251 - 125 for i in range(hd)]]
+                               for h in range(H)] for t in range(T)], dtype=np.int8)
+                rows = (d16, q)
+            cache.set_stored(l, "kv"[which], rows, T)
+    cache.n_past = T
+    blob = oracle.state_bytes(cache, 1e6)
+    assert len(blob) == 32 + L * 2 * T * H * rb
+    for l in range(L):
+        for which in range(2):
+            for t in range(T):
+                for h in range(H):
+                    c = code(l, which, t, h)
+                    off = 32 + l * 2 * T * H * rb + which * T * H * rb + (t * H + h) * rb
+                    row = blob[off:off + rb]
+                    if kv == "f16":
+                        want = np.arange(c * 32, c * 32 + hd, dtype=np.float64).astype("<f2").tobytes()
+                    else:
+                        want = np.array([1.0 + c], dtype="<f2").tobytes() + bytes(
+                            ((c * 5 + i) % 251 - 125) & 0xFF for i in range(hd))
+                    assert row == want, (l, which, t, h)
+    # the parser reads the same rows back from those offsets
+    _, layers = oracle.parse_state(blob)
+    for l in range(L):
+        for which in range(2):
+            got = layers[l][which]
+            ref = cache.stored(l, "kv"[which], T)
+            if kv == "f16":
+                assert np.array_equal(got, ref)
+            else:
+                assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
