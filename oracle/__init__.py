@@ -31,7 +31,7 @@ Parity status of each function (what pins it) is stated in its docstring.
 """
 from .q8_0 import (q8_0_encode, q8_0_decode, q8_0_to_bytes, q8_0_from_bytes,
                    q8_0_encode_bytes, q8_0_decode_bytes, QK)
-from .layer import (rmsnorm, rope_table, rope_apply_f32, rope_apply, attention,
+from .layer import (rmsnorm, rope_table, rope_apply_f32, rope_apply, attention, to_f16,
                     swiglu_ffn, router_logits_ordered, moe_route, moe_ffn,
                     cache_encode_rows, cache_decode_rows)
 from .prefill import OracleModel, OracleCache, dequant_layer, quantize_layer

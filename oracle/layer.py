@@ -25,6 +25,29 @@ from .q8_0 import q8_0_encode, q8_0_decode, QK
 
 
 # ---------------------------------------------------------------------------------------
+# fp16 operands
+# ---------------------------------------------------------------------------------------
+
+F16_MAX = 65504.0
+
+
+def to_f16(x: np.ndarray, saturate: bool = False) -> np.ndarray:
+    """Values rounded to IEEE binary16 (round to nearest, ties to even), returned as
+    float64.  saturate: clamp to +-65504 first (the largest finite binary16).
+
+    Used by the oracle's "f16 operands" mode: every matrix-product operand is rounded to
+    binary16 and the products are then accumulated exactly (float64), the arithmetic the
+    library states for its matrix products.  Pinned by: hand-picked ties and boundaries
+    (1 + 2^-11 -> 1, 1 + 3*2^-11 -> 1 + 2^-9, 65519 -> 65504, 65520 -> inf, saturated
+    -> 65504), and agreement with the bit patterns of the float16 type.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if saturate:
+        x = np.clip(x, -F16_MAX, F16_MAX)
+    return x.astype(np.float16).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------------------
 # RMSNorm
 # ---------------------------------------------------------------------------------------
 
@@ -126,15 +149,19 @@ def cache_decode_rows(stored, kv_type: str) -> np.ndarray:
 # ---------------------------------------------------------------------------------------
 
 def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, positions: np.ndarray,
-              block: int = 512) -> np.ndarray:
+              block: int = 512, p_f16: bool = False) -> np.ndarray:
     """Causal GQA softmax attention (float64).
 
     q: [n][Hq][hd]; K, V: [T][Hkv][hd] (cache values, position = row index);
     positions: [n] absolute position of each query row.  Query row i of head h
     attends keys j <= positions[i] of kv head h // (Hq/Hkv):
         s_j = q_i . K_j / sqrt(hd),  P = softmax(s) (max subtracted),  o_i = sum_j P_j V_j
+    p_f16: the unnormalised weights exp(s_j - max) are rounded to binary16 (the operand of
+    the P.V product) and the row is normalised by the sum of the rounded weights.
     Pinned by: brute-force scalar loops on tiny inputs, a single visible key
-    returning its value row, causality, duplicated KV heads = multi-head.
+    returning its value row, causality, duplicated KV heads = multi-head; with p_f16,
+    scores at multiples of ln 2 (weights exact powers of two) give the exact result, and
+    random scores stay within binary16 rounding of it.
     """
     q = np.asarray(q, dtype=np.float64)
     n, Hq, hd = q.shape
@@ -157,6 +184,8 @@ def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, positions: np.ndarray
             s[mask] = -np.inf
             s -= s.max(axis=1, keepdims=True)
             p = np.exp(s)
+            if p_f16:
+                p = to_f16(p)
             p /= p.sum(axis=1, keepdims=True)
             out[r0:r1, h, :] = p @ V64[:Tb, g, :]
     return out
@@ -171,17 +200,20 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 
 def swiglu_ffn(y: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
-               block: int = 2048) -> np.ndarray:
+               block: int = 2048, h_f16: bool = False) -> np.ndarray:
     """(silu(y Wg^T) * (y Wu^T)) Wd^T in float64, evaluated in row blocks.
 
-    Wg, Wu: [F][d]; Wd: [d][F].  Pinned by: the closed form on a tiny example,
-    silu(0) = 0.
+    Wg, Wu: [F][d]; Wd: [d][F].  h_f16: the intermediate h (the down projection's
+    operand) is saturated to +-65504 and rounded to binary16.  Pinned by: the closed form
+    on a tiny example, silu(0) = 0.
     """
     y = np.asarray(y, dtype=np.float64)
     out = np.empty((y.shape[0], Wd.shape[0]), dtype=np.float64)
     for r0 in range(0, y.shape[0], block):
         yb = y[r0:r0 + block]
         h = silu(yb @ Wg.T) * (yb @ Wu.T)
+        if h_f16:
+            h = to_f16(h, saturate=True)
         out[r0:r0 + block] = h @ Wd.T
     return out
 
@@ -237,7 +269,7 @@ def moe_route(r32: np.ndarray, k: int):
 
 
 def moe_ffn(y: np.ndarray, idx: np.ndarray, w: np.ndarray, Wg: np.ndarray, Wu: np.ndarray,
-            Wd: np.ndarray) -> np.ndarray:
+            Wd: np.ndarray, h_f16: bool = False) -> np.ndarray:
     """sum_{rank 0..k-1} w[t,rank] * FFN_{idx[t,rank]}(y_t), summed in rank order (float64).
 
     Wg, Wu: [E][Fe][d]; Wd: [E][d][Fe].  Pinned by: E identical experts reduce
@@ -251,6 +283,6 @@ def moe_ffn(y: np.ndarray, idx: np.ndarray, w: np.ndarray, Wg: np.ndarray, Wu: n
         col = idx[:, rank]
         for e in np.unique(col):
             rows = np.nonzero(col == e)[0]
-            contrib[rows] = swiglu_ffn(y[rows], Wg[e], Wu[e], Wd[e])
+            contrib[rows] = swiglu_ffn(y[rows], Wg[e], Wu[e], Wd[e], h_f16=h_f16)
         out = out + w[:, rank][:, None] * contrib
     return out

@@ -26,7 +26,7 @@ import numpy as np
 from .q8_0 import q8_0_decode_bytes, q8_0_from_bytes, q8_0_encode_bytes, QK
 from .layer import (rmsnorm, rope_table, rope_apply_f32, attention, swiglu_ffn,
                     router_logits_ordered, moe_route, moe_ffn, cache_encode_rows,
-                    cache_decode_rows)
+                    cache_decode_rows, to_f16)
 
 MATRIX_NAMES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "w_router")
 
@@ -40,13 +40,31 @@ def quantize_layer(fp32_layer: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
     return out
 
 
+def _decode_matrix(b: np.ndarray, K: int, dtype, rows_per_block: int = 1024) -> np.ndarray:
+    """q8_0_decode_bytes of every row, converted to dtype.  Each row decodes on its own, so
+    the rows are split into blocks decoded by a thread pool (NumPy releases the GIL in
+    these loops); the values are those of one call over the whole matrix."""
+    from concurrent.futures import ThreadPoolExecutor
+    import os
+    flat = b.reshape(-1, b.shape[-1])
+    out = np.empty((flat.shape[0], K), dtype=dtype)
+
+    def work(s):
+        out[s:s + rows_per_block] = q8_0_decode_bytes(flat[s:s + rows_per_block], K)
+
+    starts = range(0, flat.shape[0], rows_per_block)
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(work, starts))
+    return out.reshape(b.shape[:-1] + (K,))
+
+
 def dequant_layer(qlayer: Dict[str, np.ndarray], K_of: Dict[str, int],
                   dtype=np.float64) -> Dict[str, np.ndarray]:
     """Interchange bytes -> dense matrices (float64 by default); gains passed through."""
     out = {}
     for name, t in qlayer.items():
         if name in MATRIX_NAMES:
-            out[name] = q8_0_decode_bytes(t, K_of[name]).astype(dtype)
+            out[name] = _decode_matrix(t, K_of[name], dtype)
         else:
             out[name] = np.asarray(t, dtype=dtype)
     return out
@@ -112,12 +130,26 @@ class OracleModel:
     n_expert, n_expert_used, expert_ffn_dim, rms_eps, rope_theta, kv_type.
     layers: one dict per layer (see quantize_layer).  Dequantised float64
     weights are kept for at most `keep_layers` layers at a time.
+
+    operands: "exact" (default) evaluates every matrix product on the exact operands in
+    float64.  "f16" rounds every operand of a matrix product to binary16 first and then
+    accumulates exactly (float64): the normed rows entering the projections, each q8_0
+    weight (the binary16 of d*q), q and the cache values entering attention, the
+    unnormalised attention weights, the attention output, and the SwiGLU intermediate
+    (saturated to +-65504).  It is the arithmetic the library states for its matrix
+    products, and it is where a q8_0 cache's codes are decided: a K/V value is encoded from
+    the products of those operands.  Everything else (norms, RoPE, cache encode, router,
+    softmax normaliser, residual) is the same in both modes.
     """
 
-    def __init__(self, cfg, layers: Sequence[Dict[str, np.ndarray]], keep_layers: int = 64):
+    def __init__(self, cfg, layers: Sequence[Dict[str, np.ndarray]], keep_layers: int = 64,
+                 operands: str = "exact"):
+        if operands not in ("exact", "f16"):
+            raise ValueError(operands)
         self.cfg = cfg
         self.layers = list(layers)
         self.keep = keep_layers
+        self.f16 = operands == "f16"
         self._deq: Dict[int, Dict[str, np.ndarray]] = {}
         self._rope = None
         c = cfg
@@ -131,8 +163,16 @@ class OracleModel:
         if l not in self._deq:
             if len(self._deq) >= self.keep:
                 self._deq.pop(next(iter(self._deq)))
-            self._deq[l] = dequant_layer(self.layers[l], self.K_of)
+            W = dequant_layer(self.layers[l], self.K_of)
+            if self.f16:
+                for name in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
+                    W[name] = to_f16(W[name])
+            self._deq[l] = W
         return self._deq[l]
+
+    def _op(self, a: np.ndarray) -> np.ndarray:
+        """A matrix-product operand as this mode takes it."""
+        return to_f16(a) if self.f16 else a
 
     def rope(self, n_pos: int):
         if self._rope is None or self._rope[0].shape[0] < n_pos:
@@ -152,7 +192,7 @@ class OracleModel:
         """
         c, W = self.cfg, self.weights(l)
         n, hd = x.shape[0], c.head_dim
-        y = rmsnorm(x, W["attn_norm"], c.rms_eps)
+        y = self._op(rmsnorm(x, W["attn_norm"], c.rms_eps))
         q = (y @ W["wq"].T).astype(np.float32).reshape(n, c.n_head, hd)
         k = (y @ W["wk"].T).astype(np.float32).reshape(n, c.n_kv_head, hd)
         v = (y @ W["wv"].T).astype(np.float32).reshape(n, c.n_kv_head, hd)
@@ -165,7 +205,7 @@ class OracleModel:
         the K/V half of qkv_rows, for rows whose query is not needed."""
         c, W = self.cfg, self.weights(l)
         n, hd = x.shape[0], c.head_dim
-        y = rmsnorm(x, W["attn_norm"], c.rms_eps)
+        y = self._op(rmsnorm(x, W["attn_norm"], c.rms_eps))
         k = (y @ W["wk"].T).astype(np.float32).reshape(n, c.n_kv_head, hd)
         v = (y @ W["wv"].T).astype(np.float32).reshape(n, c.n_kv_head, hd)
         cos, sin = self.rope(int(np.max(positions)) + 1)
@@ -175,7 +215,11 @@ class OracleModel:
                       positions: np.ndarray) -> np.ndarray:
         """Attention of rows q32 against cache values K/V, then x + o W_o^T."""
         c, W = self.cfg, self.weights(l)
-        o = attention(q32, K, V, positions)
+        if self.f16:
+            T = int(np.max(positions)) + 1
+            o = to_f16(attention(to_f16(q32), to_f16(K[:T]), to_f16(V[:T]), positions, p_f16=True))
+        else:
+            o = attention(q32, K, V, positions)
         return np.asarray(x, np.float64) + o.reshape(x.shape[0], -1) @ W["wo"].T
 
     def ffn_rows(self, l: int, x: np.ndarray, return_routing: bool = False):
@@ -183,13 +227,13 @@ class OracleModel:
         c, W = self.cfg, self.weights(l)
         y = rmsnorm(x, W["ffn_norm"], c.rms_eps)
         if not c.n_expert:
-            out = x + swiglu_ffn(y, W["w_gate"], W["w_up"], W["w_down"])
+            out = x + swiglu_ffn(self._op(y), W["w_gate"], W["w_up"], W["w_down"], h_f16=self.f16)
             return (out, None) if return_routing else out
         nb = c.d_model // QK
         d16, q = q8_0_from_bytes(self.layers[l]["w_router"], nb)
         r = router_logits_ordered(y.astype(np.float32), d16, q)
         idx, w = moe_route(r, c.n_expert_used)
-        out = x + moe_ffn(y, idx, w, W["w_gate"], W["w_up"], W["w_down"])
+        out = x + moe_ffn(self._op(y), idx, w, W["w_gate"], W["w_up"], W["w_down"], h_f16=self.f16)
         return (out, (r, idx, w)) if return_routing else out
 
     def layer(self, l: int, x: np.ndarray, cache: OracleCache, start: int,

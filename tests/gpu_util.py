@@ -66,3 +66,28 @@ def run_prefill(torch, w, qlayers, x: np.ndarray, chunk: int, n_ctx: int = None,
     if trace:
         return (res, ctx, lo.cpu().numpy(), None if ro is None else ro.cpu().numpy())
     return res, ctx
+
+
+# A GPU expert set may differ from the oracle's only where the oracle's own k-th and
+# (k+1)-th router logits are closer than this fraction of max|r| (a near tie that the
+# 16-bit-level difference of the router input can flip).
+ROUTE_TIE = 1e-3
+
+
+def routing_agreement(r: np.ndarray, own: np.ndarray, got: np.ndarray, tie: float = ROUTE_TIE):
+    """Compare the GPU's expert sets `got` [T][k] with the oracle's `own` for the oracle's
+    logits r [T][E].  Asserts that every row whose set differs sits at a near tie of the
+    oracle's logits and that the GPU's set is still a top-k set there up to the same margin;
+    returns the boolean mask of rows whose sets agree."""
+    k = own.shape[1]
+    same = np.all(np.sort(own, 1) == np.sort(got, 1), axis=1)
+    tol = tie * float(np.max(np.abs(r)))
+    if not same.all():
+        srt = -np.sort(-np.asarray(r, np.float64), axis=1)
+        near = srt[:, k - 1] - srt[:, k] < tol if k < r.shape[1] else np.ones(len(r), bool)
+        mask = np.zeros(r.shape, bool)
+        np.put_along_axis(mask, got.astype(np.int64), True, axis=1)
+        gap = np.where(mask, -np.inf, r).max(axis=1) - np.where(mask, r, np.inf).min(axis=1)
+        assert np.all(near[~same]), "an expert set differs away from a near tie"
+        assert np.all(gap[~same] <= tol)
+    return same

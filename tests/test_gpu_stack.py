@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import log, need_gpu, rel_err, run_prefill
+from gpu_util import log, need_gpu, rel_err, routing_agreement, run_prefill
 from model_inputs import q8_layers
 
 pytestmark = pytest.mark.gpu
@@ -32,26 +32,23 @@ def route_gap(r: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return outside - inside
 
 
-def check_layers(w, qlayers, x, lo, ro, tol=TOL, route_tol=1e-2):
+def check_layers(w, qlayers, x, lo, ro, tol=TOL):
     """The GPU's output of every layer against the oracle's own layer-major run from the
     same seeded input (nothing the GPU produced is fed to the oracle).
 
-    Routed layers: the GPU's expert set of each token must be a top-k set of the oracle's
-    logits up to a 16-bit-level perturbation of the router input (route_tol * max|r|); the
-    hidden states are compared where both sides chose the same set, which the seeded
-    inputs here make every token.  Returns the oracle's final output."""
+    Routed layers: a GPU expert set may differ from the oracle's only at a near tie of the
+    oracle's logits (gap below 1e-3 * max|r|); the hidden states are compared where both
+    sides chose the same set, which the seeded inputs here make every token.  Returns the
+    oracle's final output."""
     m = oracle.OracleModel(w, qlayers)
     ref_lo, routing = [], []
     ref = m.prefill_layer_major(x, layer_outputs=ref_lo, routing_out=routing)
     for l in range(w.n_layer):
         if ro is not None:
             r, own, _ = routing[l]
-            gap = route_gap(r, ro[l])
-            tolr = route_tol * float(np.max(np.abs(r)))
-            same = np.all(np.sort(own, 1) == np.sort(ro[l], 1), axis=1)
+            same = routing_agreement(r, own, ro[l])
             log(f"  layer {l}: routing agreement {float(np.mean(same)):.5f}, "
-                f"worst top-k gap {gap.max():.3e} (tol {tolr:.3e})")
-            assert np.all(gap <= tolr)
+                f"worst top-k gap {route_gap(r, ro[l]).max():.3e}")
             assert np.all(same), "expert sets differ at a near tie: compare per token instead"
         e = rel_err(lo[l], ref_lo[l])
         log(f"  layer {l}: max rel err {e:.3e}")

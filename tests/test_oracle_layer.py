@@ -157,3 +157,62 @@ def test_cache_rows_f16_rne_and_q8_0():
     assert d16.shape == (3, 2, 2) and q.shape == (3, 2, 2, 32)
     back = oracle.cache_decode_rows((d16, q), "q8_0")
     assert back.shape == rows.shape and np.max(np.abs(back - rows)) < 0.02
+
+
+# ----------------------------------------------------------------------- fp16 operands
+
+def test_to_f16_round_to_nearest_even_and_saturation():
+    """binary16 has 10 fraction bits: the spacing at 1 is 2^-10, the largest finite value
+    is 65504, the smallest subnormal 2^-24; halfway cases go to the even neighbour."""
+    f = oracle.to_f16
+    assert f(1 + 2.0 ** -11) == 1.0                       # tie -> even (1.0)
+    assert f(1 + 3 * 2.0 ** -11) == 1 + 2.0 ** -9         # tie -> even (1 + 2 * 2^-10)
+    assert f(1 + 2.0 ** -11 + 2.0 ** -30) == 1 + 2.0 ** -10
+    assert f(-(1 + 2.0 ** -11 + 2.0 ** -30)) == -(1 + 2.0 ** -10)
+    assert f(65519.0) == 65504.0                          # below the overflow midpoint
+    with np.errstate(over="ignore"):
+        assert np.isinf(f(65520.0))                       # at it: rounds to infinity
+    assert f(1e6, saturate=True) == 65504.0 and f(-1e6, saturate=True) == -65504.0
+    assert f(2.0 ** -24) == 2.0 ** -24                    # smallest subnormal
+    assert f(2.0 ** -25) == 0.0                           # tie -> even (0)
+    assert f(3 * 2.0 ** -25) == 2.0 ** -23                # tie -> even (2 * 2^-24)
+    x = synth.normal(50, (4096,), scale=3.0).astype(np.float64)
+    r = f(x)
+    assert np.all(np.abs(r - x) <= np.abs(x) * 2.0 ** -11 + 2.0 ** -25)
+
+
+def test_attention_f16_weights_exact_at_powers_of_two_and_bounded_otherwise():
+    """p_f16 rounds exp(s - max) to binary16.  With scores at integer multiples of ln 2
+    the weights are powers of two (exact in binary16) and the result is the exact one; with
+    random scores it stays within binary16 rounding (2^-11 relative per weight) of it."""
+    n, hd = 6, 4
+    ks = np.array([0, -1, -3, -2, -5, -4, -7, -6, -1, -2], dtype=np.float64)[:n]
+    K = np.zeros((n, 1, hd))
+    K[:, 0, 0] = ks * math.log(2.0)
+    q = np.zeros((n, 1, hd))
+    q[:, 0, 0] = math.sqrt(hd)                            # s_j = q . K_j / sqrt(hd) = k_j ln 2
+    V = synth.normal(51, (n, 1, hd), scale=1.0).astype(np.float64)
+    pos = np.arange(n)
+    a = oracle.attention(q, K, V, pos)
+    b = oracle.attention(q, K, V, pos, p_f16=True)
+    assert np.allclose(a, b, rtol=0, atol=1e-13)
+    q = synth.normal(52, (9, 2, 8), scale=2.0).astype(np.float64)
+    K = synth.normal(53, (9, 2, 8), scale=2.0).astype(np.float64)
+    V = synth.normal(54, (9, 2, 8), scale=1.0).astype(np.float64)
+    pos = np.arange(9)
+    a = oracle.attention(q, K, V, pos)
+    b = oracle.attention(q, K, V, pos, p_f16=True)
+    bound = 2 * 2.0 ** -11 * np.max(np.abs(V))
+    assert 0 < np.max(np.abs(a - b)) <= bound
+
+
+def test_swiglu_f16_intermediate_saturates_and_rounds():
+    y = np.array([[1.0, 2.0]])
+    Wg = np.array([[100.0, 0.0], [1.0, 0.0]])             # gate: 100, 1
+    Wu = np.array([[0.0, 400.0], [0.0, 1.0 / 3.0]])       # up: 800, 2/3
+    Wd = np.eye(2)
+    h = oracle.swiglu_ffn(y, Wg, Wu, Wd, h_f16=True)
+    # silu(100) * 800 = 80000 (saturated to 65504); silu(1) * 2/3 rounded to binary16
+    s1 = 1.0 / (1.0 + math.exp(-1.0)) * (2.0 / 3.0)
+    assert h[0, 0] == 65504.0
+    assert h[0, 1] == float(np.float16(s1)) and h[0, 1] != s1

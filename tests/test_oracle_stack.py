@@ -178,3 +178,23 @@ def test_state_byte_order_at_explicit_offsets(kv):
                 assert np.array_equal(got, ref)
             else:
                 assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+@pytest.mark.parametrize("base", [TINY_DENSE, TINY_MOE])
+@pytest.mark.parametrize("kv", ["f16", "q8_0"])
+def test_f16_operand_mode_is_a_bounded_rounding_of_the_exact_mode(base, kv):
+    """The "f16" operand mode takes every matrix-product operand as binary16: its weights
+    are binary16 values, it differs from the exact mode by rounding-sized amounts (nonzero,
+    well inside 1e-2), and its chunked and layer-major drivers agree."""
+    w = base.with_(kv_type=kv)
+    ql = q8_layers(w)
+    x = synth.prompt_inputs(w)
+    exact = oracle.OracleModel(w, ql).prefill_layer_major(x)
+    m = oracle.OracleModel(w, ql, operands="f16")
+    f16 = m.prefill_layer_major(x)
+    e = rel(f16, exact)
+    assert 1e-7 < e < 1e-2, e
+    W = m.weights(0)
+    for name in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
+        assert np.array_equal(oracle.to_f16(W[name]), W[name])
+    assert rel(m.prefill(x, 7), f16) < 1e-3
