@@ -40,17 +40,20 @@ def quantize_layer(fp32_layer: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
     return out
 
 
-def _decode_matrix(b: np.ndarray, K: int, dtype, rows_per_block: int = 1024) -> np.ndarray:
-    """q8_0_decode_bytes of every row, converted to dtype.  Each row decodes on its own, so
-    the rows are split into blocks decoded by a thread pool (NumPy releases the GIL in
-    these loops); the values are those of one call over the whole matrix."""
+def _decode_matrix(b: np.ndarray, K: int, dtype, rows_per_block: int = 1024,
+                   f16: bool = False) -> np.ndarray:
+    """q8_0_decode_bytes of every row, converted to dtype (f16: each value rounded to
+    binary16 first).  Each row decodes on its own, so the rows are split into blocks
+    decoded by a thread pool (NumPy releases the GIL in these loops); the values are those
+    of one call over the whole matrix."""
     from concurrent.futures import ThreadPoolExecutor
     import os
     flat = b.reshape(-1, b.shape[-1])
     out = np.empty((flat.shape[0], K), dtype=dtype)
 
     def work(s):
-        out[s:s + rows_per_block] = q8_0_decode_bytes(flat[s:s + rows_per_block], K)
+        blk = q8_0_decode_bytes(flat[s:s + rows_per_block], K)
+        out[s:s + rows_per_block] = to_f16(blk) if f16 else blk
 
     starts = range(0, flat.shape[0], rows_per_block)
     with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
@@ -59,12 +62,13 @@ def _decode_matrix(b: np.ndarray, K: int, dtype, rows_per_block: int = 1024) -> 
 
 
 def dequant_layer(qlayer: Dict[str, np.ndarray], K_of: Dict[str, int],
-                  dtype=np.float64) -> Dict[str, np.ndarray]:
-    """Interchange bytes -> dense matrices (float64 by default); gains passed through."""
+                  dtype=np.float64, f16_names=()) -> Dict[str, np.ndarray]:
+    """Interchange bytes -> dense matrices (float64 by default); gains passed through.
+    Matrices named in f16_names have every value rounded to binary16."""
     out = {}
     for name, t in qlayer.items():
         if name in MATRIX_NAMES:
-            out[name] = _decode_matrix(t, K_of[name], dtype)
+            out[name] = _decode_matrix(t, K_of[name], dtype, f16=name in f16_names)
         else:
             out[name] = np.asarray(t, dtype=dtype)
     return out
@@ -163,11 +167,8 @@ class OracleModel:
         if l not in self._deq:
             if len(self._deq) >= self.keep:
                 self._deq.pop(next(iter(self._deq)))
-            W = dequant_layer(self.layers[l], self.K_of)
-            if self.f16:
-                for name in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
-                    W[name] = to_f16(W[name])
-            self._deq[l] = W
+            f16_names = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down") if self.f16 else ()
+            self._deq[l] = dequant_layer(self.layers[l], self.K_of, f16_names=f16_names)
         return self._deq[l]
 
     def _op(self, a: np.ndarray) -> np.ndarray:
