@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -33,6 +34,9 @@ struct Dims {
 };
 
 int64_t round_up(int64_t v, int64_t g) { return (v + g - 1) / g * g; }
+
+// Size of the static scratch array that prefill_chunk_static takes a chunk's buffers from.
+constexpr size_t kStaticScratchBytes = (size_t)256 << 20;
 
 std::string validate(const cp_config* c) {
   if (!c) return "config is NULL";
@@ -433,6 +437,9 @@ struct cp_ctx {
   uint8_t* warena = nullptr;
   uint8_t* kv = nullptr;
   uint8_t* ws = nullptr;
+  uint8_t* stage = nullptr;     // the per-chunk buffers (offsets WS.stage on): ws + WS.stage,
+                                // or this device's static array during prefill_chunk_static
+  int device = 0;               // the device current at prefill_init
   std::vector<LayerW> layers;
   int32_t n_past = 0;
   std::string err;
@@ -444,7 +451,9 @@ struct cp_ctx {
   std::vector<hipEvent_t> pool;
   std::map<std::string, std::pair<double, int>> totals;
 
-  template <typename T> T* wsp(size_t off) { return reinterpret_cast<T*>(ws + off); }
+  template <typename T> T* wsp(size_t off) {
+    return reinterpret_cast<T*>(off >= WS.stage ? stage + (off - WS.stage) : ws + off);
+  }
 
   hipEvent_t ev() {
     if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
@@ -612,7 +621,78 @@ int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int sta
   return CP_OK;
 }
 
+// All layers of one checked chunk at positions n_past .. n_past+n-1; advances n_past.
+int run_chunk(cp_ctx* c, const float* x_in, float* x_out, int n) {
+  const int start = c->n_past;
+  c->pend_x = PendingSum();
+  for (int l = 0; l < c->D.L; ++l) {
+    const int r = run_layer(c, l, l == 0 ? x_in : x_out, x_out, n, start, l == c->D.L - 1);
+    if (r != CP_OK) return r;
+  }
+  c->n_past = start + n;
+  return CP_OK;
+}
+
+// The workspace layout of a chunk of exactly n tokens whose per-chunk part (offsets from
+// WS.stage on) must fit kStaticScratchBytes.  The RoPE tables before it keep their offsets
+// (they depend on n_ctx only).  If the split-KV partial rows do not fit, they are dropped:
+// attention then runs unsplit (same result to rounding, no partials).  False when even
+// that does not fit.
+bool static_stage_layout(const Dims& D0, int n, WsLayout* out) {
+  Dims D = D0;
+  D.Cm = n;
+  WsLayout L = workspace_layout(D);
+  if (L.total - L.stage > kStaticScratchBytes && L.arows) {
+    L.total = L.apo;
+    L.arows = 0;
+    L.apo = L.apml = 0;
+  }
+  if (L.total - L.stage > kStaticScratchBytes) return false;
+  *out = L;
+  return true;
+}
+
 bool aligned(const void* p) { return ((uintptr_t)p % kAlign) == 0; }
+
+}  // namespace
+
+// --------------------------------------------------------------------------------------
+// The static scratch array of prefill_chunk_static: one copy per device, which that device
+// holds from the library's load until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device address): it looks
+// the device address up once per device with hipGetSymbolAddress and uses that.
+// --------------------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// This device's address of `scratch`, looked up on the first call for the device with
+// that device current (then restored), and kept.
+hipError_t static_scratch(int device, uint8_t** out) {
+  static std::mutex mu;
+  static uint8_t* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != device) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p || (uintptr_t)p % kAlign) return hipErrorInvalidSymbol;
+    addr[device] = static_cast<uint8_t*>(p);
+  }
+  *out = addr[device];
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -680,10 +760,12 @@ int prefill_init(const cp_config* cfg, const cp_layer_weights* layers, void* wei
   c->warena = (uint8_t*)weights_arena;
   c->kv = (uint8_t*)kv_buf;
   c->ws = (uint8_t*)workspace;
+  c->stage = c->ws + c->WS.stage;
   const Dims& D = c->D;
+  auto bail = [&](int code) { delete c; return code; };
+  if (hipGetDevice(&c->device) != hipSuccess) return bail(CP_E_DEVICE);
   const WLayout& W = c->WL;
   hipStream_t s = c->stream;
-  auto bail = [&](int code) { delete c; return code; };
   for (int l = 0; l < D.L; ++l) {
     const cp_layer_weights& src = layers[l];
     if (!src.wq || !src.wk || !src.wv || !src.wo || !src.attn_norm || !src.ffn_norm || !src.w_gate ||
@@ -766,14 +848,27 @@ int prefill_init(const cp_config* cfg, const cp_layer_weights* layers, void* wei
 int prefill_chunk(cp_ctx* c, const float* x_in, float* x_out, int32_t n) {
   if (!c) return CP_E_INVALID;
   if (const int r = chunk_check(&c->cfg, c->n_past, x_in, x_out, n, c->err); r != CP_OK) return r;
-  const int start = c->n_past;
-  c->pend_x = PendingSum();
-  for (int l = 0; l < c->D.L; ++l) {
-    const int r = run_layer(c, l, l == 0 ? x_in : x_out, x_out, n, start, l == c->D.L - 1);
-    if (r != CP_OK) return r;
-  }
-  c->n_past = start + n;
-  return CP_OK;
+  return run_chunk(c, x_in, x_out, n);
+}
+
+int prefill_chunk_static(cp_ctx* c, const float* x_in, float* x_out, int32_t n) {
+  if (!c) return CP_E_INVALID;
+  if (const int r = chunk_check(&c->cfg, c->n_past, x_in, x_out, n, c->err); r != CP_OK) return r;
+  WsLayout L;
+  if (!static_stage_layout(c->D, n, &L))
+    return fail(c, CP_E_CAPACITY, "the chunk's buffers exceed the static scratch array (" +
+                                      std::to_string(kStaticScratchBytes >> 20) + " MiB)");
+  uint8_t* base = nullptr;
+  const hipError_t e = static_scratch(c->device, &base);
+  if (e != hipSuccess) return hip_fail(c, e, "static scratch address");
+  // the chunk's buffers are taken from the static array for this call only
+  struct Swap {
+    cp_ctx* c; WsLayout ws; uint8_t* stage;
+    ~Swap() { c->WS = ws; c->stage = stage; }
+  } restore{c, c->WS, c->stage};
+  c->WS = L;
+  c->stage = base;
+  return run_chunk(c, x_in, x_out, n);
 }
 
 int prefill_chunk_trace(cp_ctx* c, const float* x_in, float* x_out, int32_t n, float* layer_out,
@@ -1032,12 +1127,12 @@ size_t cp_test_router_scratch_bytes(int32_t n_expert, int32_t d) {
 }
 
 int cp_test_router(const float* y, const void* w_router, int32_t n, int32_t d, int32_t E, int32_t k,
-                   float* logits, int32_t* idx, float* weight, void* scratch, void* stream) {
-  if (!y || !w_router || !logits || !idx || !weight || !scratch || n < 1 || d < 32 || d % 32 ||
+                   float* logits, int32_t* idx, float* weight, void* work, void* stream) {
+  if (!y || !w_router || !logits || !idx || !weight || !work || n < 1 || d < 32 || d % 32 ||
       E < 1 || E > 256 || k < 1 || k > E || k > 16)
     return CP_E_INVALID;
-  int8_t* q = (int8_t*)scratch;
-  uint16_t* dd = (uint16_t*)((uint8_t*)scratch + align_up((size_t)E * d));
+  int8_t* q = (int8_t*)work;
+  uint16_t* dd = (uint16_t*)((uint8_t*)work + align_up((size_t)E * d));
   hipStream_t s = (hipStream_t)stream;
   if (launch_unpack_router(w_router, E, d, q, dd, s) != hipSuccess) return CP_E_DEVICE;
   return launch_router(y, q, dd, n, d, E, k, logits, idx, weight, s) == hipSuccess ? CP_OK : CP_E_DEVICE;
@@ -1060,16 +1155,16 @@ size_t cp_test_gemm_scratch_bytes(int32_t M, int32_t N, int32_t K, int32_t split
 }
 
 int cp_test_gemm_ex(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
-                    int32_t splits, int32_t row_tile, void* out, void* scratch, void* stream) {
-  if (!A || !W || !out || !scratch || M < 1 || N < 32 || N % 32 || K < 128 || K % 128 || mode < 0 ||
+                    int32_t splits, int32_t row_tile, void* out, void* work, void* stream) {
+  if (!A || !W || !out || !work || M < 1 || N < 32 || N % 32 || K < 128 || K % 128 || mode < 0 ||
       mode > 2 || splits < 0)
     return CP_E_INVALID;
   if (!test_row_tile_ok(M, N, row_tile)) return CP_E_INVALID;
   if (mode == GM_SWIGLU && N % 64) return CP_E_INVALID;
   hipStream_t s = (hipStream_t)stream;
   QMat q;
-  q.q = (int8_t*)scratch;
-  q.d = (uint32_t*)((uint8_t*)scratch + align_up(QMat::q_bytes(N, K)));
+  q.q = (int8_t*)work;
+  q.d = (uint32_t*)((uint8_t*)work + align_up(QMat::q_bytes(N, K)));
   q.N = N; q.K = K;
   float* partial = (float*)((uint8_t*)q.d + align_up(QMat::d_bytes(N, K)));
   const GemmPlan p = plan_gemm(M, N, K, splits, row_tile);
@@ -1095,8 +1190,8 @@ int cp_test_gemm_ex(const void* A, const void* W, int32_t M, int32_t N, int32_t 
 }
 
 int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
-                 int32_t splits, void* out, void* scratch, void* stream) {
-  return cp_test_gemm_ex(A, W, M, N, K, mode, splits, 0, out, scratch, stream);
+                 int32_t splits, void* out, void* work, void* stream) {
+  return cp_test_gemm_ex(A, W, M, N, K, mode, splits, 0, out, work, stream);
 }
 
 int cp_test_gemm_plan(int32_t M, int32_t N, int32_t K, int32_t* out6) {
@@ -1117,8 +1212,8 @@ size_t cp_test_attention_scratch_bytes(int32_t n, int32_t n_head, int32_t head_d
 
 int cp_test_attention(const void* q, const void* kv, int32_t n, int32_t start, int32_t n_head,
                       int32_t n_kv_head, int32_t head_dim, int32_t kv_type, int32_t n_ctx,
-                      int32_t kv_splits, void* out, void* scratch, void* stream) {
-  if (!q || !kv || !out || !scratch || n < 1 || start < 0 || start + n > n_ctx) return CP_E_INVALID;
+                      int32_t kv_splits, void* out, void* work, void* stream) {
+  if (!q || !kv || !out || !work || n < 1 || start < 0 || start + n > n_ctx) return CP_E_INVALID;
   if ((head_dim != 64 && head_dim != 128) || n_kv_head < 1 || n_head % n_kv_head || kv_splits < 0 || kv_splits > 32)
     return CP_E_INVALID;
   Dims D{};
@@ -1130,8 +1225,8 @@ int cp_test_attention(const void* q, const void* kv, int32_t n, int32_t start, i
   a.n = n; a.start = start; a.n_head = n_head; a.n_kv_head = n_kv_head; a.head_dim = head_dim;
   a.kv_type = kv_type; a.n_ctx = nc; a.out = (_Float16*)out;
   a.splits = kv_splits > 0 ? kv_splits : attn_splits(D, n, start);
-  a.part_o = (float*)scratch;
-  a.part_ml = (float*)((uint8_t*)scratch + align_up((size_t)a.splits * n * n_head * head_dim * 4));
+  a.part_o = (float*)work;
+  a.part_ml = (float*)((uint8_t*)work + align_up((size_t)a.splits * n * n_head * head_dim * 4));
   return launch_attention(a, (hipStream_t)stream) == hipSuccess ? CP_OK : CP_E_DEVICE;
 }
 

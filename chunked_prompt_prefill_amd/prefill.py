@@ -94,6 +94,12 @@ class PrefillContext:
         self._check(self.L.prefill_chunk(self._ctx, ptr(x_in), ptr(x_out), x_in.shape[0]))
         return x_out
 
+    def prefill_chunk_static(self, x_in: torch.Tensor, x_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """prefill_chunk with the chunk's buffers in the library's static device array."""
+        x_out = torch.empty_like(x_in) if x_out is None else x_out
+        self._check(self.L.prefill_chunk_static(self._ctx, ptr(x_in), ptr(x_out), x_in.shape[0]))
+        return x_out
+
     def prefill_chunk_trace(self, x_in: torch.Tensor, x_out: torch.Tensor, layer_out=None,
                             layer_stride: int = 0, route_idx=None, route_stride: int = 0):
         """layer_out / route_idx: device tensors (or None); strides in elements."""

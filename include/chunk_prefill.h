@@ -132,6 +132,27 @@ int prefill_init(const cp_config* cfg, const cp_layer_weights* layers, void* wei
  * enqueued).  Returns once the work is enqueued; n_past advances by n_tokens. */
 int prefill_chunk(cp_ctx* ctx, const float* x_in, float* x_out, int32_t n_tokens);
 
+/* prefill_chunk for callers that cannot allocate device memory at the call (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * chunk's per-chunk buffers (normed rows, projections, attention output, FFN
+ * intermediate, split-K and split-KV partial sums, routing tables) are taken from a
+ * static device array of 256 MiB inside the library instead of the context's workspace,
+ * whose RoPE tables are still read.  Same arguments, checks, kernels and result as
+ * prefill_chunk (bitwise, whenever the chunk's split-KV partials fit beside the other
+ * buffers; else attention runs unsplit, the same to rounding).  Allocates nothing: no
+ * hipMalloc, hipFree or allocating library call.
+ *   - The array holds the buffers of one chunk of exactly n_tokens rows; a chunk whose
+ *     buffers exceed 256 MiB (e.g. more than about 600 rows at d_model 5120, FFN 17408)
+ *     is rejected with CP_E_CAPACITY before anything is enqueued, and the context is
+ *     unchanged (prefill_last_error says why).
+ *   - One array per device, held from the library's load until the process ends.  Every
+ *     call on a device shares it, and it keeps the last call's contents (nothing in it
+ *     needs to start at zero): calls that overlap on one device (two streams, or two
+ *     host threads) race and give wrong results.  Serialise them.
+ *   - The device is the one current at prefill_init.
+ * Returns as prefill_chunk, and CP_E_DEVICE if the array's address cannot be found. */
+int prefill_chunk_static(cp_ctx* ctx, const float* x_in, float* x_out, int32_t n_tokens);
+
 /* Same as prefill_chunk, then synchronises and writes the time of each layer (ms,
  * hipEvents recorded on the stream at every layer boundary) to host layer_ms[n_layer].
  * This is the per-layer t(C, D) the b + a*C cost model is fitted to ("Prompt chunks
