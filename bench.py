@@ -100,12 +100,13 @@ def gpu_layers(w, torch, cpa, synth):
 def dominant_work(w, cpa, chunks):
     """Algorithmic work of the dominant kernel's launches in one pass over `chunks`.
 
-    Dense: the unsplit column range of the SwiGLU gate/up GEMM (the layer's launch plan,
-    cp_test_gemm_plan).  Per launch of M rows over columns [n0, n1) of W_gate|W_up with
-    K = d_model: flops 2*M*(n1-n0)*K; bytes = q8_0 weights (n1-n0)*K*34/32 + A rows
-    M*K*2 (fp16) + h written M*(n1-n0)/2*2 (fp16).  Routed experts: the grouped gate/up
-    GEMM over the C*k token-slots, flops 2*C*k*2*Fe*d, bytes = every expert's gate/up
-    weights + the gathered A rows + h.
+    Dense: the SwiGLU gate/up GEMM of a chunk-layer as one operation: every column range
+    of its launch plan, split or not, and the split-K reduction (the library's
+    "gemm_gate_up" timing class brackets all of them with one pair of events).  Per chunk
+    of M rows, N = 2 * FFN (padded to 128) columns of W_gate|W_up, K = d_model: flops
+    2*M*N*K; bytes = q8_0 weights N*K*34/32 + A rows M*K*2 (fp16) + h written M*N/2*2.
+    Routed experts: the grouped gate/up GEMM over the C*k token-slots, flops 2*C*k*2*Fe*d,
+    bytes = every expert's gate/up weights + the gathered A rows + h.
     Returns (flops, bytes, per-launch figures of the full-size chunk)."""
     flops = bytes_ = 0.0
     launches = 0
@@ -116,26 +117,16 @@ def dominant_work(w, cpa, chunks):
             Fe = w.expert_ffn_dim
             f = 2.0 * M * w.n_expert_used * 2 * Fe * w.d_model
             b = w.n_expert * 2 * Fe * w.d_model * 34 / 32 + M * w.n_expert_used * (w.d_model + Fe) * 2
-            flops += f
-            bytes_ += b
-            launches += 1
-            if first is None:
-                first = {"flops": f, "bytes": b, "rows": M}
-            continue
-        N = 2 * (-(-w.ffn_dim // 128) * 128)
-        K = w.d_model
-        _, parts = cpa.cp_test_gemm_plan(M, N, K)
-        for i, (n0, splits) in enumerate(parts):
-            n1 = parts[i + 1][0] if i + 1 < len(parts) else N
-            if splits > 1:
-                continue
-            f = 2.0 * M * (n1 - n0) * K
-            b = (n1 - n0) * K * 34 / 32 + M * K * 2 + M * (n1 - n0) // 2 * 2
-            flops += f
-            bytes_ += b
-            launches += 1
-            if first is None:
-                first = {"flops": f, "bytes": b, "rows": M}
+        else:
+            N = 2 * (-(-w.ffn_dim // 128) * 128)
+            K = w.d_model
+            f = 2.0 * M * N * K
+            b = N * K * 34 / 32 + M * K * 2 + M * N // 2 * 2
+        flops += f
+        bytes_ += b
+        launches += 1
+        if first is None:
+            first = {"flops": f, "bytes": b, "rows": M}
     first = dict(first or {"flops": 0.0, "bytes": 0.0, "rows": 0})
     first["launches"] = launches
     return flops, bytes_, first
@@ -167,39 +158,45 @@ def measured_traffic(kernel, per_launch):
 # sources whose text defines the dominant kernel's code: a change to any of them makes the
 # stored counter readings stale (measured_traffic then reports None)
 PMC_SOURCES = ["chunked_prompt_prefill_amd/csrc/k_gemm_big.hip",
+               "chunked_prompt_prefill_amd/csrc/k_gemm.hip",
                "chunked_prompt_prefill_amd/csrc/k_common.h",
-               "chunked_prompt_prefill_amd/csrc/cp_internal.h"]
+               "chunked_prompt_prefill_amd/csrc/cp_internal.h",
+               "chunked_prompt_prefill_amd/csrc/cp_api.cpp"]
 
 
 def pmc_digest(fetch_csv, write_csv, copy_mib):
     """Fold two rocprofv3 --pmc counter files of the --pmc-probe run (FETCH_SIZE, then
-    WRITE_SIZE) into profiles/pmc_traffic.json: the unsplit gate/up launch's readings,
-    each scaled by what the same counter reads for the plain copy of copy_mib MiB that the
-    probe runs first (the copy reads and writes exactly that many bytes)."""
+    WRITE_SIZE; 512-token chunk) into profiles/pmc_traffic.json: the readings of the
+    gate/up GEMM's dispatches (its unsplit launch, then, when the plan has a split-K
+    column tail, the tail's launch and its reduction, in dispatch order), each scaled by
+    what the same counter reads for the plain copy of copy_mib MiB that the probe runs
+    first (the copy reads and writes exactly that many bytes)."""
     import csv
     import hashlib
+    import chunked_prompt_prefill_amd as cpa
+    _, parts = cpa.cp_test_gemm_plan(512, 34816, 5120)
+    n_disp = len(parts) + (1 if any(sp > 1 for _, sp in parts) else 0)
 
-    def readings(path, grid_wg):
+    def readings(path):
         with open(path) as f:
-            rows = list(csv.DictReader(f))
+            rows = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
         copy = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")]
-        k = [float(r["Counter_Value"]) for r in rows
-             if "gemm_q8_big_kernel<2, false>" in r["Kernel_Name"]
-             and int(r["Grid_Size"]) // int(r["Workgroup_Size"]) == grid_wg]
-        if not copy or len(k) != 1:
-            raise SystemExit(f"{path}: expected the copy and one unsplit gate/up launch, got {len(copy)} / {len(k)}")
-        return copy[0], k[0]
+        first = [i for i, r in enumerate(rows) if "gemm_q8_big_kernel<2, false>" in r["Kernel_Name"]]
+        if not copy or len(first) != 1:
+            raise SystemExit(f"{path}: expected the copy and one unsplit gate/up launch, got {len(copy)} / {len(first)}")
+        op = rows[first[0]:first[0] + n_disp]
+        return copy[0], sum(float(r["Counter_Value"]) for r in op), [r["Kernel_Name"].split("(")[0] for r in op]
 
-    cf, kf = readings(fetch_csv, 256)
-    cw, kw = readings(write_csv, 256)
+    cf, kf, names = readings(fetch_csv)
+    cw, kw, _ = readings(write_csv)
     probe_kib = copy_mib * 1024
     ff, fw = probe_kib / cf, probe_kib / cw
     h = hashlib.sha256()
     for src in PMC_SOURCES:
         with open(os.path.join(ROOT, src), "rb") as f:
             h.update(f.read())
-    rec = {"gemm_gate_up/full": {
-        "kernel": "gemm_q8_big_kernel<GM_SWIGLU> (256 workgroups, 256x256 tiles)",
+    rec = {"gemm_gate_up": {
+        "kernel": "the gate/up GEMM of a 512-token chunk-layer: " + " + ".join(names),
         "rows": 512, "fetch_size_kib": kf, "write_size_kib": kw,
         "copy_probe_bytes": probe_kib * 1024, "copy_fetch_size_kib": cf, "copy_write_size_kib": cw,
         "fetch_factor": ff, "write_factor": fw,
@@ -236,9 +233,9 @@ def run_main(args, torch, cpa, synth):
         step()
         torch.cuda.synchronize()
         note(f"warmup step {i + 1}/{args.warmup} done")
-    # dominant kernel: the unsplit SwiGLU gate/up launch (one kernel per launch), or the
-    # grouped expert gate/up GEMM of a routed FFN
-    dom = "moe_gemm_gate_up" if w.n_expert else "gemm_gate_up/full"
+    # dominant kernel: the SwiGLU gate/up GEMM of each chunk-layer as a whole (all of its
+    # launches and the reduction), or the grouped expert gate/up GEMM of a routed FFN
+    dom = "moe_gemm_gate_up" if w.n_expert else "gemm_gate_up"
     ctx.cp_kernel_timing(dom)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -324,7 +321,7 @@ def run_main(args, torch, cpa, synth):
     return w, res
 
 
-def run_config(name, torch, cpa, synth, steps=1, warmup=1):
+def run_config(name, torch, cpa, synth, steps=1, warmup=1, attention_roofline=False):
     """Whole-prompt prefill rate of another workload (chunks of its own size from an empty
     cache), with its roofline fraction: the sum over chunk-layers of max(flops / MFMA peak,
     bytes / HBM peak) against the measured time.  Same seeded synthetic weights and inputs."""
@@ -359,13 +356,31 @@ def run_config(name, torch, cpa, synth, steps=1, warmup=1):
     dt = (time.perf_counter() - t0) / steps
     bound = sum(roofline_s(w, e - s, s) for s, e in chunks) * w.n_layer
     flops = sum(chunk_flops(w, e - s, s) for s, e in chunks) * w.n_layer
+    res = {"workload": w.name, "n_layer": w.n_layer, "prompt_tokens": n, "chunk": C,
+           "kv_type": w.kv_type, "tokens_per_s": n / dt, "ms_per_prompt": dt * 1e3,
+           "algorithmic_tflop_per_s": flops / dt / 1e12,
+           "roofline_bound_ms": bound * 1e3, "roofline_frac": bound / dt}
+    if attention_roofline:
+        # one more step with HIP events around every attention launch (the kernel and, for
+        # split KV, its merge) on the library's stream; algorithmic flops of the unmasked
+        # causal part, 4*Hq*hd*(C*D + C(C+1)/2) per chunk-layer
+        ctx.cp_kernel_timing("attention")
+        step()
+        ms, launches = ctx.cp_kernel_times("attention")
+        ctx.cp_kernel_timing(None)
+        af = sum(4.0 * w.n_head * w.head_dim * ((e - s) * s + (e - s) * (e - s + 1) / 2)
+                 for s, e in chunks) * w.n_layer
+        ach = af / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+        res["roofline"] = {"bound": "mfma", "kernel": f"attention ({w.kv_type} cache)",
+                           "achieved": ach, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": ach / PEAK_F16_TFLOPS, "traffic": None, "launches": launches,
+                           "avg_launch_us": ms * 1e3 / max(1, launches),
+                           "flops_per_launch": af / max(1, launches),
+                           "share_of_step": ms * 1e-3 / dt}
     ctx.close()
     del x, out
     torch.cuda.empty_cache()
-    return {"workload": w.name, "n_layer": w.n_layer, "prompt_tokens": n, "chunk": C,
-            "kv_type": w.kv_type, "tokens_per_s": n / dt, "ms_per_prompt": dt * 1e3,
-            "algorithmic_tflop_per_s": flops / dt / 1e12,
-            "roofline_bound_ms": bound * 1e3, "roofline_frac": bound / dt}
+    return res
 
 
 def run_pmc_probe(args, torch, cpa, synth):
@@ -453,10 +468,12 @@ def run_sweep(args, torch, cpa, synth, oracle_fit):
 
 
 def run_cpu_baseline(args, w):
-    """The oracle as it stands, on a bounded sample: one layer of the workload's shapes over
-    the first `cpu_tokens` prompt tokens (layer-major from an empty cache), weights
-    dequantised inside the timed region.  Scaled to the whole share: tokens/s =
-    tokens / (n_layer * seconds per layer)."""
+    """The oracle as it stands, on a bounded sample: one of the share's layers over the whole
+    prompt (layer-major from an empty cache, so every attention depth of the prompt is in
+    the sample), weights dequantised inside the timed region.  The layers of a share have
+    identical shapes and cost, so the share's rate is tokens / (n_layer * seconds per
+    layer).  --cpu-tokens N limits the prompt to its first N tokens instead (attention at
+    depth is then under-represented and the rate overstated)."""
     import numpy as np
     import oracle
     import synth
@@ -465,7 +482,7 @@ def run_cpu_baseline(args, w):
         blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
     except Exception:
         blas = []
-    n = min(args.cpu_tokens, w.n_prompt)
+    n = min(args.cpu_tokens, w.n_prompt) if args.cpu_tokens > 0 else w.n_prompt
     one = w.with_(n_layer=1)
     note(f"cpu baseline: generating one {w.d_model}-wide layer and {n} input rows")
     fp = {name: synth.layer_weight(one, 0, name, shape) for name, shape in synth.weight_shapes(one)}
@@ -478,9 +495,11 @@ def run_cpu_baseline(args, w):
     dt = time.perf_counter() - t0
     threads = max([t for _, t in blas if t] or [os.cpu_count() or 1])
     note(f"cpu baseline: {dt:.1f}s for one layer x {n} tokens")
+    what = "the whole prompt" if n == w.n_prompt else f"the first {n} prompt tokens"
     return {"value": n / (w.n_layer * dt), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"1 of {w.n_layer} layers, first {n} prompt tokens, float64 NumPy, "
-                      f"weights dequantised in the timed region ({dt:.2f} s)",
+            "sample": f"1 of the {w.n_layer} identical layers over {what} ({n} tokens, every "
+                      f"attention depth), float64 NumPy, weights dequantised in the timed region "
+                      f"({dt:.2f} s); rate = tokens / ({w.n_layer} x that time)",
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
             "blas": blas}
 
@@ -496,7 +515,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the whole-prompt rates of the other workloads")
     ap.add_argument("--sweep-reps", type=int, default=5)
-    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="CPU baseline over the first N prompt tokens (0: the whole prompt)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for rocprofv3 --pmc: the copy probe, then one chunk of the workload's "
                          "chunk size through one of its layers (no timing events), and exit")
@@ -545,7 +565,9 @@ def main():
     configs = []
     if not args.no_configs:
         for name in ("tiny_dense", "dense27b_q8", "moe_a3b"):
-            configs.append(run_config(name, torch, cpa, synth))
+            # the 58,300-token q8_0-cache share is the largest that fits one GPU; its
+            # dominant kernel is attention over the q8_0 cache
+            configs.append(run_config(name, torch, cpa, synth, attention_roofline=name != "tiny_dense"))
     sweep = None
     if not args.no_sweep:
         sweep = run_sweep(args, torch, cpa, synth, fit_linear)
@@ -569,6 +591,9 @@ def main():
         "measured_peaks": {"mfma_f16_tflops": mf_tflops, "hbm_read_gbs": hbm_gbs,
                            "published": {"mfma_f16_tflops": PEAK_F16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}},
         "cpu_baseline": cpu,
+        "sweep_mfma_frac_chunks_ge_1024": None if sweep is None else {
+            str(D): [round(p["mfma_frac"], 3) for p in sweep["points"] if p["depth"] == D and p["chunk"] >= 1024]
+            for D in sorted({p["depth"] for p in sweep["points"]})},
         "configs": configs,
         "sweep": sweep,
     }
