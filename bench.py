@@ -214,40 +214,63 @@ def run_main(args, torch, cpa, synth):
     note(f"workload {w.name}: {w.n_layer} layers, {n} tokens in {C}-token chunks, {w.kv_type} cache")
     t = time.time()
     layers = gpu_layers(w, torch, cpa, synth)
-    ctx = cpa.PrefillContext(cpa.make_config(w, n + DECODE_ROOM, C), layers)
+    # the context's own stream (not the default one, which would serialise with the
+    # second lane's stream) and a second stream for prefill_chunks
+    ctx = cpa.PrefillContext(cpa.make_config(w, n + DECODE_ROOM, C), layers, stream=torch.cuda.Stream())
     del layers
     torch.cuda.empty_cache()
     x = synth.prompt_inputs(w, backend="torch", device="cuda")
     out = torch.empty_like(x)
+    torch.cuda.synchronize()          # inputs are read on the context's own streams
     note(f"weights generated, encoded and repacked in {time.time() - t:.1f}s")
     chunks = [(s, min(n, s + C)) for s in range(0, n, C)]
 
     def step():
+        # the whole prompt in chunks of C, two chunks in flight on two streams
+        ctx.kv_cache_truncate(0)
+        rc = ctx.prefill_chunks_raw(x.data_ptr(), out.data_ptr(), n, C)
+        if rc != 0:
+            raise RuntimeError(f"prefill_chunks failed: {rc} {ctx.last_error()}")
+
+    def step_one_lane():
+        # the same chunks one after another through prefill_chunk
         ctx.kv_cache_truncate(0)
         for s, e in chunks:
             rc = ctx.prefill_chunk_raw(x[s:e].data_ptr(), out[s:e].data_ptr(), e - s)
             if rc != 0:
                 raise RuntimeError(f"prefill_chunk failed: {rc} {ctx.last_error()}")
 
+    run_step = step if args.lanes == 2 else step_one_lane
     for i in range(args.warmup):
-        step()
+        run_step()
         torch.cuda.synchronize()
         note(f"warmup step {i + 1}/{args.warmup} done")
-    # dominant kernel: the SwiGLU gate/up GEMM of each chunk-layer as a whole (all of its
-    # launches and the reduction), or the grouped expert gate/up GEMM of a routed FFN
-    dom = "moe_gemm_gate_up" if w.n_expert else "gemm_gate_up"
-    ctx.cp_kernel_timing(dom)
+    # headline: K steps, two chunks in flight (prefill_chunks) unless --lanes 1
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step()
+        run_step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    dom_ms, dom_launches = ctx.cp_kernel_times(dom)
-    ctx.cp_kernel_timing(None)
-    note(f"timed {args.steps} steps in {t1 - t0:.3f}s")
+    note(f"timed {args.steps} steps in {t1 - t0:.3f}s ({args.lanes} lane(s))")
     total = t1 - t0
     tps = n * args.steps / total
+    # the dominant kernel's roofline, timed by HIP events around its launches over K more
+    # steps on one lane, where each launch has the device to itself: the SwiGLU gate/up GEMM
+    # of each chunk-layer as a whole (all of its launches and the reduction), or the
+    # grouped expert gate/up GEMM of a routed FFN
+    dom = "moe_gemm_gate_up" if w.n_expert else "gemm_gate_up"
+    step_one_lane()
+    ctx.cp_kernel_timing(dom)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        step_one_lane()
+    torch.cuda.synchronize()
+    one_lane = n * args.steps / (time.perf_counter() - t2)
+    dom_ms, dom_launches = ctx.cp_kernel_times(dom)
+    ctx.cp_kernel_timing(None)
+    note(f"one lane: {one_lane:.0f} tokens/s (with events around the {dom} launches)")
     # roofline of the dominant kernel: algorithmic flops of every timed launch
     dom_flops, dom_bytes, per_launch = dominant_work(w, cpa, chunks)
     dom_flops *= w.n_layer * args.steps
@@ -303,7 +326,8 @@ def run_main(args, torch, cpa, synth):
     res = {
         "value": tps,
         "ms_per_step": total / args.steps * 1e3,
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": dom, "timed_on": "one lane (each launch alone)",
+                     "achieved": achieved,
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_F16_TFLOPS,
                      "traffic": measured_traffic(dom, per_launch),
@@ -312,6 +336,7 @@ def run_main(args, torch, cpa, synth):
                      "algorithmic_bytes_per_launch": per_launch["bytes"]},
         "prompt_roofline": {"bound_ms_per_step": bound * 1e3,
                             "frac": bound / (total / args.steps)},
+        "one_lane_tokens_per_s": one_lane,
         "decode_regime": decode,
         "last_logits": last_logits,
     }
@@ -321,7 +346,7 @@ def run_main(args, torch, cpa, synth):
     return w, res
 
 
-def run_config(name, torch, cpa, synth, steps=1, warmup=1, attention_roofline=False):
+def run_config(name, torch, cpa, synth, steps=1, warmup=1, attention_roofline=False, lanes=2):
     """Whole-prompt prefill rate of another workload (chunks of its own size from an empty
     cache), with its roofline fraction: the sum over chunk-layers of max(flops / MFMA peak,
     bytes / HBM peak) against the measured time.  Same seeded synthetic weights and inputs."""
@@ -329,7 +354,7 @@ def run_config(name, torch, cpa, synth, steps=1, warmup=1, attention_roofline=Fa
     n, C = w.n_prompt, w.chunk
     note(f"config {w.name}: {w.n_layer} layers, {n} tokens in {C}-token chunks, {w.kv_type} cache")
     layers = gpu_layers(w, torch, cpa, synth)
-    ctx = cpa.PrefillContext(cpa.make_config(w, n, C), layers)
+    ctx = cpa.PrefillContext(cpa.make_config(w, n, C), layers, stream=torch.cuda.Stream())
     del layers
     torch.cuda.empty_cache()
     if w.vocab:
@@ -337,15 +362,23 @@ def run_config(name, torch, cpa, synth, steps=1, warmup=1, attention_roofline=Fa
     else:
         x = synth.prompt_inputs(w, backend="torch", device="cuda")
     out = torch.empty_like(x)
+    torch.cuda.synchronize()          # inputs are read on the context's own streams
     chunks = [(s, min(n, s + C)) for s in range(0, n, C)]
 
-    def step():
+    def step_two_lanes():
+        ctx.kv_cache_truncate(0)
+        rc = ctx.prefill_chunks_raw(x.data_ptr(), out.data_ptr(), n, C)
+        if rc != 0:
+            raise RuntimeError(f"prefill_chunks failed: {rc} {ctx.last_error()}")
+
+    def step_one_lane():
         ctx.kv_cache_truncate(0)
         for s, e in chunks:
             rc = ctx.prefill_chunk_raw(x[s:e].data_ptr(), out[s:e].data_ptr(), e - s)
             if rc != 0:
                 raise RuntimeError(f"prefill_chunk failed: {rc} {ctx.last_error()}")
 
+    step = step_two_lanes if lanes == 2 else step_one_lane
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -357,15 +390,20 @@ def run_config(name, torch, cpa, synth, steps=1, warmup=1, attention_roofline=Fa
     bound = sum(roofline_s(w, e - s, s) for s, e in chunks) * w.n_layer
     flops = sum(chunk_flops(w, e - s, s) for s, e in chunks) * w.n_layer
     res = {"workload": w.name, "n_layer": w.n_layer, "prompt_tokens": n, "chunk": C,
-           "kv_type": w.kv_type, "tokens_per_s": n / dt, "ms_per_prompt": dt * 1e3,
+           "kv_type": w.kv_type, "lanes": lanes, "tokens_per_s": n / dt, "ms_per_prompt": dt * 1e3,
            "algorithmic_tflop_per_s": flops / dt / 1e12,
            "roofline_bound_ms": bound * 1e3, "roofline_frac": bound / dt}
     if attention_roofline:
-        # one more step with HIP events around every attention launch (the kernel and, for
-        # split KV, its merge) on the library's stream; algorithmic flops of the unmasked
-        # causal part, 4*Hq*hd*(C*D + C(C+1)/2) per chunk-layer
+        # one more step, on one lane (each launch alone on the device), with HIP events
+        # around every attention launch (the kernel and, for split KV, its merge) on the
+        # library's stream; algorithmic flops of the unmasked causal part,
+        # 4*Hq*hd*(C*D + C(C+1)/2) per chunk-layer
         ctx.cp_kernel_timing("attention")
-        step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        step_one_lane()
+        torch.cuda.synchronize()
+        dt1 = time.perf_counter() - t1
         ms, launches = ctx.cp_kernel_times("attention")
         ctx.cp_kernel_timing(None)
         af = sum(4.0 * w.n_head * w.head_dim * ((e - s) * s + (e - s) * (e - s + 1) / 2)
@@ -376,7 +414,7 @@ def run_config(name, torch, cpa, synth, steps=1, warmup=1, attention_roofline=Fa
                            "frac": ach / PEAK_F16_TFLOPS, "traffic": None, "launches": launches,
                            "avg_launch_us": ms * 1e3 / max(1, launches),
                            "flops_per_launch": af / max(1, launches),
-                           "share_of_step": ms * 1e-3 / dt}
+                           "share_of_one_lane_step": ms * 1e-3 / dt1}
     ctx.close()
     del x, out
     torch.cuda.empty_cache()
@@ -515,6 +553,9 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the whole-prompt rates of the other workloads")
     ap.add_argument("--sweep-reps", type=int, default=5)
+    ap.add_argument("--lanes", type=int, choices=(1, 2), default=2,
+                    help="chunks in flight in the timed steps: 2 (prefill_chunks, two streams) "
+                         "or 1 (prefill_chunk for each chunk in turn)")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="CPU baseline over the first N prompt tokens (0: the whole prompt)")
     ap.add_argument("--pmc-probe", action="store_true",
@@ -567,7 +608,9 @@ def main():
         for name in ("tiny_dense", "dense27b_q8", "moe_a3b"):
             # the 58,300-token q8_0-cache share is the largest that fits one GPU; its
             # dominant kernel is attention over the q8_0 cache
-            configs.append(run_config(name, torch, cpa, synth, attention_roofline=name != "tiny_dense"))
+            # the tiny decoder is launch-bound: one lane (a second lane only adds event waits)
+            configs.append(run_config(name, torch, cpa, synth, attention_roofline=name != "tiny_dense",
+                                      lanes=1 if name == "tiny_dense" else args.lanes))
     sweep = None
     if not args.no_sweep:
         sweep = run_sweep(args, torch, cpa, synth, fit_linear)
@@ -586,6 +629,8 @@ def main():
                    "kv_type": w.kv_type},
         "roofline": res["roofline"],
         "prompt_roofline": res["prompt_roofline"],
+        "lanes": args.lanes,
+        "one_lane_tokens_per_s": res["one_lane_tokens_per_s"],
         "decode_regime": res["decode_regime"],
         "last_logits": res["last_logits"],
         "measured_peaks": {"mfma_f16_tflops": mf_tflops, "hbm_read_gbs": hbm_gbs,

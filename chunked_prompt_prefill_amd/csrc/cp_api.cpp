@@ -440,6 +440,7 @@ struct cp_ctx {
   uint8_t* stage = nullptr;     // the per-chunk buffers (offsets WS.stage on): ws + WS.stage,
                                 // or this device's static array during prefill_chunk_static
   int device = 0;               // the device current at prefill_init
+  std::vector<hipEvent_t> wave_ev; // prefill_chunks: [lane][layer] "layer done" events
   std::vector<LayerW> layers;
   int32_t n_past = 0;
   std::string err;
@@ -871,6 +872,75 @@ int prefill_chunk_static(cp_ctx* c, const float* x_in, float* x_out, int32_t n) 
   return run_chunk(c, x_in, x_out, n);
 }
 
+int prefill_chunks(cp_ctx* c, const float* x_in, float* x_out, int32_t n_tokens, int32_t chunk,
+                   void* workspace2, void* hip_stream2) {
+  if (!c) return CP_E_INVALID;
+  if (!workspace2 || !aligned(workspace2)) return fail(c, CP_E_ARENA, "workspace2 is NULL or not 256-byte aligned");
+  if (chunk < 1 || chunk > c->cfg.n_chunk_max) return fail(c, CP_E_CAPACITY, "chunk outside [1, n_chunk_max]");
+  if (n_tokens < 1) return fail(c, CP_E_INVALID, "n_tokens < 1");
+  // every chunk's checks before anything is enqueued (rows are d_model floats apart, so a
+  // chunk's rows keep the 16-byte alignment of x_in / x_out)
+  if (const int r = chunk_check(&c->cfg, c->n_past, x_in, x_out, std::min(chunk, n_tokens), c->err); r != CP_OK)
+    return r;
+  if ((int64_t)c->n_past + n_tokens > c->cfg.n_ctx_max) return fail(c, CP_E_CAPACITY, "n_past + n_tokens > n_ctx_max");
+  const Dims& D = c->D;
+  const int L = D.L;
+  const int K = (n_tokens + chunk - 1) / chunk;
+  hipStream_t s0 = c->stream, s1 = (hipStream_t)hip_stream2;
+  if (s1 == s0) return fail(c, CP_E_INVALID, "hip_stream2 must differ from the context's stream");
+  if (c->wave_ev.empty()) {
+    c->wave_ev.assign(2 * L, nullptr);
+    for (auto& e : c->wave_ev) {
+      const hipError_t er = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+      if (er != hipSuccess) {
+        for (auto& f : c->wave_ev) if (f) hipEventDestroy(f);
+        c->wave_ev.clear();
+        return hip_fail(c, er, "event create");
+      }
+    }
+  }
+  struct Lane { hipStream_t stream; uint8_t* stage; PendingSum pend; };
+  Lane lanes[2] = {{s0, c->stage, PendingSum()}, {s1, (uint8_t*)workspace2 + c->WS.stage, PendingSum()}};
+  const hipStream_t saved_stream = c->stream;
+  uint8_t* const saved_stage = c->stage;
+  auto restore = [&] { c->stream = saved_stream; c->stage = saved_stage; c->pend_x = PendingSum(); };
+  // the second stream starts after the work already on the context's stream (a "layer
+  // done" event of lane 1 serves as the join point, recorded before any of its layers)
+  hipEvent_t join = c->wave_ev[L];
+  CP_HIP(c, hipEventRecord(join, s0), "event record");
+  CP_HIP(c, hipStreamWaitEvent(s1, join, 0), "stream wait");
+  const int start0 = c->n_past;
+  // Chunk i runs on lane i % 2, its layers in order; its layer l starts once chunk i-1
+  // (the other lane) has finished layer l, whose cache rows it attends to.  So while chunk
+  // i runs layer l, chunk i+1 runs layer l-1 on the other stream.  A lane runs its chunks
+  // whole, one after another, so its buffers (and the split-K sums one layer leaves to the
+  // next) belong to one chunk at a time.
+  for (int i = 0; i < K; ++i) {
+    Lane& ln = lanes[i & 1];
+    const int s = i * chunk, n = std::min(chunk, n_tokens - s);
+    const float* xi = x_in + (int64_t)s * D.d;
+    float* xo = x_out + (int64_t)s * D.d;
+    c->stream = ln.stream;
+    c->stage = ln.stage;
+    c->pend_x = PendingSum();
+    for (int l = 0; l < L; ++l) {
+      if (i > 0) {
+        const hipError_t e = hipStreamWaitEvent(ln.stream, c->wave_ev[((i - 1) & 1) * L + l], 0);
+        if (e != hipSuccess) { restore(); return hip_fail(c, e, "stream wait"); }
+      }
+      const int r = run_layer(c, l, l == 0 ? xi : xo, xo, n, start0 + s, l == L - 1);
+      if (r != CP_OK) { restore(); return r; }
+      const hipError_t e = hipEventRecord(c->wave_ev[(i & 1) * L + l], ln.stream);
+      if (e != hipSuccess) { restore(); return hip_fail(c, e, "event record"); }
+    }
+  }
+  restore();
+  // the context's stream continues after both lanes
+  if (K > 1) CP_HIP(c, hipStreamWaitEvent(s0, c->wave_ev[1 * L + (L - 1)], 0), "stream wait");
+  c->n_past = start0 + n_tokens;
+  return CP_OK;
+}
+
 int prefill_chunk_trace(cp_ctx* c, const float* x_in, float* x_out, int32_t n, float* layer_out,
                         int64_t layer_stride, int32_t* route_idx, int64_t route_stride) {
   if (!c) return CP_E_INVALID;
@@ -991,6 +1061,7 @@ void prefill_free(cp_ctx* c) {
   hipStreamSynchronize(c->stream);
   for (auto& r : c->pending) { hipEventDestroy(r.a); hipEventDestroy(r.b); }
   for (auto e : c->pool) hipEventDestroy(e);
+  for (auto e : c->wave_ev) hipEventDestroy(e);
   delete c;
 }
 

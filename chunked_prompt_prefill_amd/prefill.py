@@ -89,20 +89,67 @@ class PrefillContext:
         if rc != CP_OK:
             raise PrefillError(rc, self.L.prefill_last_error(self._ctx).decode())
 
+    def _out_like(self, x_in: torch.Tensor, *streams) -> torch.Tensor:
+        """An output allocated here for work on the context's own stream(s): torch's caching
+        allocator is told those streams use it, so the block is not handed out again
+        before their work on it is done (even if the caller drops the tensor at once)."""
+        x_out = torch.empty_like(x_in)
+        for st in (self.stream,) + streams:
+            if st is not None:
+                x_out.record_stream(st)
+        return x_out
+
+    def _follow_caller(self):
+        """With a stream of its own, the context's work starts after the work already
+        enqueued on the caller's current stream: the producers of the tensors it is handed,
+        and the last users of any block torch's allocator hands out there."""
+        if self.stream is not None:
+            self.stream.wait_stream(torch.cuda.current_stream(self.device))
+
     def prefill_chunk(self, x_in: torch.Tensor, x_out: Optional[torch.Tensor] = None) -> torch.Tensor:
-        x_out = torch.empty_like(x_in) if x_out is None else x_out
+        self._follow_caller()
+        x_out = self._out_like(x_in) if x_out is None else x_out
         self._check(self.L.prefill_chunk(self._ctx, ptr(x_in), ptr(x_out), x_in.shape[0]))
         return x_out
 
+    def prefill_chunks(self, x_in: torch.Tensor, x_out: Optional[torch.Tensor] = None, chunk: int = 0,
+                       stream2: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """The prompt x_in in chunks of `chunk` tokens (default n_chunk_max) on two lanes: the
+        context's stream and stream2 (a second stream, created on first use if None), with
+        the second lane's buffers in a second workspace owned by this object."""
+        self._follow_caller()
+        if getattr(self, "ws2", None) is None:
+            self.ws2 = torch.empty_like(self.ws)
+        if stream2 is None:
+            if getattr(self, "stream2", None) is None:
+                self.stream2 = torch.cuda.Stream(device=self.device)
+            stream2 = self.stream2
+        x_out = self._out_like(x_in, stream2) if x_out is None else x_out
+        self._check(self.L.prefill_chunks(self._ctx, ptr(x_in), ptr(x_out), x_in.shape[0],
+                                          chunk or self.cfg.n_chunk_max, ptr(self.ws2),
+                                          stream2.cuda_stream))
+        return x_out
+
+    def prefill_chunks_raw(self, x_in_ptr: int, x_out_ptr: int, n: int, chunk: int) -> int:
+        """prefill_chunks on raw device pointers (the second workspace and stream as above)."""
+        if getattr(self, "ws2", None) is None:
+            self.ws2 = torch.empty_like(self.ws)
+        if getattr(self, "stream2", None) is None:
+            self.stream2 = torch.cuda.Stream(device=self.device)
+        return self.L.prefill_chunks(self._ctx, x_in_ptr, x_out_ptr, n, chunk, ptr(self.ws2),
+                                     self.stream2.cuda_stream)
+
     def prefill_chunk_static(self, x_in: torch.Tensor, x_out: Optional[torch.Tensor] = None) -> torch.Tensor:
         """prefill_chunk with the chunk's buffers in the library's static device array."""
-        x_out = torch.empty_like(x_in) if x_out is None else x_out
+        self._follow_caller()
+        x_out = self._out_like(x_in) if x_out is None else x_out
         self._check(self.L.prefill_chunk_static(self._ctx, ptr(x_in), ptr(x_out), x_in.shape[0]))
         return x_out
 
     def prefill_chunk_trace(self, x_in: torch.Tensor, x_out: torch.Tensor, layer_out=None,
                             layer_stride: int = 0, route_idx=None, route_stride: int = 0):
         """layer_out / route_idx: device tensors (or None); strides in elements."""
+        self._follow_caller()
         self._check(self.L.prefill_chunk_trace(self._ctx, ptr(x_in), ptr(x_out), x_in.shape[0],
                                                ptr(layer_out), layer_stride, ptr(route_idx),
                                                route_stride))
@@ -112,7 +159,8 @@ class PrefillContext:
         return self.L.prefill_chunk(self._ctx, x_in_ptr, x_out_ptr, n)
 
     def prefill_chunk_timed(self, x_in: torch.Tensor, x_out: Optional[torch.Tensor] = None):
-        x_out = torch.empty_like(x_in) if x_out is None else x_out
+        self._follow_caller()
+        x_out = self._out_like(x_in) if x_out is None else x_out
         ms = (ctypes.c_float * self.cfg.n_layer)()
         self._check(self.L.prefill_chunk_timed(self._ctx, ptr(x_in), ptr(x_out), x_in.shape[0], ms))
         return x_out, list(ms)

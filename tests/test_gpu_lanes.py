@@ -1,0 +1,114 @@
+"""prefill_chunks (two chunks in flight on two streams) against prefill_chunk in turn (GPU).
+
+Both run the same kernels in the same launch plans on the same rows; only the order in
+which chunks and layers overlap differs, and every cross-chunk dependency (a chunk's
+layer reads the cache rows the previous chunk wrote at that layer) is ordered by events.
+So outputs, n_past and the cache state must be bitwise equal, for dense and routed
+layers, both cache types, even and odd chunk counts, a ragged last chunk, a prompt that
+starts at a non-zero depth and one that fits a single chunk.
+"""
+import pytest
+
+import synth
+from gpu_util import log, need_gpu
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(300)]
+
+
+@pytest.fixture(scope="module")
+def torch():
+    return need_gpu()
+
+
+def gpu_layers(torch, cpa, w):
+    out = []
+    for l in range(w.n_layer):
+        lw = {}
+        for name, shape in synth.weight_shapes(w):
+            t = synth.layer_weight(w, l, name, shape, backend="torch", device="cuda", gains="random")
+            lw[name] = t if name.endswith("_norm") else cpa.cp_quantize_q8_0(t)
+        out.append(lw)
+    torch.cuda.synchronize()
+    return out
+
+
+def compare(torch, w, n, chunk, prefix=0, in_place=False):
+    import chunked_prompt_prefill_amd as cpa
+    layers = gpu_layers(torch, cpa, w)
+    chunk = min(chunk, prefix + n)
+    cfg = cpa.make_config(w, prefix + n, chunk)
+    ref = cpa.PrefillContext(cfg, layers)
+    lan = cpa.PrefillContext(cfg, layers, stream=torch.cuda.Stream())
+    x = torch.from_numpy(synth.prompt_inputs(w, prefix + n)).cuda()
+    torch.cuda.synchronize()          # x is read on the contexts' own streams
+    if prefix:
+        for c in (ref, lan):
+            for s in range(0, prefix, chunk):
+                c.prefill_chunk(x[s:min(prefix, s + chunk)])
+    out_ref = torch.empty_like(x[prefix:])
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        ref.prefill_chunk(x[prefix + s:prefix + e], out_ref[s:e])
+    if in_place:
+        out = x[prefix:].clone()
+        lan.prefill_chunks(out, out, chunk)
+    else:
+        out = lan.prefill_chunks(x[prefix:], None, chunk)
+    torch.cuda.synchronize()
+    same = torch.equal(out, out_ref)
+    log(f"  {w.name} n={n} chunk={chunk} prefix={prefix} in_place={in_place}: bitwise equal {same}")
+    assert same
+    assert lan.n_past == ref.n_past == prefix + n
+    assert lan.kv_cache_get_state() == ref.kv_cache_get_state()
+    ref.close()
+    lan.close()
+
+
+@pytest.mark.parametrize("kv", ["f16", "q8_0"])
+def test_lanes_equal_sequential_dense(torch, kv):
+    """Two layers of the 27B-class dense shapes: 5 chunks of 512 and a ragged sixth."""
+    w = synth.WORKLOADS["dense27b_sweep"].with_(n_layer=2, kv_type=kv)
+    compare(torch, w, 5 * 512 + 137, 512)
+
+
+def test_lanes_equal_sequential_routed_experts(torch):
+    """Two routed-expert layers: 4 chunks of 384 (an even count) after a 100-token prefix."""
+    w = synth.WORKLOADS["moe_a3b"].with_(n_layer=2)
+    compare(torch, w, 4 * 384, 384, prefix=100)
+
+
+def test_lanes_small_shapes_in_place_and_single_chunk(torch):
+    """The tiny decoder: chunks of 7 (odd count), in place, after a prefix; and a prompt of
+    one chunk."""
+    w = synth.WORKLOADS["tiny_dense"]
+    compare(torch, w.with_(kv_type="q8_0"), 23, 7, prefix=9, in_place=True)
+    compare(torch, w, 5, 7)
+
+
+def test_lanes_refuse_before_enqueue(torch):
+    """A chunk above n_chunk_max, a prompt past n_ctx_max and the context's own stream as
+    the second stream are refused; n_past and the cache are unchanged."""
+    import chunked_prompt_prefill_amd as cpa
+    from chunked_prompt_prefill_amd._lib import CP_E_CAPACITY, CP_E_INVALID
+    w = synth.WORKLOADS["tiny_dense"]
+    layers = gpu_layers(torch, cpa, w)
+    ctx = cpa.PrefillContext(cpa.make_config(w, 32, 8), layers)
+    x = torch.from_numpy(synth.prompt_inputs(w, 40)).cuda()
+    ctx.prefill_chunk(x[:8])
+    blob = ctx.kv_cache_get_state()
+    out = torch.empty_like(x)
+    ws2 = torch.empty_like(ctx.ws)
+    s2 = torch.cuda.Stream()
+    L = ctx.L
+    assert L.prefill_chunks(ctx._ctx, x.data_ptr(), out.data_ptr(), 16, 9, ws2.data_ptr(), s2.cuda_stream) == CP_E_CAPACITY
+    assert L.prefill_chunks(ctx._ctx, x.data_ptr(), out.data_ptr(), 25, 8, ws2.data_ptr(), s2.cuda_stream) == CP_E_CAPACITY
+    own = torch.cuda.current_stream().cuda_stream
+    assert L.prefill_chunks(ctx._ctx, x.data_ptr(), out.data_ptr(), 8, 8, ws2.data_ptr(), own) == CP_E_INVALID
+    assert ctx.n_past == 8
+    assert ctx.kv_cache_get_state() == blob
+    # and it still works afterwards
+    ctx.prefill_chunks(x[8:24], out[8:24], 8, s2)
+    torch.cuda.synchronize()
+    assert ctx.n_past == 24
+    assert bool(torch.isfinite(out[8:24]).all())
+    ctx.close()
