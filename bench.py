@@ -185,7 +185,9 @@ def pmc_digest(fetch_csv, write_csv, copy_mib):
         if not copy or len(first) != 1:
             raise SystemExit(f"{path}: expected the copy and one unsplit gate/up launch, got {len(copy)} / {len(first)}")
         op = rows[first[0]:first[0] + n_disp]
-        return copy[0], sum(float(r["Counter_Value"]) for r in op), [r["Kernel_Name"].split("(")[0] for r in op]
+        def short(name):
+            return name.rsplit("(", 1)[0].replace("void ", "").replace("cp::(anonymous namespace)::", "").replace("cp::", "")
+        return copy[0], sum(float(r["Counter_Value"]) for r in op), [short(r["Kernel_Name"]) for r in op]
 
     cf, kf, names = readings(fetch_csv)
     cw, kw, _ = readings(write_csv)
