@@ -217,7 +217,7 @@ def run_main(args, torch, cpa, synth):
     t = time.time()
     layers = gpu_layers(w, torch, cpa, synth)
     # the context's own stream (not the default one, which would serialise with the
-    # second lane's stream) and a second stream for prefill_chunks
+    # other lanes' streams); prefill_chunks adds a stream per further lane
     ctx = cpa.PrefillContext(cpa.make_config(w, n + DECODE_ROOM, C), layers, stream=torch.cuda.Stream())
     del layers
     torch.cuda.empty_cache()
@@ -228,9 +228,9 @@ def run_main(args, torch, cpa, synth):
     chunks = [(s, min(n, s + C)) for s in range(0, n, C)]
 
     def step():
-        # the whole prompt in chunks of C, two chunks in flight on two streams
+        # the whole prompt in chunks of C, args.lanes chunks in flight on as many streams
         ctx.kv_cache_truncate(0)
-        rc = ctx.prefill_chunks_raw(x.data_ptr(), out.data_ptr(), n, C)
+        rc = ctx.prefill_chunks_raw(x.data_ptr(), out.data_ptr(), n, C, args.lanes)
         if rc != 0:
             raise RuntimeError(f"prefill_chunks failed: {rc} {ctx.last_error()}")
 
@@ -242,12 +242,12 @@ def run_main(args, torch, cpa, synth):
             if rc != 0:
                 raise RuntimeError(f"prefill_chunk failed: {rc} {ctx.last_error()}")
 
-    run_step = step if args.lanes == 2 else step_one_lane
+    run_step = step if args.lanes > 1 else step_one_lane
     for i in range(args.warmup):
         run_step()
         torch.cuda.synchronize()
         note(f"warmup step {i + 1}/{args.warmup} done")
-    # headline: K steps, two chunks in flight (prefill_chunks) unless --lanes 1
+    # headline: K steps, args.lanes chunks in flight (prefill_chunks) unless --lanes 1
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -293,7 +293,21 @@ def run_main(args, torch, cpa, synth):
                 raise RuntimeError(f"prefill_chunk failed: {rc} {ctx.last_error()}")
         torch.cuda.synchronize()
         dt2 = time.perf_counter() - t2
+        # the same 32 chunks as one prompt through prefill_chunks, 2 and 3 tiny chunks in
+        # flight (prompt tokens known in advance; generated tokens would depend on the
+        # previous one)
+        lanes_ms = {}
+        for nl in (2, 3):
+            ctx.kv_cache_truncate(n)
+            torch.cuda.synchronize()
+            t3 = time.perf_counter()
+            rc = ctx.prefill_chunks_raw(x.data_ptr(), out.data_ptr(), 32 * dc, dc, nl)
+            if rc != 0:
+                raise RuntimeError(f"prefill_chunks failed: {rc} {ctx.last_error()}")
+            torch.cuda.synchronize()
+            lanes_ms[str(nl)] = (time.perf_counter() - t3) / 32 * 1e3
         decode[f"chunk_{dc}"] = {"tokens_per_s": 32 * dc / dt2, "ms_per_chunk": dt2 / 32 * 1e3,
+                                 "lanes_ms_per_chunk": lanes_ms,
                                  "depth": n,
                                  "hbm_roofline_ms_per_chunk": roofline_s(w, dc, n) * w.n_layer * 1e3}
     # The step after the prompt: logits of the last position over a q8_0 LM head of
@@ -367,9 +381,9 @@ def run_config(name, torch, cpa, synth, steps=1, warmup=1, attention_roofline=Fa
     torch.cuda.synchronize()          # inputs are read on the context's own streams
     chunks = [(s, min(n, s + C)) for s in range(0, n, C)]
 
-    def step_two_lanes():
+    def step_lanes():
         ctx.kv_cache_truncate(0)
-        rc = ctx.prefill_chunks_raw(x.data_ptr(), out.data_ptr(), n, C)
+        rc = ctx.prefill_chunks_raw(x.data_ptr(), out.data_ptr(), n, C, lanes)
         if rc != 0:
             raise RuntimeError(f"prefill_chunks failed: {rc} {ctx.last_error()}")
 
@@ -380,7 +394,7 @@ def run_config(name, torch, cpa, synth, steps=1, warmup=1, attention_roofline=Fa
             if rc != 0:
                 raise RuntimeError(f"prefill_chunk failed: {rc} {ctx.last_error()}")
 
-    step = step_two_lanes if lanes == 2 else step_one_lane
+    step = step_lanes if lanes > 1 else step_one_lane
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -555,9 +569,9 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the whole-prompt rates of the other workloads")
     ap.add_argument("--sweep-reps", type=int, default=5)
-    ap.add_argument("--lanes", type=int, choices=(1, 2), default=2,
-                    help="chunks in flight in the timed steps: 2 (prefill_chunks, two streams) "
-                         "or 1 (prefill_chunk for each chunk in turn)")
+    ap.add_argument("--lanes", type=int, choices=range(1, 9), default=3,
+                    help="chunks in flight in the timed steps: 2 .. 8 (prefill_chunks, one "
+                         "stream per lane) or 1 (prefill_chunk for each chunk in turn)")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="CPU baseline over the first N prompt tokens (0: the whole prompt)")
     ap.add_argument("--pmc-probe", action="store_true",
@@ -610,7 +624,7 @@ def main():
         for name in ("tiny_dense", "dense27b_q8", "moe_a3b"):
             # the 58,300-token q8_0-cache share is the largest that fits one GPU; its
             # dominant kernel is attention over the q8_0 cache
-            # the tiny decoder is launch-bound: one lane (a second lane only adds event waits)
+            # the tiny decoder is launch-bound: one lane (more lanes only add event waits)
             configs.append(run_config(name, torch, cpa, synth, attention_roofline=name != "tiny_dense",
                                       lanes=1 if name == "tiny_dense" else args.lanes))
     sweep = None

@@ -48,7 +48,8 @@ SIGNATURES = {
                                     c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(c_vp)]),
     "prefill_chunk": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32]),
     "prefill_chunk_static": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32]),
-    "prefill_chunks": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp]),
+    "prefill_chunks": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, ctypes.POINTER(c_vp),
+                                      ctypes.POINTER(c_vp)]),
     "prefill_chunk_timed": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32, ctypes.POINTER(c_f)]),
     "prefill_chunk_trace": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32, c_vp, c_i64, c_vp, c_i64]),
     "kv_cache_get_state": (ctypes.c_int, [c_vp, c_vp, c_sz, ctypes.POINTER(c_sz)]),

@@ -35,6 +35,9 @@ struct Dims {
 
 int64_t round_up(int64_t v, int64_t g) { return (v + g - 1) / g * g; }
 
+// Most chunks prefill_chunks keeps in flight (one stream and one workspace each).
+constexpr int kMaxLanes = 8;
+
 // Size of the static scratch array that prefill_chunk_static takes a chunk's buffers from.
 constexpr size_t kStaticScratchBytes = (size_t)256 << 20;
 
@@ -873,9 +876,18 @@ int prefill_chunk_static(cp_ctx* c, const float* x_in, float* x_out, int32_t n) 
 }
 
 int prefill_chunks(cp_ctx* c, const float* x_in, float* x_out, int32_t n_tokens, int32_t chunk,
-                   void* workspace2, void* hip_stream2) {
+                   int32_t n_lanes, void* const* workspaces, void* const* hip_streams) {
   if (!c) return CP_E_INVALID;
-  if (!workspace2 || !aligned(workspace2)) return fail(c, CP_E_ARENA, "workspace2 is NULL or not 256-byte aligned");
+  if (n_lanes < 1 || n_lanes > kMaxLanes) return fail(c, CP_E_INVALID, "n_lanes outside [1, 8]");
+  if (n_lanes > 1 && (!workspaces || !hip_streams)) return fail(c, CP_E_INVALID, "workspaces / hip_streams is NULL");
+  for (int j = 1; j < n_lanes; ++j) {
+    if (!workspaces[j - 1] || !aligned(workspaces[j - 1]))
+      return fail(c, CP_E_ARENA, "a lane's workspace is NULL or not 256-byte aligned");
+    if ((hipStream_t)hip_streams[j - 1] == c->stream)
+      return fail(c, CP_E_INVALID, "a lane's stream is the context's stream");
+    for (int i = 1; i < j; ++i)
+      if (hip_streams[i - 1] == hip_streams[j - 1]) return fail(c, CP_E_INVALID, "two lanes share a stream");
+  }
   if (chunk < 1 || chunk > c->cfg.n_chunk_max) return fail(c, CP_E_CAPACITY, "chunk outside [1, n_chunk_max]");
   if (n_tokens < 1) return fail(c, CP_E_INVALID, "n_tokens < 1");
   // every chunk's checks before anything is enqueued (rows are d_model floats apart, so a
@@ -886,10 +898,11 @@ int prefill_chunks(cp_ctx* c, const float* x_in, float* x_out, int32_t n_tokens,
   const Dims& D = c->D;
   const int L = D.L;
   const int K = (n_tokens + chunk - 1) / chunk;
-  hipStream_t s0 = c->stream, s1 = (hipStream_t)hip_stream2;
-  if (s1 == s0) return fail(c, CP_E_INVALID, "hip_stream2 must differ from the context's stream");
-  if (c->wave_ev.empty()) {
-    c->wave_ev.assign(2 * L, nullptr);
+  // events: [lane][layer] "layer done", and one join event (the context's stream at entry)
+  const size_t n_ev = (size_t)kMaxLanes * L + 1;
+  if (c->wave_ev.size() != n_ev) {
+    for (auto& e : c->wave_ev) if (e) hipEventDestroy(e);
+    c->wave_ev.assign(n_ev, nullptr);
     for (auto& e : c->wave_ev) {
       const hipError_t er = hipEventCreateWithFlags(&e, hipEventDisableTiming);
       if (er != hipSuccess) {
@@ -899,24 +912,29 @@ int prefill_chunks(cp_ctx* c, const float* x_in, float* x_out, int32_t n_tokens,
       }
     }
   }
-  struct Lane { hipStream_t stream; uint8_t* stage; PendingSum pend; };
-  Lane lanes[2] = {{s0, c->stage, PendingSum()}, {s1, (uint8_t*)workspace2 + c->WS.stage, PendingSum()}};
+  auto ev = [&](int lane, int layer) { return c->wave_ev[(size_t)lane * L + layer]; };
+  struct Lane { hipStream_t stream; uint8_t* stage; };
+  Lane lanes[kMaxLanes];
+  lanes[0] = {c->stream, c->stage};
+  for (int j = 1; j < n_lanes; ++j)
+    lanes[j] = {(hipStream_t)hip_streams[j - 1], (uint8_t*)workspaces[j - 1] + c->WS.stage};
   const hipStream_t saved_stream = c->stream;
   uint8_t* const saved_stage = c->stage;
   auto restore = [&] { c->stream = saved_stream; c->stage = saved_stage; c->pend_x = PendingSum(); };
-  // the second stream starts after the work already on the context's stream (a "layer
-  // done" event of lane 1 serves as the join point, recorded before any of its layers)
-  hipEvent_t join = c->wave_ev[L];
-  CP_HIP(c, hipEventRecord(join, s0), "event record");
-  CP_HIP(c, hipStreamWaitEvent(s1, join, 0), "stream wait");
+  // the other lanes start after the work already on the context's stream
+  hipEvent_t join = c->wave_ev[n_ev - 1];
+  CP_HIP(c, hipEventRecord(join, lanes[0].stream), "event record");
+  for (int j = 1; j < n_lanes; ++j) CP_HIP(c, hipStreamWaitEvent(lanes[j].stream, join, 0), "stream wait");
   const int start0 = c->n_past;
-  // Chunk i runs on lane i % 2, its layers in order; its layer l starts once chunk i-1
-  // (the other lane) has finished layer l, whose cache rows it attends to.  So while chunk
-  // i runs layer l, chunk i+1 runs layer l-1 on the other stream.  A lane runs its chunks
+  // Chunk i runs on lane i mod n_lanes, its layers in order; its layer l starts once chunk
+  // i-1 (the previous lane) has finished layer l, whose cache rows it attends to.  So while
+  // chunk i runs layer l, chunk i+1 runs layer l-1, and so on.  A lane runs its chunks
   // whole, one after another, so its buffers (and the split-K sums one layer leaves to the
-  // next) belong to one chunk at a time.
+  // next) belong to one chunk at a time.  An event is re-recorded by chunk i+n_lanes only
+  // after chunk i+1's wait on it has been enqueued.
   for (int i = 0; i < K; ++i) {
-    Lane& ln = lanes[i & 1];
+    const int li = i % n_lanes, lp = (i + n_lanes - 1) % n_lanes;
+    const Lane& ln = lanes[li];
     const int s = i * chunk, n = std::min(chunk, n_tokens - s);
     const float* xi = x_in + (int64_t)s * D.d;
     float* xo = x_out + (int64_t)s * D.d;
@@ -924,19 +942,23 @@ int prefill_chunks(cp_ctx* c, const float* x_in, float* x_out, int32_t n_tokens,
     c->stage = ln.stage;
     c->pend_x = PendingSum();
     for (int l = 0; l < L; ++l) {
-      if (i > 0) {
-        const hipError_t e = hipStreamWaitEvent(ln.stream, c->wave_ev[((i - 1) & 1) * L + l], 0);
+      if (i > 0 && n_lanes > 1) {
+        const hipError_t e = hipStreamWaitEvent(ln.stream, ev(lp, l), 0);
         if (e != hipSuccess) { restore(); return hip_fail(c, e, "stream wait"); }
       }
       const int r = run_layer(c, l, l == 0 ? xi : xo, xo, n, start0 + s, l == L - 1);
       if (r != CP_OK) { restore(); return r; }
-      const hipError_t e = hipEventRecord(c->wave_ev[(i & 1) * L + l], ln.stream);
-      if (e != hipSuccess) { restore(); return hip_fail(c, e, "event record"); }
+      if (n_lanes > 1) {
+        const hipError_t e = hipEventRecord(ev(li, l), ln.stream);
+        if (e != hipSuccess) { restore(); return hip_fail(c, e, "event record"); }
+      }
     }
   }
   restore();
-  // the context's stream continues after both lanes
-  if (K > 1) CP_HIP(c, hipStreamWaitEvent(s0, c->wave_ev[1 * L + (L - 1)], 0), "stream wait");
+  // the context's stream continues after every lane: the last chunk's last layer follows
+  // every earlier chunk's last layer through the waits above
+  const int last_lane = (K - 1) % n_lanes;
+  if (last_lane != 0) CP_HIP(c, hipStreamWaitEvent(lanes[0].stream, ev(last_lane, L - 1), 0), "stream wait");
   c->n_past = start0 + n_tokens;
   return CP_OK;
 }

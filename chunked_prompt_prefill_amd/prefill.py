@@ -12,7 +12,7 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 import torch
 
-from ._lib import (CP_OK, KV_TYPES, PrefillError, cp_config, cp_layer_weights, lib, ptr,
+from ._lib import (CP_OK, KV_TYPES, PrefillError, c_vp, cp_config, cp_layer_weights, lib, ptr,
                    stream_ptr)
 
 MATRIX_KEYS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "w_router")
@@ -112,32 +112,35 @@ class PrefillContext:
         self._check(self.L.prefill_chunk(self._ctx, ptr(x_in), ptr(x_out), x_in.shape[0]))
         return x_out
 
+    def _lanes(self, n_lanes: int):
+        """Workspaces and streams of lanes 1 .. n_lanes-1, created on first use and kept (as
+        ctypes arrays of their addresses)."""
+        if not hasattr(self, "lane_ws"):
+            self.lane_ws, self.lane_streams = [], []
+        while len(self.lane_ws) < n_lanes - 1:
+            self.lane_ws.append(torch.empty_like(self.ws))
+            self.lane_streams.append(torch.cuda.Stream(device=self.device))
+        k = max(0, n_lanes - 1)
+        ws = (c_vp * max(1, k))(*[t.data_ptr() for t in self.lane_ws[:k]])
+        st = (c_vp * max(1, k))(*[s.cuda_stream for s in self.lane_streams[:k]])
+        return ws, st
+
     def prefill_chunks(self, x_in: torch.Tensor, x_out: Optional[torch.Tensor] = None, chunk: int = 0,
-                       stream2: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-        """The prompt x_in in chunks of `chunk` tokens (default n_chunk_max) on two lanes: the
-        context's stream and stream2 (a second stream, created on first use if None), with
-        the second lane's buffers in a second workspace owned by this object."""
+                       n_lanes: int = 2) -> torch.Tensor:
+        """The prompt x_in in chunks of `chunk` tokens (default n_chunk_max), n_lanes chunks in
+        flight: lane 0 is the context's stream, the others have streams and workspaces owned
+        by this object."""
         self._follow_caller()
-        if getattr(self, "ws2", None) is None:
-            self.ws2 = torch.empty_like(self.ws)
-        if stream2 is None:
-            if getattr(self, "stream2", None) is None:
-                self.stream2 = torch.cuda.Stream(device=self.device)
-            stream2 = self.stream2
-        x_out = self._out_like(x_in, stream2) if x_out is None else x_out
+        ws, st = self._lanes(n_lanes)
+        x_out = self._out_like(x_in, *self.lane_streams[:n_lanes - 1]) if x_out is None else x_out
         self._check(self.L.prefill_chunks(self._ctx, ptr(x_in), ptr(x_out), x_in.shape[0],
-                                          chunk or self.cfg.n_chunk_max, ptr(self.ws2),
-                                          stream2.cuda_stream))
+                                          chunk or self.cfg.n_chunk_max, n_lanes, ws, st))
         return x_out
 
-    def prefill_chunks_raw(self, x_in_ptr: int, x_out_ptr: int, n: int, chunk: int) -> int:
-        """prefill_chunks on raw device pointers (the second workspace and stream as above)."""
-        if getattr(self, "ws2", None) is None:
-            self.ws2 = torch.empty_like(self.ws)
-        if getattr(self, "stream2", None) is None:
-            self.stream2 = torch.cuda.Stream(device=self.device)
-        return self.L.prefill_chunks(self._ctx, x_in_ptr, x_out_ptr, n, chunk, ptr(self.ws2),
-                                     self.stream2.cuda_stream)
+    def prefill_chunks_raw(self, x_in_ptr: int, x_out_ptr: int, n: int, chunk: int, n_lanes: int = 2) -> int:
+        """prefill_chunks on raw device pointers (lanes as above)."""
+        ws, st = self._lanes(n_lanes)
+        return self.L.prefill_chunks(self._ctx, x_in_ptr, x_out_ptr, n, chunk, n_lanes, ws, st)
 
     def prefill_chunk_static(self, x_in: torch.Tensor, x_out: Optional[torch.Tensor] = None) -> torch.Tensor:
         """prefill_chunk with the chunk's buffers in the library's static device array."""

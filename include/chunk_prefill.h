@@ -134,28 +134,29 @@ int prefill_chunk(cp_ctx* ctx, const float* x_in, float* x_out, int32_t n_tokens
 
 /* A prompt of n_tokens rows read in consecutive chunks of `chunk` tokens (the last one
  * shorter): the same work and the same result, bit for bit, as calling prefill_chunk for
- * each chunk in turn, with two chunks in flight on one device.  This is the two-lane
- * scheme of the llama.cpp "--split-overlap" pull request (section "How"): consecutive
- * chunks alternate between two lanes, each with its own stream and its own per-chunk
- * buffers, sharing the weights and the KV cache, and a lane's step waits by event only
- * for the other lane's work on the cache it reads.  There the overlap hides a
- * multi-device AllReduce; on one device it lets each chunk fill the compute units the
- * other leaves idle (launch tails, small kernels, the gaps between launches).
- * Chunk i runs on the context's stream (i even) or on hip_stream2 (i odd), its layers in
- * order; its layer l starts once chunk i-1 has finished layer l, whose cache rows it
- * attends to, so while one chunk runs layer l the next runs layer l-1.
+ * each chunk in turn, with up to n_lanes chunks in flight on one device.  This is the
+ * lane scheme of the llama.cpp "--split-overlap" pull request (section "How"):
+ * consecutive chunks alternate between lanes, each with its own stream and its own
+ * per-chunk buffers, sharing the weights and the KV cache, and a lane's step waits by
+ * event only for the other lanes' work on the cache it reads.  There two lanes hide a
+ * multi-device AllReduce; on one device the lanes let each chunk fill the compute units
+ * the others leave idle (launch tails, small kernels, the gaps between launches).
+ * Chunk i runs on lane i % n_lanes (lane 0 is the context's stream and workspace), its
+ * layers in order; its layer l starts once chunk i-1 has finished layer l, whose cache
+ * rows it attends to, so while one chunk runs layer l the next runs layer l-1.
  *   x_in, x_out: dev float32 [n_tokens][d_model], 16-byte aligned; x_out may equal x_in.
- *   workspace2: dev, cp_workspace_bytes(cfg) bytes, 256-byte aligned, the second
- *     chunk's buffers (the context's own workspace holds the first's and the RoPE
- *     tables); caller-owned, borrowed for the call's work.
- *   hip_stream2: a second stream (not the context's; default priority), caller-owned.
+ *   n_lanes: 1 .. 8 (1: prefill_chunk for each chunk in turn).
+ *   workspaces[j], hip_streams[j] (j < n_lanes - 1): lane j+1's buffers (dev,
+ *     cp_workspace_bytes(cfg) bytes each, 256-byte aligned; the context's own workspace
+ *     keeps the RoPE tables) and stream (not the context's, all distinct, default
+ *     priority); caller-owned, borrowed for the call's work.  May be NULL for one lane.
  * Requires 1 <= chunk <= n_chunk_max and n_past + n_tokens <= n_ctx_max (else
- * CP_E_CAPACITY), n_tokens >= 1 and the alignments (else CP_E_INVALID / CP_E_ARENA);
- * every check is made before anything is enqueued.  Returns once the work is enqueued;
- * work enqueued later on the context's stream runs after all of it.  n_past advances by
- * n_tokens. */
+ * CP_E_CAPACITY), n_tokens >= 1, distinct streams and the alignments (else CP_E_INVALID /
+ * CP_E_ARENA); every check is made before anything is enqueued.  Returns once the work is
+ * enqueued; work enqueued later on the context's stream runs after all of it.  n_past
+ * advances by n_tokens. */
 int prefill_chunks(cp_ctx* ctx, const float* x_in, float* x_out, int32_t n_tokens, int32_t chunk,
-                   void* workspace2, void* hip_stream2);
+                   int32_t n_lanes, void* const* workspaces, void* const* hip_streams);
 
 /* prefill_chunk for callers that cannot allocate device memory at the call (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation): the

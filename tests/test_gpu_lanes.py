@@ -1,11 +1,13 @@
-"""prefill_chunks (two chunks in flight on two streams) against prefill_chunk in turn (GPU).
+"""prefill_chunks (several chunks in flight on several streams) against prefill_chunk in
+turn (GPU).
 
 Both run the same kernels in the same launch plans on the same rows; only the order in
 which chunks and layers overlap differs, and every cross-chunk dependency (a chunk's
 layer reads the cache rows the previous chunk wrote at that layer) is ordered by events.
 So outputs, n_past and the cache state must be bitwise equal, for dense and routed
-layers, both cache types, even and odd chunk counts, a ragged last chunk, a prompt that
-starts at a non-zero depth and one that fits a single chunk.
+layers, both cache types, two to eight lanes, chunk counts that are and are not a
+multiple of the lane count, a ragged last chunk, a prompt that starts at a non-zero depth
+and one that fits a single chunk.
 """
 import pytest
 
@@ -32,7 +34,7 @@ def gpu_layers(torch, cpa, w):
     return out
 
 
-def compare(torch, w, n, chunk, prefix=0, in_place=False):
+def compare(torch, w, n, chunk, prefix=0, in_place=False, lanes=2):
     import chunked_prompt_prefill_amd as cpa
     layers = gpu_layers(torch, cpa, w)
     chunk = min(chunk, prefix + n)
@@ -51,12 +53,13 @@ def compare(torch, w, n, chunk, prefix=0, in_place=False):
         ref.prefill_chunk(x[prefix + s:prefix + e], out_ref[s:e])
     if in_place:
         out = x[prefix:].clone()
-        lan.prefill_chunks(out, out, chunk)
+        lan.prefill_chunks(out, out, chunk, lanes)
     else:
-        out = lan.prefill_chunks(x[prefix:], None, chunk)
+        out = lan.prefill_chunks(x[prefix:], None, chunk, lanes)
     torch.cuda.synchronize()
     same = torch.equal(out, out_ref)
-    log(f"  {w.name} n={n} chunk={chunk} prefix={prefix} in_place={in_place}: bitwise equal {same}")
+    log(f"  {w.name} n={n} chunk={chunk} prefix={prefix} in_place={in_place} lanes={lanes}: "
+        f"bitwise equal {same}")
     assert same
     assert lan.n_past == ref.n_past == prefix + n
     assert lan.kv_cache_get_state() == ref.kv_cache_get_state()
@@ -64,11 +67,11 @@ def compare(torch, w, n, chunk, prefix=0, in_place=False):
     lan.close()
 
 
-@pytest.mark.parametrize("kv", ["f16", "q8_0"])
-def test_lanes_equal_sequential_dense(torch, kv):
+@pytest.mark.parametrize("kv,lanes", [("f16", 2), ("q8_0", 2), ("f16", 3)])
+def test_lanes_equal_sequential_dense(torch, kv, lanes):
     """Two layers of the 27B-class dense shapes: 5 chunks of 512 and a ragged sixth."""
     w = synth.WORKLOADS["dense27b_sweep"].with_(n_layer=2, kv_type=kv)
-    compare(torch, w, 5 * 512 + 137, 512)
+    compare(torch, w, 5 * 512 + 137, 512, lanes=lanes)
 
 
 def test_lanes_equal_sequential_routed_experts(torch):
@@ -85,9 +88,19 @@ def test_lanes_small_shapes_in_place_and_single_chunk(torch):
     compare(torch, w, 5, 7)
 
 
+@pytest.mark.parametrize("lanes,n", [(1, 30), (4, 30), (8, 29), (8, 21)])
+def test_lanes_count(torch, lanes, n):
+    """The tiny decoder in 4-token chunks after a 5-token prefix: one lane; four lanes over
+    eight chunks (a ragged last one); eight lanes over eight chunks and over six."""
+    w = synth.WORKLOADS["tiny_dense"]
+    compare(torch, w, n, 4, prefix=5, lanes=lanes)
+
+
 def test_lanes_refuse_before_enqueue(torch):
-    """A chunk above n_chunk_max, a prompt past n_ctx_max and the context's own stream as
-    the second stream are refused; n_past and the cache are unchanged."""
+    """A chunk above n_chunk_max, a prompt past n_ctx_max, a lane count outside 1 .. 8, the
+    context's own stream as a lane stream and one stream given to two lanes are refused;
+    n_past and the cache are unchanged."""
+    import ctypes
     import chunked_prompt_prefill_amd as cpa
     from chunked_prompt_prefill_amd._lib import CP_E_CAPACITY, CP_E_INVALID
     w = synth.WORKLOADS["tiny_dense"]
@@ -97,18 +110,28 @@ def test_lanes_refuse_before_enqueue(torch):
     ctx.prefill_chunk(x[:8])
     blob = ctx.kv_cache_get_state()
     out = torch.empty_like(x)
-    ws2 = torch.empty_like(ctx.ws)
-    s2 = torch.cuda.Stream()
+    ws = [torch.empty_like(ctx.ws) for _ in range(8)]
+    st = [torch.cuda.Stream() for _ in range(8)]
     L = ctx.L
-    assert L.prefill_chunks(ctx._ctx, x.data_ptr(), out.data_ptr(), 16, 9, ws2.data_ptr(), s2.cuda_stream) == CP_E_CAPACITY
-    assert L.prefill_chunks(ctx._ctx, x.data_ptr(), out.data_ptr(), 25, 8, ws2.data_ptr(), s2.cuda_stream) == CP_E_CAPACITY
+
+    def call(n, chunk, lanes, streams):
+        arr = ctypes.c_void_p * 8
+        return L.prefill_chunks(ctx._ctx, x.data_ptr(), out.data_ptr(), n, chunk, lanes,
+                                arr(*[t.data_ptr() for t in ws]), arr(*streams))
+
+    ok = [s.cuda_stream for s in st]
     own = torch.cuda.current_stream().cuda_stream
-    assert L.prefill_chunks(ctx._ctx, x.data_ptr(), out.data_ptr(), 8, 8, ws2.data_ptr(), own) == CP_E_INVALID
+    assert call(16, 9, 2, ok) == CP_E_CAPACITY
+    assert call(25, 8, 2, ok) == CP_E_CAPACITY
+    assert call(8, 8, 0, ok) == CP_E_INVALID
+    assert call(8, 8, 9, ok) == CP_E_INVALID
+    assert call(8, 8, 2, [own] + ok[1:]) == CP_E_INVALID
+    assert call(16, 4, 3, [ok[0], ok[0]] + ok[2:]) == CP_E_INVALID
     assert ctx.n_past == 8
     assert ctx.kv_cache_get_state() == blob
     # and it still works afterwards
-    ctx.prefill_chunks(x[8:24], out[8:24], 8, s2)
+    assert call(16, 8, 2, ok) == 0
     torch.cuda.synchronize()
     assert ctx.n_past == 24
-    assert bool(torch.isfinite(out[8:24]).all())
+    assert bool(torch.isfinite(out[:16]).all())
     ctx.close()
