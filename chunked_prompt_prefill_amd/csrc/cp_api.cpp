@@ -897,9 +897,9 @@ int prefill_chunks(cp_ctx* c, const float* x_in, float* x_out, int32_t n_tokens,
   if ((int64_t)c->n_past + n_tokens > c->cfg.n_ctx_max) return fail(c, CP_E_CAPACITY, "n_past + n_tokens > n_ctx_max");
   const Dims& D = c->D;
   const int L = D.L;
-  const int K = (n_tokens + chunk - 1) / chunk;
-  // events: [lane][layer] "layer done", and one join event (the context's stream at entry)
-  const size_t n_ev = (size_t)kMaxLanes * L + 1;
+  // events: [lane][layer] "layer done", one "lane done" per lane,
+  // and one join event (the context's stream at entry)
+  const size_t n_ev = (size_t)kMaxLanes * (L + 1) + 1;
   if (c->wave_ev.size() != n_ev) {
     for (auto& e : c->wave_ev) if (e) hipEventDestroy(e);
     c->wave_ev.assign(n_ev, nullptr);
@@ -913,6 +913,7 @@ int prefill_chunks(cp_ctx* c, const float* x_in, float* x_out, int32_t n_tokens,
     }
   }
   auto ev = [&](int lane, int layer) { return c->wave_ev[(size_t)lane * L + layer]; };
+  auto lane_done = [&](int lane) { return c->wave_ev[(size_t)kMaxLanes * L + lane]; };
   struct Lane { hipStream_t stream; uint8_t* stage; };
   Lane lanes[kMaxLanes];
   lanes[0] = {c->stream, c->stage};
@@ -921,10 +922,12 @@ int prefill_chunks(cp_ctx* c, const float* x_in, float* x_out, int32_t n_tokens,
   const hipStream_t saved_stream = c->stream;
   uint8_t* const saved_stage = c->stage;
   auto restore = [&] { c->stream = saved_stream; c->stage = saved_stage; c->pend_x = PendingSum(); };
+  const int K = (n_tokens + chunk - 1) / chunk;
+  const int used = std::min(n_lanes, K);
   // the other lanes start after the work already on the context's stream
   hipEvent_t join = c->wave_ev[n_ev - 1];
   CP_HIP(c, hipEventRecord(join, lanes[0].stream), "event record");
-  for (int j = 1; j < n_lanes; ++j) CP_HIP(c, hipStreamWaitEvent(lanes[j].stream, join, 0), "stream wait");
+  for (int j = 1; j < used; ++j) CP_HIP(c, hipStreamWaitEvent(lanes[j].stream, join, 0), "stream wait");
   const int start0 = c->n_past;
   // Chunk i runs on lane i mod n_lanes, its layers in order; its layer l starts once chunk
   // i-1 (the previous lane) has finished layer l, whose cache rows it attends to.  So while
@@ -955,10 +958,11 @@ int prefill_chunks(cp_ctx* c, const float* x_in, float* x_out, int32_t n_tokens,
     }
   }
   restore();
-  // the context's stream continues after every lane: the last chunk's last layer follows
-  // every earlier chunk's last layer through the waits above
-  const int last_lane = (K - 1) % n_lanes;
-  if (last_lane != 0) CP_HIP(c, hipStreamWaitEvent(lanes[0].stream, ev(last_lane, L - 1), 0), "stream wait");
+  // the context's stream continues after every lane's last chunk
+  for (int j = 1; j < used; ++j) {
+    CP_HIP(c, hipEventRecord(lane_done(j), lanes[j].stream), "event record");
+    CP_HIP(c, hipStreamWaitEvent(lanes[0].stream, lane_done(j), 0), "stream wait");
+  }
   c->n_past = start0 + n_tokens;
   return CP_OK;
 }
