@@ -16,7 +16,7 @@
 // tiles.  K/V tiles are 64 positions, double buffered in LDS; the V tile is stored
 // transposed ([dim][position]) in the cache.  f16 tiles arrive by asynchronous
 // global->LDS loads (the swizzle is chosen through each lane's source address); q8_0
-// tiles are loaded into registers one tile ahead and dequantised into LDS.  Long KV
+// tiles are loaded into registers two tiles ahead and dequantised into LDS.  Long KV
 // ranges with few query tiles are split across workgroups and merged by a log-sum-exp
 // combine kernel.
 #include "cp_internal.h"
@@ -150,67 +150,63 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
     for (int j = 0; j < NVL; ++j) lds_dma16(vrs, (lvoid_a*)&bufV(J)[(j * AW + wave) * 64], voff[j], j0 * 2);
   };
   // q8_0: one 16-int8 chunk of K and of V per thread (and its scales), held in registers.
+  // A tile's positions are all below the cache capacity (a multiple of the tile), so every
+  // thread loads its chunk unconditionally: the same loads for every tile, which keeps the
+  // compiler's load-count waits exact while the next tiles are in flight.
   constexpr int KQ = KVT * (HD / 16), VQ = HD * (KVT / 16);   // int8 chunks per tile
+  static_assert(!Q8 || (KQ <= AW * 64 && VQ <= AW * 64), "at most one K and one V chunk per thread");
+  constexpr bool all_k = KQ == AW * 64, all_v = VQ == AW * 64;   // every thread has one
   const int8_t* Kq = reinterpret_cast<const int8_t*>(a.kv.k) + (int64_t)g * n_ctx * HD;
   const int8_t* Vq = reinterpret_cast<const int8_t*>(a.kv.v) + (int64_t)g * HD * n_ctx;
   const uint16_t* Kd = a.kv.kd + (int64_t)g * n_ctx * (HD / QK);
   const uint16_t* Vd = a.kv.vd + (int64_t)g * (HD / QK) * n_ctx;
-  uint4 qk_raw = make_uint4(0, 0, 0, 0), qv_raw = make_uint4(0, 0, 0, 0);
-  uint16_t qk_sc = 0;
-  uint4 qv_sc0 = make_uint4(0, 0, 0, 0), qv_sc1 = make_uint4(0, 0, 0, 0);
-  auto load_q8 = [&](int jt) __attribute__((always_inline)) {
+  const int qk_row = tid / (HD / 16), qk_c16 = tid % (HD / 16);
+  const int qv_d = tid / (KVT / 16), qv_c16 = tid % (KVT / 16);
+  struct Q8Regs { uint4 k, v, vs0, vs1; uint16_t ks; };
+  auto load_q8 = [&](int jt, Q8Regs& r) __attribute__((always_inline)) {
     const int j0 = jt * KVT;
-    if (tid < KQ) {
-      const int row = tid / (HD / 16), c16 = tid % (HD / 16);
-      const int pos = j0 + row;
-      if (pos < kv_end) {
-        qk_raw = *reinterpret_cast<const uint4*>(Kq + (int64_t)pos * HD + c16 * 16);
-        qk_sc = Kd[(int64_t)pos * (HD / QK) + c16 / 2];
-      } else {
-        qk_raw = make_uint4(0, 0, 0, 0);
-        qk_sc = 0;
-      }
+    if (all_k || tid < KQ) {
+      const int pos = j0 + qk_row;
+      r.k = *reinterpret_cast<const uint4*>(Kq + (int64_t)pos * HD + qk_c16 * 16);
+      r.ks = Kd[(int64_t)pos * (HD / QK) + qk_c16 / 2];
     }
-    if (tid < VQ) {
-      const int d = tid / (KVT / 16), c16 = tid % (KVT / 16);
-      const int pos0 = j0 + c16 * 16;
-      const int8_t* src = Vq + (int64_t)d * n_ctx + pos0;
-      const uint16_t* sd = Vd + (int64_t)(d / QK) * n_ctx + pos0;
-      if (pos0 + 16 <= kv_end) {
-        qv_raw = *reinterpret_cast<const uint4*>(src);
-        qv_sc0 = *reinterpret_cast<const uint4*>(sd);
-        qv_sc1 = *reinterpret_cast<const uint4*>(sd + 8);
-      } else {
-        uint32_t w[4] = {0, 0, 0, 0}, s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int e = 0; e < 16; ++e) {
-          if (pos0 + e < kv_end) {
-            w[e >> 2] |= (uint32_t)(uint8_t)src[e] << (8 * (e & 3));
-            s[e >> 1] |= (uint32_t)sd[e] << (16 * (e & 1));
-          }
-        }
-        qv_raw = make_uint4(w[0], w[1], w[2], w[3]);
-        qv_sc0 = make_uint4(s[0], s[1], s[2], s[3]);
-        qv_sc1 = make_uint4(s[4], s[5], s[6], s[7]);
-      }
+    if (all_v || tid < VQ) {
+      const int pos0 = j0 + qv_c16 * 16;
+      r.v = *reinterpret_cast<const uint4*>(Vq + (int64_t)qv_d * n_ctx + pos0);
+      const uint16_t* sd = Vd + (int64_t)(qv_d / QK) * n_ctx + pos0;
+      r.vs0 = *reinterpret_cast<const uint4*>(sd);
+      r.vs1 = *reinterpret_cast<const uint4*>(sd + 8);
     }
   };
   // Dequantisation into LDS: packed fp16, each value the correctly rounded fp16 of d*q.
-  auto store_q8 = [&](uint4* kb, uint4* vb) __attribute__((always_inline)) {
-    if (tid < KQ) {
-      const int row = tid / (HD / 16), c16 = tid % (HD / 16);
-      const int sw = row % NCH;
+  // V positions at or past kv_end are stored as zeros (their probabilities are zero; this
+  // keeps whatever the cache holds there out of the product).  K rows there need no
+  // care: their scores are masked to -inf.
+  auto store_q8 = [&](const Q8Regs& r, int jt, uint4* kb, uint4* vb) __attribute__((always_inline)) {
+    if (all_k || tid < KQ) {
+      const int sw = qk_row % NCH;
       uint4 lo, hi;
-      dequant16_f16(qk_raw, qk_sc, lo, hi);
-      kb[row * NCH + ((2 * c16) ^ sw)] = lo;
-      kb[row * NCH + ((2 * c16 + 1) ^ sw)] = hi;
+      dequant16_f16(r.k, r.ks, lo, hi);
+      kb[qk_row * NCH + ((2 * qk_c16) ^ sw)] = lo;
+      kb[qk_row * NCH + ((2 * qk_c16 + 1) ^ sw)] = hi;
     }
-    if (tid < VQ) {
-      const int d = tid / (KVT / 16), c16 = tid % (KVT / 16);
-      const int sw = vswz(d);
+    if (all_v || tid < VQ) {
+      uint4 qv = r.v, s0 = r.vs0, s1 = r.vs1;
+      const int nv = kv_end - (jt * KVT + qv_c16 * 16);   // valid positions of the chunk
+      if (nv < 16) {
+        auto keep = [&](int first, int per) -> uint32_t {   // mask of the valid lanes of a dword
+          const int k = min(max(nv - first, 0), 32 / per);
+          return k >= 32 / per ? 0xFFFFFFFFu : (1u << (per * k)) - 1u;
+        };
+        qv.x &= keep(0, 8); qv.y &= keep(4, 8); qv.z &= keep(8, 8); qv.w &= keep(12, 8);
+        s0.x &= keep(0, 16); s0.y &= keep(2, 16); s0.z &= keep(4, 16); s0.w &= keep(6, 16);
+        s1.x &= keep(8, 16); s1.y &= keep(10, 16); s1.z &= keep(12, 16); s1.w &= keep(14, 16);
+      }
+      const int sw = vswz(qv_d);
       uint4 lo, hi;
-      dequant16_f16_scales(qv_raw, qv_sc0, qv_sc1, lo, hi);
-      vb[d * 8 + ((2 * c16) ^ sw)] = lo;
-      vb[d * 8 + ((2 * c16 + 1) ^ sw)] = hi;
+      dequant16_f16_scales(qv, s0, s1, lo, hi);
+      vb[qv_d * 8 + ((2 * qv_c16) ^ sw)] = lo;
+      vb[qv_d * 8 + ((2 * qv_c16 + 1) ^ sw)] = hi;
     }
   };
 
@@ -396,17 +392,38 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
       }
       attn_wait_vm0();
     } else {
-      // NB = 2: the next tile is loaded to registers during the arithmetic, dequantised after
-      // it (no asynchronous LDS writes here, so the buffer is picked at run time)
-      load_q8(jt0);
-      store_q8(sK0, sV0);
-      for (int t = jt0; t < jt1; ++t) {
-        const bool odd = (t - jt0) & 1;
-        __syncthreads();               // tile t in LDS; the buffer of t+1 is free
-        if (t + 1 < jt1) load_q8(t + 1);
-        compute(odd ? sK1 : sK0, odd ? sV1 : sV0, t * KVT);
-        if (t + 1 < jt1) store_q8(odd ? sK0 : sK1, odd ? sV0 : sV1);
+      // NB = 2 LDS buffers and two register sets: tile t+2 is loaded to registers while tile
+      // t is computed, and tile t+1 (loaded one step earlier) is dequantised into the other
+      // buffer after it, so a tile's loads have two tiles' arithmetic to land.  Every step
+      // issues the same loads and stores (past the range they repeat the last tile, and
+      // only the arithmetic is skipped), so the compiler's load-count waits stay exact; the
+      // barrier waits only for this wave's LDS writes, not for the loads in flight.
+      auto barrier = [&]() __attribute__((always_inline)) {
+        attn_cfence();
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        attn_cfence();
+      };
+      const int t0 = __builtin_amdgcn_readfirstlane(jt0);
+      const int tl = __builtin_amdgcn_readfirstlane(last);
+      const int npairs = __builtin_amdgcn_readfirstlane((jt1 - jt0 + 1) / 2);
+      Q8Regs ra, rb;
+      load_q8(t0, ra);
+      load_q8(min(t0 + 1, tl), rb);
+      store_q8(ra, t0, sK0, sV0);
+      attn_wait_vm0();                 // (the Q fragments too: nothing older is in flight)
+      for (int pr = 0; pr < npairs; ++pr) {
+        const int t = t0 + 2 * pr;
+        barrier();                     // tile t in buffer 0; buffer 1 is free
+        load_q8(min(t + 2, tl), ra);
+        compute(sK0, sV0, t * KVT);
+        store_q8(rb, min(t + 1, tl), sK1, sV1);
+        barrier();                     // tile t+1 in buffer 1; buffer 0 is free
+        load_q8(min(t + 3, tl), rb);
+        if (t + 1 <= tl) compute(sK1, sV1, (t + 1) * KVT);
+        store_q8(ra, min(t + 2, tl), sK0, sV0);
       }
+      attn_wait_vm0();
     }
   }
   l += __shfl_xor(l, 32, 64);          // per-lane partial sums -> row sum
