@@ -268,7 +268,11 @@ def build_cache(torch, cpa, Hq, Hkv, hd, kv, T, seed, k_gain=None):
 @pytest.mark.parametrize("hd,Hq,Hkv,n,start,splits", [
     (64, 4, 2, 40, 0, 0), (64, 4, 2, 33, 100, 0), (128, 40, 8, 70, 300, 0),
     (128, 40, 8, 128, 700, 5), (128, 32, 4, 200, 0, 0), (128, 8, 8, 1, 250, 0),
-    (128, 40, 8, 300, 1234, 1), (128, 40, 8, 256, 1000, 3), (64, 8, 2, 3, 900, 6)])
+    (128, 40, 8, 300, 1234, 1), (128, 40, 8, 256, 1000, 3), (64, 8, 2, 3, 900, 6),
+    # decode-sized chunks: one token deep in the cache, three tokens, two tokens of a G = 8
+    # model, head_dim 64 with a ragged last tile, the most forced splits (32) over few tiles
+    (128, 40, 8, 1, 17000, 0), (128, 40, 8, 3, 5000, 0), (128, 32, 4, 2, 100, 0),
+    (64, 4, 2, 8, 333, 0), (128, 40, 8, 2, 1000, 32)])
 def test_attention_matches_oracle(torch, cpa, kv, hd, Hq, Hkv, n, start, splits):
     log(f"attention kv={kv} hd={hd} Hq={Hq} Hkv={Hkv} n={n} start={start} splits={splits}")
     T = start + n
@@ -285,14 +289,16 @@ def test_attention_matches_oracle(torch, cpa, kv, hd, Hq, Hkv, n, start, splits)
 
 
 @pytest.mark.parametrize("kv", ["f16", "q8_0"])
-def test_attention_keys_of_one_lane_half_dominate(torch, cpa, kv):
-    """Keys whose position has bit 3 set get 8x larger K rows, so in every 16-key group the
-    scores one half of the lanes holds exceed the other half's by far more than fp16 can
-    carry: the running maximum must combine both lane halves of each query row."""
-    hd, Hq, Hkv, n, start = 128, 40, 8, 96, 160
+@pytest.mark.parametrize("n,bit", [(96, 8), (1, 8), (3, 8)])
+def test_attention_keys_of_one_lane_half_dominate(torch, cpa, kv, n, bit):
+    """Keys whose position has the given bit set get 8x larger K rows, so the scores one
+    half of the lanes holds exceed the other half's by far more than fp16 can carry: the
+    running maximum must combine both lane halves of each query row, which split each
+    16-key group by bit 3 of the position; chunks of 96, 1 and 3 tokens."""
+    hd, Hq, Hkv, start = 128, 40, 8, 160
     T = start + n
-    gain = np.where((np.arange(T) & 8) != 0, 8.0, 1.0)
-    log(f"attention kv={kv} with dominant keys at positions with bit 3 set")
+    gain = np.where((np.arange(T) & bit) != 0, 8.0, 1.0)
+    log(f"attention kv={kv} n={n} with dominant keys at positions with bit {bit} set")
     q_all, kvbuf, qf, Kv, Vv = build_cache(torch, cpa, Hq, Hkv, hd, kv, T,
                                            synth.tensor_seed("att-half", T), k_gain=gain)
     q = q_all[start:].contiguous()
