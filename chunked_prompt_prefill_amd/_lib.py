@@ -78,7 +78,8 @@ SIGNATURES = {
     "cp_test_router": (ctypes.c_int, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
                                       c_vp, c_vp]),
     "cp_test_gemm_scratch_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32]),
-    "cp_test_gemm_plan": (ctypes.c_int, [c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]),
+    "cp_test_gemm_plan": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]),
+    "cp_test_set_plan_shared": (ctypes.c_int, [c_vp, c_i32]),
     "cp_test_gemm": (ctypes.c_int, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
                                     c_vp]),
     "cp_test_gemm_scratch_bytes_ex": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),

@@ -217,9 +217,22 @@ bool skinny_fits(int M, int N) { return M <= kSkinnyMaxRows && N % 64 == 0; }
 // force_mt > 0 pins the row tile (tests; 1 = the weight-streaming kernel, which needs
 // M <= kSkinnyMaxRows and N % 64 == 0); force_splits > 0 forces one launch with that
 // split-K factor.
-GemmPlan plan_gemm(int M, int N, int K, int force_splits = 0, int force_mt = 0) {
+//
+// shared: the launch shares the device with other chunks in flight (prefill_chunks with
+// several lanes).  Their kernels fill the CUs a launch leaves idle, so rounds and tails no
+// longer decide; what a split still buys is a shorter workgroup on a narrow launch, at the
+// price of partial sums and padding stages.  Chunks of more than 128 rows then take one
+// launch of 256-row tiles, unsplit when its tiles cover three quarters of the CUs, else
+// in two K splits.  (Measured with three lanes against the single-lane plans and other
+// fixed split counts: +9% at 512-row chunks, +2% at 2048, +1% at 3328.)
+constexpr int kSharedUnsplitTiles = 192;
+GemmPlan plan_gemm(int M, int N, int K, int force_splits = 0, int force_mt = 0, bool shared = false) {
   if (force_mt == 1 || (force_mt == 0 && skinny_fits(M, N))) return plan_gemm_skinny(M, N, K, force_splits);
   if (force_mt > 0) return plan_gemm_mt(M, N, K, force_mt, force_splits);
+  if (shared && M > 128 && force_splits == 0) {
+    const int64_t T = ceil_div(M, 256) * ceil_div(N, 256);
+    return plan_gemm_mt(M, N, K, 256, T >= kSharedUnsplitTiles ? 1 : 2);
+  }
   if (M <= 64) return plan_gemm_mt(M, N, K, 64, force_splits);
   GemmPlan best = plan_gemm_mt(M, N, K, 128, force_splits);
   if (M <= 128) {
@@ -317,7 +330,9 @@ size_t max_partial_bytes(const Dims& D) {
   const int Ks[4] = {D.d, D.Dq, D.d, D.moe ? 0 : D.Fp};
   for (int g = 0; g < 4; ++g) {
     if (!Ns[g] || !Ks[g]) continue;
-    for (int M = 1; M <= D.Cm; ++M) best = std::max(best, plan_gemm(M, Ns[g], Ks[g]).partial_bytes);
+    for (int M = 1; M <= D.Cm; ++M)
+      for (const bool shared : {false, true})
+        best = std::max(best, plan_gemm(M, Ns[g], Ks[g], 0, 0, shared).partial_bytes);
   }
   return best;
 }
@@ -437,6 +452,7 @@ struct cp_ctx {
   WsLayout WS;
   hipStream_t stream = nullptr;
   PendingSum pend_x;            // split-K sums into the chunk's x not yet added
+  bool plan_shared = false;      // GEMM launch plans for a device shared with other lanes
   uint8_t* warena = nullptr;
   uint8_t* kv = nullptr;
   uint8_t* ws = nullptr;
@@ -509,7 +525,7 @@ hipError_t timed(cp_ctx* c, const char* cls, F&& launch) {
 constexpr int kDeferMinRows = 64;
 hipError_t gemm(cp_ctx* c, const char* cls, const _Float16* A, int lda, int M, const QMat& W,
                 int mode, void* out, int ldo, PendingSum* defer = nullptr) {
-  const GemmPlan p = plan_gemm(M, W.N, W.K);
+  const GemmPlan p = plan_gemm(M, W.N, W.K, 0, 0, c->plan_shared);
   if (defer) *defer = PendingSum();
   return timed(c, cls, [&] {
     for (int i = 0; i < p.nparts; ++i) {
@@ -921,7 +937,10 @@ int prefill_chunks(cp_ctx* c, const float* x_in, float* x_out, int32_t n_tokens,
     lanes[j] = {(hipStream_t)hip_streams[j - 1], (uint8_t*)workspaces[j - 1] + c->WS.stage};
   const hipStream_t saved_stream = c->stream;
   uint8_t* const saved_stage = c->stage;
-  auto restore = [&] { c->stream = saved_stream; c->stage = saved_stage; c->pend_x = PendingSum(); };
+  const bool saved_shared = c->plan_shared;
+  auto restore = [&] {
+    c->stream = saved_stream; c->stage = saved_stage; c->pend_x = PendingSum(); c->plan_shared = saved_shared;
+  };
   const int K = (n_tokens + chunk - 1) / chunk;
   const int used = std::min(n_lanes, K);
   // the other lanes start after the work already on the context's stream
@@ -929,6 +948,7 @@ int prefill_chunks(cp_ctx* c, const float* x_in, float* x_out, int32_t n_tokens,
   CP_HIP(c, hipEventRecord(join, lanes[0].stream), "event record");
   for (int j = 1; j < used; ++j) CP_HIP(c, hipStreamWaitEvent(lanes[j].stream, join, 0), "stream wait");
   const int start0 = c->n_past;
+  if (n_lanes > 1) c->plan_shared = true;     // restored with the rest
   // Chunk i runs on lane i mod n_lanes, its layers in order; its layer l starts once chunk
   // i-1 (the previous lane) has finished layer l, whose cache rows it attends to.  So while
   // chunk i runs layer l, chunk i+1 runs layer l-1, and so on.  A lane runs its chunks
@@ -1089,6 +1109,12 @@ void prefill_free(cp_ctx* c) {
   for (auto e : c->pool) hipEventDestroy(e);
   for (auto e : c->wave_ev) hipEventDestroy(e);
   delete c;
+}
+
+int cp_test_set_plan_shared(cp_ctx* c, int32_t shared) {
+  if (!c || (shared != 0 && shared != 1)) return CP_E_INVALID;
+  c->plan_shared = shared != 0;
+  return CP_OK;
 }
 
 int cp_kernel_timing(cp_ctx* c, const char* classes) {
@@ -1291,9 +1317,9 @@ int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, 
   return cp_test_gemm_ex(A, W, M, N, K, mode, splits, 0, out, work, stream);
 }
 
-int cp_test_gemm_plan(int32_t M, int32_t N, int32_t K, int32_t* out6) {
+int cp_test_gemm_plan(int32_t M, int32_t N, int32_t K, int32_t shared, int32_t* out6) {
   if (!out6 || M < 1 || N < 32 || K < 128) return CP_E_INVALID;
-  const GemmPlan p = plan_gemm(M, N, K);
+  const GemmPlan p = plan_gemm(M, N, K, 0, 0, shared != 0);
   out6[0] = p.mt; out6[1] = p.nparts;
   for (int i = 0; i < 2; ++i) {
     out6[2 + 2 * i] = i < p.nparts ? p.part[i].n0 : 0;

@@ -189,6 +189,11 @@ class PrefillContext:
     def last_error(self) -> str:
         return self.L.prefill_last_error(self._ctx).decode()
 
+    def set_plan_shared(self, shared: bool):
+        """GEMM launch plans of later single-chunk calls: those prefill_chunks uses with
+        several lanes (True) or the single-lane ones (False, the default)."""
+        self._check(self.L.cp_test_set_plan_shared(self._ctx, int(shared)))
+
     def cp_kernel_timing(self, classes: Optional[str]):
         """None: off; "*": every class; else comma-separated class names."""
         self._check(self.L.cp_kernel_timing(self._ctx, None if classes is None else classes.encode()))
@@ -302,10 +307,11 @@ def cp_test_gemm(A, W, M, N, K, mode, splits, out, row_tile=0):
         raise PrefillError(rc, "cp_test_gemm failed")
 
 
-def cp_test_gemm_plan(M, N, K):
-    """(row tile, [(first column, split-K factor), ...]) of the layer's launch plan."""
+def cp_test_gemm_plan(M, N, K, shared=False):
+    """(row tile, [(first column, split-K factor), ...]) of the layer's launch plan, on a
+    device of its own or (shared) beside other chunks in flight."""
     out = (ctypes.c_int32 * 6)()
-    rc = lib().cp_test_gemm_plan(M, N, K, out)
+    rc = lib().cp_test_gemm_plan(M, N, K, int(shared), out)
     if rc != CP_OK:
         raise PrefillError(rc, "cp_test_gemm_plan failed")
     return out[0], [(out[2 + 2 * i], out[3 + 2 * i]) for i in range(out[1])]

@@ -133,8 +133,8 @@ int prefill_init(const cp_config* cfg, const cp_layer_weights* layers, void* wei
 int prefill_chunk(cp_ctx* ctx, const float* x_in, float* x_out, int32_t n_tokens);
 
 /* A prompt of n_tokens rows read in consecutive chunks of `chunk` tokens (the last one
- * shorter): the same work and the same result, bit for bit, as calling prefill_chunk for
- * each chunk in turn, with up to n_lanes chunks in flight on one device.  This is the
+ * shorter): the work of calling prefill_chunk for each chunk in turn, with up to n_lanes
+ * chunks in flight on one device.  This is the
  * lane scheme of the llama.cpp "--split-overlap" pull request (section "How"):
  * consecutive chunks alternate between lanes, each with its own stream and its own
  * per-chunk buffers, sharing the weights and the KV cache, and a lane's step waits by
@@ -143,9 +143,13 @@ int prefill_chunk(cp_ctx* ctx, const float* x_in, float* x_out, int32_t n_tokens
  * the others leave idle (launch tails, small kernels, the gaps between launches).
  * Chunk i runs on lane i % n_lanes (lane 0 is the context's stream and workspace), its
  * layers in order; its layer l starts once chunk i-1 has finished layer l, whose cache
- * rows it attends to, so while one chunk runs layer l the next runs layer l-1.
+ * rows it attends to, so while one chunk runs layer l the next runs layer l-1.  With two
+ * or more lanes the GEMMs of chunks above 128 tokens take launch plans sized for a shared
+ * device (fewer K splits; see cp_test_set_plan_shared), so the result equals prefill_chunk
+ * per chunk up to the order of the split-K sums, and bitwise equals prefill_chunk per
+ * chunk under the shared plans.
  *   x_in, x_out: dev float32 [n_tokens][d_model], 16-byte aligned; x_out may equal x_in.
- *   n_lanes: 1 .. 8 (1: prefill_chunk for each chunk in turn).
+ *   n_lanes: 1 .. 8 (1: prefill_chunk for each chunk in turn, with the context's plans).
  *   workspaces[j], hip_streams[j] (j < n_lanes - 1): lane j+1's buffers (dev,
  *     cp_workspace_bytes(cfg) bytes each, 256-byte aligned; the context's own workspace
  *     keeps the RoPE tables) and stream (not the context's, all distinct, default
@@ -235,6 +239,14 @@ int kv_cache_truncate(cp_ctx* ctx, int32_t n_keep);
 int32_t prefill_n_past(const cp_ctx* ctx);
 const char* prefill_last_error(const cp_ctx* ctx);
 void prefill_free(cp_ctx* ctx);   /* releases host-side state only; buffers stay the caller's */
+
+/* The GEMM launch plans of later prefill_chunk / prefill_chunk_trace / prefill_chunk_timed
+ * calls on this context: shared = 1 takes the plans prefill_chunks uses with several
+ * lanes (sized for a device shared with other chunks in flight), 0 (the default) the
+ * single-lane plans.  Both give the same result up to the order of the split-K sums; a
+ * chunk's result under one plan is bitwise the same whether or not other chunks run
+ * beside it.  CP_E_INVALID for a NULL context or shared outside {0, 1}. */
+int cp_test_set_plan_shared(cp_ctx* ctx, int32_t shared);
 
 /* Per-kernel timing.  classes: NULL turns timing off; "*" times every kernel class; else
  * a comma-separated list of class names.  While on, every launch of a selected class is
@@ -347,10 +359,11 @@ int cp_test_router(const float* y, const void* w_router, int32_t n, int32_t d, i
  * buffer of cp_test_gemm_scratch_bytes(M, N, K, splits) bytes (repacked weights and
  * partial sums). */
 size_t cp_test_gemm_scratch_bytes(int32_t M, int32_t N, int32_t K, int32_t splits);
-/* The launch plan the layer uses for an M x N x K GEMM (host only): out6 = {row tile (1 =
- * the weight-streaming kernel), number of launches, first column of launch 0, its split-K
- * factor, first column of launch 1, its split-K factor}. */
-int cp_test_gemm_plan(int32_t M, int32_t N, int32_t K, int32_t* out6);
+/* The launch plan the layer uses for an M x N x K GEMM (host only), with shared = 0 on a
+ * device of its own, shared = 1 beside other chunks in flight (prefill_chunks with several
+ * lanes): out6 = {row tile (1 = the weight-streaming kernel), number of launches, first
+ * column of launch 0, its split-K factor, first column of launch 1, its split-K factor}. */
+int cp_test_gemm_plan(int32_t M, int32_t N, int32_t K, int32_t shared, int32_t* out6);
 int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
                  int32_t splits, void* out, void* scratch, void* hip_stream);
 /* Same with the row tile pinned: row_tile 64 or 128 runs the kernel that keeps two

@@ -128,6 +128,21 @@ def test_gemm_launch_plans_cover_the_columns(cpa, M, N, K):
         assert mt != 128 or M > 64
 
 
+@pytest.mark.parametrize("M", [1, 4, 64, 128, 129, 300, 512, 2048, 3328, 8192])
+@pytest.mark.parametrize("N,K", [(34816, 5120), (5120, 17408), (7168, 5120), (5120, 5120), (5120, 2048),
+                                 (2048, 4096), (256, 256)])
+def test_gemm_launch_plans_beside_other_chunks(cpa, M, N, K):
+    """The plans of a device shared with other chunks in flight (host only): chunks of up
+    to 128 rows keep the single-lane plan; larger ones take one launch of 256-row tiles,
+    unsplit when the tiles number 192 or more, else two K splits."""
+    shared = cpa.cp_test_gemm_plan(M, N, K, shared=True)
+    if M <= 128:
+        assert shared == cpa.cp_test_gemm_plan(M, N, K)
+        return
+    tiles = -(-M // 256) * -(-N // 256)
+    assert shared == (256, [(0, 1 if tiles >= 192 else 2)])
+
+
 def test_chunk_limit_of_the_gemm_operand_offsets(cpa):
     """The GEMMs address their fp16 input with 32-bit byte offsets: a chunk whose widest
     operand (the dense FFN intermediate, 17,408 columns at the 27B-class shapes) reaches

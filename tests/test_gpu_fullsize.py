@@ -10,7 +10,10 @@ thousands of tokens in seconds, so the checks are:
   * properties that hold at any size: every layer's output is finite, a second run of
     the same chunks is bitwise identical, and the saved state restores byte-identically.
 Layer 0's weights are encoded by the oracle; the deeper layers, which only the property
-checks see, are generated and encoded on the GPU as the benchmark does.
+checks see, are generated and encoded on the GPU as the benchmark does.  The whole-prompt
+runs take the GEMM launch plans of the benchmark's timed steps (a device shared by several
+chunks in flight: cp_test_set_plan_shared), the chunk-size sweep those of its one-lane
+sweep.
 """
 import numpy as np
 import pytest
@@ -67,7 +70,7 @@ def layer0_kv_values(blob, n_tokens):
 class FullRun:
     """The workload's whole share on the GPU; layer 0 from oracle-encoded bytes."""
 
-    def __init__(self, torch, w, n_ctx, chunk_max):
+    def __init__(self, torch, w, n_ctx, chunk_max, shared_plans=False):
         import chunked_prompt_prefill_amd as cpa
         self.torch, self.cpa, self.w = torch, cpa, w
         log(f"{w.name}: encoding layer 0 with the oracle")
@@ -76,6 +79,7 @@ class FullRun:
         torch.cuda.synchronize()
         self.cfg = cpa.make_config(w, n_ctx, chunk_max)
         self.ctx = cpa.PrefillContext(self.cfg, dev)
+        self.ctx.set_plan_shared(shared_plans)
         self.dev = dev
 
     def run(self, x_dev, out, chunks, lo=None, ro=None, n_total=0):
@@ -119,7 +123,8 @@ def check_layer0_cache(blob, cache, n_tokens):
 def whole_prompt(torch, w, kv_state_check=False):
     n, C = w.n_prompt, w.chunk
     log(f"{w.name}: {w.n_layer} layers, {n} tokens in chunks of {C}, {w.kv_type} cache")
-    fr = FullRun(torch, w, n, C)
+    # the launch plans of the benchmark's timed steps (several chunks in flight)
+    fr = FullRun(torch, w, n, C, shared_plans=True)
     x = synth.prompt_inputs(w)
     xd = torch.from_numpy(x).cuda()
     out = torch.empty_like(xd)
@@ -144,6 +149,7 @@ def whole_prompt(torch, w, kv_state_check=False):
     assert torch.equal(out, out2)
     if kv_state_check:
         ctx2 = fr.cpa.PrefillContext(fr.cfg, fr.dev)
+        ctx2.set_plan_shared(True)
         assert ctx2.kv_cache_set_state(blob) == 0 and ctx2.n_past == n
         assert ctx2.kv_cache_get_state() == blob
         log(f"  state of {len(blob)} bytes restores byte-identically")

@@ -1,8 +1,10 @@
 """prefill_chunks (several chunks in flight on several streams) against prefill_chunk in
 turn (GPU).
 
-Both run the same kernels in the same launch plans on the same rows; only the order in
-which chunks and layers overlap differs, and every cross-chunk dependency (a chunk's
+With several lanes prefill_chunks takes the GEMM launch plans of a shared device; the
+reference runs prefill_chunk per chunk under the same plans (cp_test_set_plan_shared).
+Both then run the same kernels in the same launch plans on the same rows; only the order
+in which chunks and layers overlap differs, and every cross-chunk dependency (a chunk's
 layer reads the cache rows the previous chunk wrote at that layer) is ordered by events.
 So outputs, n_past and the cache state must be bitwise equal, for dense and routed
 layers, both cache types, two to eight lanes, chunk counts that are and are not a
@@ -40,6 +42,7 @@ def compare(torch, w, n, chunk, prefix=0, in_place=False, lanes=2):
     chunk = min(chunk, prefix + n)
     cfg = cpa.make_config(w, prefix + n, chunk)
     ref = cpa.PrefillContext(cfg, layers)
+    ref.set_plan_shared(lanes > 1)
     lan = cpa.PrefillContext(cfg, layers, stream=torch.cuda.Stream())
     x = torch.from_numpy(synth.prompt_inputs(w, prefix + n)).cuda()
     torch.cuda.synchronize()          # x is read on the contexts' own streams
@@ -65,6 +68,7 @@ def compare(torch, w, n, chunk, prefix=0, in_place=False, lanes=2):
     assert lan.kv_cache_get_state() == ref.kv_cache_get_state()
     ref.close()
     lan.close()
+    return out
 
 
 @pytest.mark.parametrize("kv,lanes", [("f16", 2), ("q8_0", 2), ("f16", 3)])
@@ -72,6 +76,19 @@ def test_lanes_equal_sequential_dense(torch, kv, lanes):
     """Two layers of the 27B-class dense shapes: 5 chunks of 512 and a ragged sixth."""
     w = synth.WORKLOADS["dense27b_sweep"].with_(n_layer=2, kv_type=kv)
     compare(torch, w, 5 * 512 + 137, 512, lanes=lanes)
+
+
+def test_shared_plans_agree_with_single_lane_plans(torch):
+    """The shared-device plans (fewer K splits) change only the order of the split-K sums:
+    three lanes against prefill_chunk per chunk under the single-lane plans, two layers of
+    the dense shapes, to max|d|/max|ref| <= 1e-3."""
+    import numpy as np
+    w = synth.WORKLOADS["dense27b_sweep"].with_(n_layer=2)
+    got = compare(torch, w, 4 * 512, 512, lanes=3).cpu().numpy()
+    single = compare(torch, w, 4 * 512, 512, lanes=1).cpu().numpy()
+    e = float(np.max(np.abs(got - single)) / np.max(np.abs(single)))
+    log(f"  shared against single-lane plans: max rel diff {e:.3e}")
+    assert 0 < e <= 1e-3      # (0 would mean the plans did not differ)
 
 
 def test_lanes_equal_sequential_routed_experts(torch):
