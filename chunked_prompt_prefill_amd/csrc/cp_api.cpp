@@ -253,8 +253,16 @@ GemmPlan plan_gemm(int M, int N, int K, int force_splits = 0, int force_mt = 0, 
 // workgroups and divide the 64-key tiles each one walks, and add a combine pass that
 // reads the s partial rows.  The factor minimises rounds x tiles per workgroup (the
 // longest query tile's range) plus that pass.
-int attn_splits(const Dims& D, int n, int start) {
+//
+// shared (prefill_chunks with several lanes): the other lanes' kernels fill the CUs an
+// unsplit launch leaves idle, so once the unsplit grid has kSharedAttnUnsplit workgroups
+// or more the combine pass and its partial rows are not worth it (measured with three
+// lanes: +3.6% on the routed-expert share at 3328-token chunks, +2.5% on the q8_0 share at
+// 2048, even at 512); decode-sized chunks, a handful of workgroups, still split.
+constexpr int64_t kSharedAttnUnsplit = 64;
+int attn_splits(const Dims& D, int n, int start, bool shared = false) {
   const int64_t base = ceil_div((int64_t)n * D.G, 256) * D.Hkv;
+  if (shared && base >= kSharedAttnUnsplit) return 1;
   const int kvt = (int)ceil_div(start + n, 64);
   const double t_tile = 1.5e-6;                              // one tile, one workgroup
   const double part = (double)n * D.Hq * D.hd * 4;          // fp32 partial rows of a split
@@ -586,7 +594,7 @@ int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int sta
   // at most the splits whose partial rows the workspace holds (sized for the deepest
   // chunk of each length)
   const int64_t rows1 = (int64_t)D.Hkv * n * D.G;
-  aa.splits = (int)std::max<int64_t>(1, std::min<int64_t>(attn_splits(D, n, start),
+  aa.splits = (int)std::max<int64_t>(1, std::min<int64_t>(attn_splits(D, n, start, c->plan_shared),
                                                           (int64_t)c->WS.arows / rows1));
   aa.part_o = c->wsp<float>(c->WS.apo);
   aa.part_ml = c->wsp<float>(c->WS.apml);

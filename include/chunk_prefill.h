@@ -144,10 +144,10 @@ int prefill_chunk(cp_ctx* ctx, const float* x_in, float* x_out, int32_t n_tokens
  * Chunk i runs on lane i % n_lanes (lane 0 is the context's stream and workspace), its
  * layers in order; its layer l starts once chunk i-1 has finished layer l, whose cache
  * rows it attends to, so while one chunk runs layer l the next runs layer l-1.  With two
- * or more lanes the GEMMs of chunks above 128 tokens take launch plans sized for a shared
- * device (fewer K splits; see cp_test_set_plan_shared), so the result equals prefill_chunk
- * per chunk up to the order of the split-K sums, and bitwise equals prefill_chunk per
- * chunk under the shared plans.
+ * or more lanes the kernels take launch plans sized for a shared device (the GEMMs of
+ * chunks above 128 tokens fewer K splits, attention of 64+ workgroups no KV splits; see
+ * cp_test_set_plan_shared), so the result equals prefill_chunk per chunk up to the order
+ * of split sums, and bitwise equals prefill_chunk per chunk under the shared plans.
  *   x_in, x_out: dev float32 [n_tokens][d_model], 16-byte aligned; x_out may equal x_in.
  *   n_lanes: 1 .. 8 (1: prefill_chunk for each chunk in turn, with the context's plans).
  *   workspaces[j], hip_streams[j] (j < n_lanes - 1): lane j+1's buffers (dev,
@@ -240,10 +240,11 @@ int32_t prefill_n_past(const cp_ctx* ctx);
 const char* prefill_last_error(const cp_ctx* ctx);
 void prefill_free(cp_ctx* ctx);   /* releases host-side state only; buffers stay the caller's */
 
-/* The GEMM launch plans of later prefill_chunk / prefill_chunk_trace / prefill_chunk_timed
- * calls on this context: shared = 1 takes the plans prefill_chunks uses with several
- * lanes (sized for a device shared with other chunks in flight), 0 (the default) the
- * single-lane plans.  Both give the same result up to the order of the split-K sums; a
+/* The launch plans (GEMM K splits, attention KV splits) of later prefill_chunk /
+ * prefill_chunk_trace / prefill_chunk_timed calls on this context: shared = 1 takes the
+ * plans prefill_chunks uses with several lanes (sized for a device shared with other
+ * chunks in flight), 0 (the default) the single-lane plans.  Both give the same result up
+ * to the order of the split sums; a
  * chunk's result under one plan is bitwise the same whether or not other chunks run
  * beside it.  CP_E_INVALID for a NULL context or shared outside {0, 1}. */
 int cp_test_set_plan_shared(cp_ctx* ctx, int32_t shared);
