@@ -135,8 +135,10 @@ def dominant_work(w, cpa, chunks):
 def measured_traffic(kernel, per_launch):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 PMC
     readings (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or None when the
-    readings are absent or were taken on another version of the kernel's source."""
+    readings are absent or were taken on another version of the kernel's source or under
+    another launch plan."""
     import hashlib
+    import chunked_prompt_prefill_amd as cpa
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     try:
         with open(path) as f:
@@ -152,16 +154,25 @@ def measured_traffic(kernel, per_launch):
             h.update(f.read())
     if h.hexdigest() != r.get("sources_sha256") or r.get("rows") != per_launch.get("rows"):
         return None
+    if r.get("plan") != plan_record(cpa):
+        return None
     return r.get("hbm_bytes_per_launch")
 
 
-# sources whose text defines the dominant kernel's code: a change to any of them makes the
-# stored counter readings stale (measured_traffic then reports None)
+# sources whose text defines the dominant kernel's code: a change to any of them, or to
+# its launch plan at 512 rows (plan_record), makes the stored counter readings stale
+# (measured_traffic then reports None)
 PMC_SOURCES = ["chunked_prompt_prefill_amd/csrc/k_gemm_big.hip",
                "chunked_prompt_prefill_amd/csrc/k_gemm.hip",
                "chunked_prompt_prefill_amd/csrc/k_common.h",
-               "chunked_prompt_prefill_amd/csrc/cp_internal.h",
-               "chunked_prompt_prefill_amd/csrc/cp_api.cpp"]
+               "chunked_prompt_prefill_amd/csrc/cp_internal.h"]
+
+
+def plan_record(cpa):
+    """The single-lane launch plan of the 512-row gate/up GEMM: [row tile, [[first column,
+    split-K factor], ...]]."""
+    mt, parts = cpa.cp_test_gemm_plan(512, 34816, 5120)
+    return [mt, [list(p) for p in parts]]
 
 
 def pmc_digest(fetch_csv, write_csv, copy_mib):
@@ -204,7 +215,7 @@ def pmc_digest(fetch_csv, write_csv, copy_mib):
         "fetch_factor": ff, "write_factor": fw,
         "hbm_read_bytes_per_launch": kf * 1024 * ff, "hbm_write_bytes_per_launch": kw * 1024 * fw,
         "hbm_bytes_per_launch": kf * 1024 * ff + kw * 1024 * fw,
-        "sources": PMC_SOURCES, "sources_sha256": h.hexdigest()}}
+        "sources": PMC_SOURCES, "sources_sha256": h.hexdigest(), "plan": plan_record(cpa)}}
     with open(os.path.join(ROOT, "profiles", "pmc_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
