@@ -355,13 +355,14 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
           const float msafe = stats(sc, t * KVT);
           qk(bufK(std::integral_constant<int, (j + 1) % 3>{}), sn);
           probs(sc, msafe, pb);
-          // three K fragment reads ahead, then {one MFMA of K Q^T, five VALU of the
-          // softmax, the next fragment read} per MFMA
+          // three K fragment reads ahead, then {one MFMA of K Q^T, one VALU of the
+          // softmax, the next fragment read} per MFMA (the rest of the softmax is scheduled
+          // freely; five VALU per MFMA were 3-5% slower, none 1-2%)
           __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
             if (i < 13) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
           pv(bufV(J), pb);
