@@ -272,7 +272,9 @@ def build_cache(torch, cpa, Hq, Hkv, hd, kv, T, seed, k_gain=None):
     # decode-sized chunks: one token deep in the cache, three tokens, two tokens of a G = 8
     # model, head_dim 64 with a ragged last tile, the most forced splits (32) over few tiles
     (128, 40, 8, 1, 17000, 0), (128, 40, 8, 3, 5000, 0), (128, 32, 4, 2, 100, 0),
-    (64, 4, 2, 8, 333, 0), (128, 40, 8, 2, 1000, 32)])
+    (64, 4, 2, 8, 333, 0), (128, 40, 8, 2, 1000, 32),
+    # 64, 60 and 65 query rows per kv head
+    (128, 8, 2, 16, 2000, 0), (128, 40, 8, 12, 3000, 0), (64, 5, 1, 13, 700, 0)])
 def test_attention_matches_oracle(torch, cpa, kv, hd, Hq, Hkv, n, start, splits):
     log(f"attention kv={kv} hd={hd} Hq={Hq} Hkv={Hkv} n={n} start={start} splits={splits}")
     T = start + n
