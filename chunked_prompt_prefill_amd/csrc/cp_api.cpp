@@ -218,20 +218,25 @@ bool skinny_fits(int M, int N) { return M <= kSkinnyMaxRows && N % 64 == 0; }
 // M <= kSkinnyMaxRows and N % 64 == 0); force_splits > 0 forces one launch with that
 // split-K factor.
 //
-// shared: the launch shares the device with other chunks in flight (prefill_chunks with
-// several lanes).  Their kernels fill the CUs a launch leaves idle, so rounds and tails no
-// longer decide; what a split still buys is a shorter workgroup on a narrow launch, at the
-// price of partial sums and padding stages.  Chunks of more than 128 rows then take one
-// launch of 256-row tiles, unsplit when its tiles cover three quarters of the CUs, else
-// in two K splits.  (Measured with three lanes against the single-lane plans and other
-// fixed split counts: +9% at 512-row chunks, +2% at 2048, +1% at 3328.)
+// plan: kPlanSingle for a device of its own; with other chunks in flight
+// (prefill_chunks with several lanes) kPlanShared, or kPlanSharedDeferred for a GEMM whose
+// split-K sums the next kernel adds as it reads them (the output and down projections),
+// so that splitting adds no pass of its own.  Beside other chunks the CUs a launch leaves
+// idle (a partial round, a narrow launch) are filled by the other lanes' kernels, so rounds
+// and tails no longer decide; what a split still buys is a shorter workgroup on a narrow
+// launch, at the price of partial sums and padding stages.  Chunks of more than 128 rows
+// then take one launch of 256-row tiles: unsplit when its tiles cover three quarters of
+// the CUs or its sums would need a reduction pass, else in two K splits.  (Measured with
+// three lanes against the single-lane plans and fixed split counts: +9% at 512-row
+// chunks, +2% at 2048, +1% at 3328.)
+constexpr int kPlanSingle = 0, kPlanShared = 1, kPlanSharedDeferred = 2;
 constexpr int kSharedUnsplitTiles = 192;
-GemmPlan plan_gemm(int M, int N, int K, int force_splits = 0, int force_mt = 0, bool shared = false) {
+GemmPlan plan_gemm(int M, int N, int K, int force_splits = 0, int force_mt = 0, int plan = kPlanSingle) {
   if (force_mt == 1 || (force_mt == 0 && skinny_fits(M, N))) return plan_gemm_skinny(M, N, K, force_splits);
   if (force_mt > 0) return plan_gemm_mt(M, N, K, force_mt, force_splits);
-  if (shared && M > 128 && force_splits == 0) {
+  if (plan != kPlanSingle && M > 128 && force_splits == 0) {
     const int64_t T = ceil_div(M, 256) * ceil_div(N, 256);
-    return plan_gemm_mt(M, N, K, 256, T >= kSharedUnsplitTiles ? 1 : 2);
+    return plan_gemm_mt(M, N, K, 256, (T >= kSharedUnsplitTiles || plan != kPlanSharedDeferred) ? 1 : 2);
   }
   if (M <= 64) return plan_gemm_mt(M, N, K, 64, force_splits);
   GemmPlan best = plan_gemm_mt(M, N, K, 128, force_splits);
@@ -339,8 +344,8 @@ size_t max_partial_bytes(const Dims& D) {
   for (int g = 0; g < 4; ++g) {
     if (!Ns[g] || !Ks[g]) continue;
     for (int M = 1; M <= D.Cm; ++M)
-      for (const bool shared : {false, true})
-        best = std::max(best, plan_gemm(M, Ns[g], Ks[g], 0, 0, shared).partial_bytes);
+      for (const int plan : {kPlanSingle, kPlanShared, kPlanSharedDeferred})
+        best = std::max(best, plan_gemm(M, Ns[g], Ks[g], 0, 0, plan).partial_bytes);
   }
   return best;
 }
@@ -533,7 +538,10 @@ hipError_t timed(cp_ctx* c, const char* cls, F&& launch) {
 constexpr int kDeferMinRows = 64;
 hipError_t gemm(cp_ctx* c, const char* cls, const _Float16* A, int lda, int M, const QMat& W,
                 int mode, void* out, int ldo, PendingSum* defer = nullptr) {
-  const GemmPlan p = plan_gemm(M, W.N, W.K, 0, 0, c->plan_shared);
+  // (split sums are deferred only for a non-SwiGLU launch of kDeferMinRows rows or more)
+  const bool deferrable = defer && mode != GM_SWIGLU && M >= kDeferMinRows;
+  const GemmPlan p = plan_gemm(M, W.N, W.K, 0, 0,
+                               !c->plan_shared ? kPlanSingle : deferrable ? kPlanSharedDeferred : kPlanShared);
   if (defer) *defer = PendingSum();
   return timed(c, cls, [&] {
     for (int i = 0; i < p.nparts; ++i) {
@@ -1325,9 +1333,9 @@ int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, 
   return cp_test_gemm_ex(A, W, M, N, K, mode, splits, 0, out, work, stream);
 }
 
-int cp_test_gemm_plan(int32_t M, int32_t N, int32_t K, int32_t shared, int32_t* out6) {
-  if (!out6 || M < 1 || N < 32 || K < 128) return CP_E_INVALID;
-  const GemmPlan p = plan_gemm(M, N, K, 0, 0, shared != 0);
+int cp_test_gemm_plan(int32_t M, int32_t N, int32_t K, int32_t plan, int32_t* out6) {
+  if (!out6 || M < 1 || N < 32 || K < 128 || plan < kPlanSingle || plan > kPlanSharedDeferred) return CP_E_INVALID;
+  const GemmPlan p = plan_gemm(M, N, K, 0, 0, plan);
   out6[0] = p.mt; out6[1] = p.nparts;
   for (int i = 0; i < 2; ++i) {
     out6[2 + 2 * i] = i < p.nparts ? p.part[i].n0 : 0;

@@ -307,11 +307,12 @@ def cp_test_gemm(A, W, M, N, K, mode, splits, out, row_tile=0):
         raise PrefillError(rc, "cp_test_gemm failed")
 
 
-def cp_test_gemm_plan(M, N, K, shared=False):
-    """(row tile, [(first column, split-K factor), ...]) of the layer's launch plan, on a
-    device of its own or (shared) beside other chunks in flight."""
+def cp_test_gemm_plan(M, N, K, plan=0):
+    """(row tile, [(first column, split-K factor), ...]) of the layer's launch plan: plan 0
+    on a device of its own, 1 beside other chunks in flight, 2 likewise for a GEMM whose
+    split-K sums the next kernel adds (output and down projections)."""
     out = (ctypes.c_int32 * 6)()
-    rc = lib().cp_test_gemm_plan(M, N, K, int(shared), out)
+    rc = lib().cp_test_gemm_plan(M, N, K, int(plan), out)
     if rc != CP_OK:
         raise PrefillError(rc, "cp_test_gemm_plan failed")
     return out[0], [(out[2 + 2 * i], out[3 + 2 * i]) for i in range(out[1])]

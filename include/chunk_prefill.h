@@ -145,9 +145,9 @@ int prefill_chunk(cp_ctx* ctx, const float* x_in, float* x_out, int32_t n_tokens
  * layers in order; its layer l starts once chunk i-1 has finished layer l, whose cache
  * rows it attends to, so while one chunk runs layer l the next runs layer l-1.  With two
  * or more lanes the kernels take launch plans sized for a shared device (the GEMMs of
- * chunks above 128 tokens fewer K splits, attention of 64+ workgroups no KV splits; see
- * cp_test_set_plan_shared), so the result equals prefill_chunk per chunk up to the order
- * of split sums, and bitwise equals prefill_chunk per chunk under the shared plans.
+ * chunks above 128 tokens at most two K splits, attention of 64+ workgroups no KV splits;
+ * see cp_test_set_plan_shared), so the result equals prefill_chunk per chunk up to the
+ * order of split sums, and bitwise equals prefill_chunk per chunk under the shared plans.
  *   x_in, x_out: dev float32 [n_tokens][d_model], 16-byte aligned; x_out may equal x_in.
  *   n_lanes: 1 .. 8 (1: prefill_chunk for each chunk in turn, with the context's plans).
  *   workspaces[j], hip_streams[j] (j < n_lanes - 1): lane j+1's buffers (dev,
@@ -360,11 +360,13 @@ int cp_test_router(const float* y, const void* w_router, int32_t n, int32_t d, i
  * buffer of cp_test_gemm_scratch_bytes(M, N, K, splits) bytes (repacked weights and
  * partial sums). */
 size_t cp_test_gemm_scratch_bytes(int32_t M, int32_t N, int32_t K, int32_t splits);
-/* The launch plan the layer uses for an M x N x K GEMM (host only), with shared = 0 on a
- * device of its own, shared = 1 beside other chunks in flight (prefill_chunks with several
- * lanes): out6 = {row tile (1 = the weight-streaming kernel), number of launches, first
- * column of launch 0, its split-K factor, first column of launch 1, its split-K factor}. */
-int cp_test_gemm_plan(int32_t M, int32_t N, int32_t K, int32_t shared, int32_t* out6);
+/* The launch plan the layer uses for an M x N x K GEMM (host only).  plan: 0 on a device of
+ * its own; beside other chunks in flight (prefill_chunks with several lanes) 1, or 2 for a
+ * GEMM whose split-K sums the next kernel adds as it reads them (the output and down
+ * projections).  out6 = {row tile (1 = the weight-streaming kernel), number of launches,
+ * first column of launch 0, its split-K factor, first column of launch 1, its split-K
+ * factor}.  CP_E_INVALID for plan outside 0..2. */
+int cp_test_gemm_plan(int32_t M, int32_t N, int32_t K, int32_t plan, int32_t* out6);
 int cp_test_gemm(const void* A, const void* W, int32_t M, int32_t N, int32_t K, int32_t mode,
                  int32_t splits, void* out, void* scratch, void* hip_stream);
 /* Same with the row tile pinned: row_tile 64 or 128 runs the kernel that keeps two

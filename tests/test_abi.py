@@ -134,13 +134,17 @@ def test_gemm_launch_plans_cover_the_columns(cpa, M, N, K):
 def test_gemm_launch_plans_beside_other_chunks(cpa, M, N, K):
     """The plans of a device shared with other chunks in flight (host only): chunks of up
     to 128 rows keep the single-lane plan; larger ones take one launch of 256-row tiles,
-    unsplit when the tiles number 192 or more, else two K splits."""
-    shared = cpa.cp_test_gemm_plan(M, N, K, shared=True)
-    if M <= 128:
-        assert shared == cpa.cp_test_gemm_plan(M, N, K)
-        return
+    unsplit when the tiles number 192 or more or the split sums would need a pass of their
+    own (plan 1), else (plan 2, sums added by the next kernel) two K splits."""
     tiles = -(-M // 256) * -(-N // 256)
-    assert shared == (256, [(0, 1 if tiles >= 192 else 2)])
+    for plan in (1, 2):
+        shared = cpa.cp_test_gemm_plan(M, N, K, plan)
+        if M <= 128:
+            assert shared == cpa.cp_test_gemm_plan(M, N, K)
+            continue
+        assert shared == (256, [(0, 2 if plan == 2 and tiles < 192 else 1)])
+    with pytest.raises(Exception):
+        cpa.cp_test_gemm_plan(M, N, K, 3)
 
 
 def test_chunk_limit_of_the_gemm_operand_offsets(cpa):
