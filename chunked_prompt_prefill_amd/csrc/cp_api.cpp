@@ -79,6 +79,12 @@ std::string validate(const cp_config* c) {
                                               moe ? (int64_t)c->n_chunk_max * c->n_expert_used * Fep * 2 : 0);
     if (a_bytes >= (1LL << 31))
       return "n_chunk_max rows of the widest fp16 GEMM operand must stay below 2 GiB";
+    // The 256-row GEMM kernel addresses a weight matrix's int8 values (N x K bytes) with
+    // 32-bit byte offsets from the matrix's base.
+    const int64_t d = c->d_model, Dq = (int64_t)c->n_head * c->head_dim;
+    const int64_t Nqkv = (int64_t)(c->n_head + 2 * c->n_kv_head) * c->head_dim;
+    const int64_t w_bytes = std::max<int64_t>({Nqkv * d, d * Dq, 2 * Fp * d, moe ? 2 * Fep * d : 0});
+    if (w_bytes >= (1LL << 31)) return "each weight matrix must stay below 2^31 int8 values";
   }
   return "";
 }

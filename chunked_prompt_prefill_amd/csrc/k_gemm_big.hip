@@ -66,6 +66,14 @@ __device__ __forceinline__ void vm_lgkm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
 }
 
+// 16 and 4 bytes through a buffer descriptor (per-lane offset, uniform offset).
+__device__ __forceinline__ u32x4_v buf_load16(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 // Compiler-only fence: memory operations are not moved across it, so the loads a stage
 // issues are counted where the vmcnt waits assume them.
 __device__ __forceinline__ void cfence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
@@ -164,16 +172,19 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_big_kernel(GemmArgs g) {
 
   const int KB = g.K / QK, KQ = g.K / 128;
   const int last32 = g.N / 32 - 1;
-  const uint4* bsrc[2];
-  const uint32_t* ssrc[2];
-#pragma unroll
-  for (int ni = 0; ni < 2; ++ni) {
-    const int64_t n32 = min((n_wave >> 5) + ni, last32);
-    bsrc[ni] = reinterpret_cast<const uint4*>(g.wq + expert * g.wq_estride) + n32 * KB * 64 + lane;
-    // scales: four fp16 per row per 128 columns; a stage takes one 32-bit pair
-    ssrc[ni] = reinterpret_cast<const uint32_t*>(g.wd + expert * g.wd_estride) + (n32 * KQ * 32 + l32) * 2;
-  }
-
+  // W and its scales through buffer descriptors (uniform base and size), with one
+  // per-lane 32-bit offset each; the second column block and the stage are uniform
+  // offsets.  Column blocks past N re-read the last one (not stored).
+  const int n32_0 = min(n_wave >> 5, last32), n32_1 = min((n_wave >> 5) + 1, last32);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.wq + expert * g.wq_estride), (short)0, (int)min((int64_t)g.N * g.K, (int64_t)0x7FFFFFFF), 0x00020000);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.wd + expert * g.wd_estride), (short)0, (int)min((int64_t)g.N * g.K / 16, (int64_t)0x7FFFFFFF),
+      0x00020000);
+  const int32_t woff = n32_0 * KB * 1024 + lane * 16;   // 1 KiB per (32 columns, q8_0 block)
+  // scales: four fp16 per row per 128 columns; a stage takes one 32-bit pair
+  const int32_t soff = (n32_0 * KQ * 32 + l32) * 8;
+  const int32_t wdelta = (n32_1 - n32_0) * KB * 1024, sdelta = (n32_1 - n32_0) * KQ * 256;
   auto bufA = [&](auto J) __attribute__((always_inline)) -> uint4* {
     if constexpr (decltype(J)::value == 0) return sA0;
     else if constexpr (decltype(J)::value == 1) return sA1;
@@ -191,11 +202,11 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_big_kernel(GemmArgs g) {
     constexpr int p = decltype(P)::value;
     if constexpr (p < 4) {
       constexpr int ni = p / 2, kb = p % 2;
-      const u32x4_v v = *(u32x4_g*)(bsrc[ni] + (2 * ks + kb) * 64);
+      const u32x4_v v = buf_load16(wrs, woff, (ni ? wdelta : 0) + (2 * ks + kb) * 1024);
       w.q[ni][kb] = make_uint4(v.x, v.y, v.z, v.w);
     } else if constexpr (p < 6) {
       constexpr int ni = p - 4;
-      w.sc[ni] = *(const __attribute__((address_space(1))) uint32_t*)(ssrc[ni] + (ks >> 1) * 64 + (ks & 1));
+      w.sc[ni] = buf_load4(srs, soff, (ni ? sdelta : 0) + ((ks >> 1) * 64 + (ks & 1)) * 4);
     } else {
       constexpr int j = p - 6;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lptr_t*)&bufA(J)[(4 * j + wave) * 64], 16, aoff[j],

@@ -75,7 +75,10 @@ enum cp_kv_type { CP_KV_F16 = 0, CP_KV_Q8_0 = 1 };
  * head_dim <= 2^31 and, because the GEMMs address their fp16 input with 32-bit byte
  * offsets, n_chunk_max * W * 2 < 2^31 for the widest GEMM input row W = max(d_model,
  * n_head*head_dim, ffn_dim rounded up to 128) (and n_expert_used * expert_ffn_dim
- * rounded up to 128 for routed experts).  Anything else is rejected with CP_E_INVALID
+ * rounded up to 128 for routed experts).  Each weight matrix holds fewer than 2^31
+ * values (N * K < 2^31 for QKV, the output projection, the gate/up pair 2 * ffn_dim
+ * rounded up to 128 by d_model, and one expert's gate/up pair), as the weight tiles are
+ * addressed with 32-bit byte offsets.  Anything else is rejected with CP_E_INVALID
  * (cp_validate_config, cp_config_error). */
 typedef struct cp_config {
   int32_t n_layer, d_model, n_head, n_kv_head, head_dim;

@@ -165,6 +165,18 @@ def test_chunk_limit_of_the_gemm_operand_offsets(cpa):
     assert cpa.validate_config(cpa.make_config(m, lim_m + 1, lim_m + 1)) != ""
 
 
+def test_weight_matrix_limit_of_the_weight_offsets(cpa):
+    """The 256-row GEMM kernel addresses a weight matrix's int8 values with 32-bit byte
+    offsets: the gate/up pair (2 * ffn_dim rounded up to 128, by d_model) must hold fewer
+    than 2^31 values, and a wider FFN is refused at configuration time."""
+    w = synth.WORKLOADS["dense27b_f16"]
+    cfg = cpa.make_config(w, 4096, 512)
+    cfg.ffn_dim = (1 << 31) // (2 * 5120) // 128 * 128        # 209,664: just below
+    assert cpa.validate_config(cfg) == ""
+    cfg.ffn_dim += 128
+    assert "2^31" in cpa.validate_config(cfg)
+
+
 @pytest.mark.parametrize("field,value", [("d_model", 5120 + 64), ("n_head", 41)])
 def test_shape_multiples_of_128(cpa, field, value):
     """d_model and n_head*head_dim must be multiples of 128, as the header documents."""
