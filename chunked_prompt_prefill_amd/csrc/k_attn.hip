@@ -97,6 +97,10 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
   const int64_t n_ctx = a.n_ctx;
 
   const int rw0 = qt * QROWS + wave * 32;
+  // A wave whose 32 rows all lie past the last query row (a short chunk: one token has G
+  // rows) still loads its share of every tile and joins every barrier, but skips the
+  // arithmetic, leaving its SIMD to the wave it shares it with.
+  const bool wave_rows = rw0 < R;
   const int i = rw0 + l32;
   const bool row_ok = i < R;
   const int t_i = row_ok ? i / G : 0;
@@ -350,7 +354,7 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
         attn_cfence();
         issue_f16(std::integral_constant<int, (j + 2) % 3>{}, min(t + 2, last));
         attn_cfence();
-        if (t < jt1) {
+        if (t < jt1 && wave_rows) {
           uint4 pb[4];
           const float msafe = stats(sc, t * KVT);
           qk(bufK(std::integral_constant<int, (j + 1) % 3>{}), sn);
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
       attn_wait_vm_lgkm<NLOAD>();      // tile jt0 landed (own loads)
       __builtin_amdgcn_s_barrier();    // everyone's
       attn_cfence();
-      qk(bufK(I0{}), sa);
+      if (wave_rows) qk(bufK(I0{}), sa);
       for (int t = jt0; t < jt1; t += 6) {
         step(I0{}, P0{}, t);
         step(I1{}, P1{}, t + 1);
@@ -417,11 +421,11 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
         const int t = t0 + 2 * pr;
         barrier();                     // tile t in buffer 0; buffer 1 is free
         load_q8(min(t + 2, tl), ra);
-        compute(sK0, sV0, t * KVT);
+        if (wave_rows) compute(sK0, sV0, t * KVT);
         store_q8(rb, min(t + 1, tl), sK1, sV1);
         barrier();                     // tile t+1 in buffer 1; buffer 0 is free
         load_q8(min(t + 3, tl), rb);
-        if (t + 1 <= tl) compute(sK1, sV1, (t + 1) * KVT);
+        if (t + 1 <= tl && wave_rows) compute(sK1, sV1, (t + 1) * KVT);
         store_q8(ra, min(t + 2, tl), sK0, sV0);
       }
       attn_wait_vm0();
