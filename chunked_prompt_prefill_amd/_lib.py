@@ -73,6 +73,8 @@ SIGNATURES = {
     "cp_test_kv_layer_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32]),
     "cp_test_rope_kv_append": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
                                               c_i32, c_i32, c_vp, c_vp, c_vp]),
+    "cp_test_rope_kv_append_planes": (ctypes.c_int, [c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                                     c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "cp_test_kv_rows": (ctypes.c_int, [c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "cp_test_router_scratch_bytes": (c_sz, [c_i32, c_i32]),
     "cp_test_router": (ctypes.c_int, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,

@@ -542,9 +542,14 @@ hipError_t timed(cp_ctx* c, const char* cls, F&& launch) {
 // chunks of kDeferMinRows rows or more: the reading kernel (RMSNorm, one workgroup per
 // row) then has rows enough to spread the partial reads over the chip.
 constexpr int kDeferMinRows = 64;
+// chunks of up to this many tokens run RoPE and the K/V append as one launch, reading the
+// QKV GEMM's split planes directly
+constexpr int kQkvPostMaxRows = kSkinnyMaxRows;
 hipError_t gemm(cp_ctx* c, const char* cls, const _Float16* A, int lda, int M, const QMat& W,
-                int mode, void* out, int ldo, PendingSum* defer = nullptr) {
-  // (split sums are deferred only for a non-SwiGLU launch of kDeferMinRows rows or more)
+                int mode, void* out, int ldo, PendingSum* defer = nullptr, bool defer_few = false) {
+  // (split sums are deferred only for a non-SwiGLU launch of kDeferMinRows rows or more, or
+  // with defer_few for any row count: the QKV sums of a few rows, which the one-launch
+  // RoPE + append takes)
   const bool deferrable = defer && mode != GM_SWIGLU && M >= kDeferMinRows;
   const GemmPlan p = plan_gemm(M, W.N, W.K, 0, 0,
                                !c->plan_shared ? kPlanSingle : deferrable ? kPlanSharedDeferred : kPlanShared);
@@ -552,7 +557,7 @@ hipError_t gemm(cp_ctx* c, const char* cls, const _Float16* A, int lda, int M, c
   return timed(c, cls, [&] {
     for (int i = 0; i < p.nparts; ++i) {
       const bool leave = defer && p.part[i].splits > 1 && i == p.nparts - 1 && mode != GM_SWIGLU &&
-                         M >= kDeferMinRows;
+                         (M >= kDeferMinRows || defer_few);
       GemmArgs g;
       g.A = A; g.lda = lda; g.M = M; g.N = p.part[i].n1; g.K = W.K; g.n0 = p.part[i].n0;
       g.wq = W.q; g.wd = W.d; g.mode = mode; g.out = out; g.ldo = ldo;
@@ -594,10 +599,16 @@ int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int sta
   if (px.partial && x_res_in != x) return fail(c, CP_E_DEVICE, "pending sums on the chunk input");
   // (x_res_in is written only when sums are pending, and then it is x)
   CP_HIP(c, timed(c, "rmsnorm", [&] { return launch_rmsnorm(const_cast<float*>(x_res_in), L.attn_norm, n, D.d, c->cfg.rms_eps, xn, nullptr, s, px); }), "rmsnorm");
-  // (the QKV sums are reduced in their own pass: RoPE reads each q/k value twice, as a
-  // value and as its rotation partner, so it would read the partials twice)
-  CP_HIP(c, gemm(c, "gemm_qkv", xn, D.d, n, L.qkv, GM_F32, qkv, D.Nqkv), "gemm_qkv");
+  // (the QKV sums of a larger chunk are reduced in their own pass: RoPE reads each q/k
+  // value twice, as a value and as its rotation partner, so it would read the partials
+  // twice.  A chunk of a few tokens hands its unsummed planes to the one-launch RoPE +
+  // append instead, which saves two launches per layer.)
+  const bool few = n <= kQkvPostMaxRows;
+  PendingSum pq;
+  CP_HIP(c, gemm(c, "gemm_qkv", xn, D.d, n, L.qkv, GM_F32, qkv, D.Nqkv, few ? &pq : nullptr, few), "gemm_qkv");
   CP_HIP(c, timed(c, "rope_kv_append", [&] {
+    if (few)
+      return launch_qkv_post(qkv, pq, cos_t, sin_t, n, start, D.Hq, D.Hkv, D.hd, D.kv_type, D.n_ctx, q, L.kv, s);
     hipError_t e = launch_rope_qk(qkv, cos_t, sin_t, n, start, D.Hq, D.Hkv, D.hd, D.kv_type, D.n_ctx, q, L.kv, s);
     if (e != hipSuccess) return e;
     return launch_v_append(qkv, n, start, D.Hq, D.Hkv, D.hd, D.kv_type, D.n_ctx, L.kv, s);
@@ -1250,6 +1261,35 @@ int cp_test_rope_kv_append(const float* qkv, const float* cos_t, const float* si
   const int nc = (int)round_up(n_ctx, 64);
   KvLayer L = kv_layer_at(kv, n_kv_head, head_dim, nc, kv_type);
   hipStream_t s = (hipStream_t)stream;
+  if (launch_rope_qk(qkv, cos_t, sin_t, n, start, n_head, n_kv_head, head_dim, kv_type, nc, (_Float16*)q_out, L, s) != hipSuccess)
+    return CP_E_DEVICE;
+  return launch_v_append(qkv, n, start, n_head, n_kv_head, head_dim, kv_type, nc, L, s) == hipSuccess ? CP_OK : CP_E_DEVICE;
+}
+
+int cp_test_rope_kv_append_planes(const float* partial, int32_t splits, const float* cos_t,
+                                  const float* sin_t, int32_t n, int32_t start, int32_t n_head,
+                                  int32_t n_kv_head, int32_t head_dim, int32_t kv_type, int32_t n_ctx,
+                                  void* q_out, void* kv, void* work, void* stream) {
+  if (!partial || !cos_t || !sin_t || !q_out || !kv || !work || splits < 1 || n < 1 || start < 0 ||
+      start + n > n_ctx)
+    return CP_E_INVALID;
+  if ((head_dim != 64 && head_dim != 128) || n_kv_head < 1 || n_head % n_kv_head) return CP_E_INVALID;
+  const int nc = (int)round_up(n_ctx, 64);
+  KvLayer L = kv_layer_at(kv, n_kv_head, head_dim, nc, kv_type);
+  hipStream_t s = (hipStream_t)stream;
+  const int32_t Nqkv = (n_head + 2 * n_kv_head) * head_dim;
+  float* qkv = (float*)work;
+  if (n <= kQkvPostMaxRows) {
+    PendingSum ps;
+    if (splits > 1) {
+      ps.partial = partial; ps.splits = splits; ps.M = n; ps.n0 = 0; ps.N = Nqkv;
+    } else {
+      qkv = const_cast<float*>(partial);
+    }
+    return launch_qkv_post(qkv, ps, cos_t, sin_t, n, start, n_head, n_kv_head, head_dim, kv_type, nc,
+                           (_Float16*)q_out, L, s) == hipSuccess ? CP_OK : CP_E_DEVICE;
+  }
+  if (launch_splitk_reduce(partial, splits, n, 0, Nqkv, GM_F32, qkv, Nqkv, s) != hipSuccess) return CP_E_DEVICE;
   if (launch_rope_qk(qkv, cos_t, sin_t, n, start, n_head, n_kv_head, head_dim, kv_type, nc, (_Float16*)q_out, L, s) != hipSuccess)
     return CP_E_DEVICE;
   return launch_v_append(qkv, n, start, n_head, n_kv_head, head_dim, kv_type, nc, L, s) == hipSuccess ? CP_OK : CP_E_DEVICE;

@@ -112,6 +112,20 @@ hipError_t launch_rope_qk(const float* qkv, const float* cos_t, const float* sin
 hipError_t launch_v_append(const float* qkv, int32_t n, int32_t start, int32_t n_head,
                            int32_t n_kv_head, int32_t head_dim, int32_t kv_type, int32_t n_ctx,
                            KvLayer kv, hipStream_t s);
+// The QKV values RoPE and the append read: output rows qkv [n][Nqkv] (splits == 0), or the
+// split planes partial [splits][n][Nqkv] of a split GEMM, added in split order.
+struct QkvSrc {
+  const float* qkv = nullptr;
+  const float* partial = nullptr;
+  int32_t splits = 0;
+  int64_t plane = 0;
+};
+// RoPE + K append + V append in one launch (chunks of a few tokens), from qkv or, when ps
+// holds them, the QKV GEMM's unsummed split planes (M == n, whole column range).
+hipError_t launch_qkv_post(const float* qkv, const PendingSum& ps, const float* cos_t,
+                           const float* sin_t, int32_t n, int32_t start, int32_t n_head,
+                           int32_t n_kv_head, int32_t head_dim, int32_t kv_type, int32_t n_ctx,
+                           _Float16* q_out, KvLayer kv, hipStream_t s);
 
 struct AttnArgs {
   const _Float16* q = nullptr;   // [n][Hq][hd]

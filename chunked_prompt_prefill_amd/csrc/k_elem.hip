@@ -197,20 +197,40 @@ KvLayer kv_layer_at(void* base, int32_t Hkv, int32_t hd, int32_t n_ctx, int32_t 
   return L;
 }
 
+// Where RoPE and the K/V append read the QKV projection: its output rows, or, for a split
+// GEMM of a few rows whose partial planes were left unsummed, those planes added in split
+// order exactly as the split-K reduction adds them (p0 + p1 + ... in float32).
+__device__ __forceinline__ float4 qkv_load4(const QkvSrc& src, int64_t off) {
+  if (src.splits == 0) return *reinterpret_cast<const float4*>(src.qkv + off);
+  float4 acc = *reinterpret_cast<const float4*>(src.partial + off);
+  for (int k = 1; k < src.splits; ++k) {
+    const float4 a = *reinterpret_cast<const float4*>(src.partial + k * src.plane + off);
+    acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
+  }
+  return acc;
+}
+__device__ __forceinline__ float qkv_load1(const QkvSrc& src, int64_t off) {
+  if (src.splits == 0) return src.qkv[off];
+  float acc = src.partial[off];
+  for (int k = 1; k < src.splits; ++k) acc += src.partial[k * src.plane + off];
+  return acc;
+}
+
 // RoPE on q and k (rotate-half pairs (i, i+hd/2)), then q -> f16 output and k -> cache.
 // Each lane handles 4 consecutive values of one head (16-byte loads); a wave covers 256
 // values of one token.  For a q8_0 cache the 32 values of a block sit in 8 lanes and
-// their amax is a reduction over those lanes.
-__global__ __launch_bounds__(256) void rope_qk_kernel(const float* __restrict__ qkv,
-                                                      const float* __restrict__ cos_t,
-                                                      const float* __restrict__ sin_t, int32_t n,
-                                                      int32_t start, int32_t Hq, int32_t Hkv,
-                                                      int32_t hd, int32_t kv_type, int32_t n_ctx,
-                                                      _Float16* __restrict__ q_out, KvLayer kv) {
+// their amax is a reduction over those lanes.  (block: this workgroup's index in the
+// RoPE part of the grid.)
+__device__ __forceinline__ void rope_qk_body(int64_t block, const QkvSrc& src,
+                                             const float* __restrict__ cos_t,
+                                             const float* __restrict__ sin_t, int32_t n,
+                                             int32_t start, int32_t Hq, int32_t Hkv, int32_t hd,
+                                             int32_t kv_type, int32_t n_ctx,
+                                             _Float16* __restrict__ q_out, const KvLayer& kv) {
   const int lane = threadIdx.x & 63;
   const int E = (Hq + Hkv) * hd;                      // rotated values per token
   const int segs = (E + 255) / 256;
-  const int64_t seg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t seg = block * 4 + (threadIdx.x >> 6);
   const int64_t t = seg / segs;
   if (t >= n) return;
   const int e0 = (int)(seg % segs) * 256 + lane * 4;
@@ -221,9 +241,8 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(const float* __restrict__ 
   const int head = e0 / hd, i0 = e0 % hd;
   const bool lo = i0 < half;
   const int ic0 = lo ? i0 : i0 - half;
-  const float* row = qkv + t * Nqkv;
-  const float4 x = *reinterpret_cast<const float4*>(row + e0);
-  const float4 y = *reinterpret_cast<const float4*>(row + head * hd + (lo ? i0 + half : i0 - half));
+  const float4 x = qkv_load4(src, t * Nqkv + e0);
+  const float4 y = qkv_load4(src, t * Nqkv + head * hd + (lo ? i0 + half : i0 - half));
   const float4 c = *reinterpret_cast<const float4*>(cos_t + p * half + ic0);
   const float4 s = *reinterpret_cast<const float4*>(sin_t + p * half + ic0);
   const float xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
@@ -260,37 +279,51 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(const float* __restrict__ 
   if ((i0 & 31) == 0) kv.kd[gi * (hd / QK) + i0 / QK] = float_to_half_bits(d);
 }
 
+__global__ __launch_bounds__(256) void rope_qk_kernel(QkvSrc src, const float* __restrict__ cos_t,
+                                                      const float* __restrict__ sin_t, int32_t n,
+                                                      int32_t start, int32_t Hq, int32_t Hkv,
+                                                      int32_t hd, int32_t kv_type, int32_t n_ctx,
+                                                      _Float16* __restrict__ q_out, KvLayer kv) {
+  rope_qk_body(blockIdx.x, src, cos_t, sin_t, n, start, Hq, Hkv, hd, kv_type, n_ctx, q_out, kv);
+}
+
+int64_t rope_qk_blocks(int32_t n, int32_t n_head, int32_t n_kv_head, int32_t head_dim) {
+  return ceil_div(ceil_div((int64_t)(n_head + n_kv_head) * head_dim, 256) * n, 4);
+}
+
 hipError_t launch_rope_qk(const float* qkv, const float* cos_t, const float* sin_t, int32_t n,
                           int32_t start, int32_t n_head, int32_t n_kv_head, int32_t head_dim,
                           int32_t kv_type, int32_t n_ctx, _Float16* q_out, KvLayer kv,
                           hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  const int64_t segs = ceil_div((int64_t)(n_head + n_kv_head) * head_dim, 256) * n;
-  hipLaunchKernelGGL(rope_qk_kernel, dim3((unsigned)ceil_div(segs, 4)), dim3(256), 0, s, qkv, cos_t,
-                     sin_t, n, start, n_head, n_kv_head, head_dim, kv_type, n_ctx, q_out, kv);
+  QkvSrc src;
+  src.qkv = qkv;
+  hipLaunchKernelGGL(rope_qk_kernel, dim3((unsigned)rope_qk_blocks(n, n_head, n_kv_head, head_dim)),
+                     dim3(256), 0, s, src, cos_t, sin_t, n, start, n_head, n_kv_head, head_dim,
+                     kv_type, n_ctx, q_out, kv);
   return hipGetLastError();
 }
 
 // V rows -> transposed cache.  A workgroup takes 32 tokens x 64 dims of one kv head: each
 // wave converts 64 consecutive dims of a token row (q8_0: per-32 amax by wavefront
 // reduction), the codes are transposed through LDS, then written 32 positions per dim.
+// (bx: token tile, by: kv head x 64-dim slice.)
 constexpr int VT = 32;
-__global__ __launch_bounds__(256) void v_append_kernel(const float* __restrict__ qkv, int32_t n,
-                                                       int32_t start, int32_t Hq, int32_t Hkv,
-                                                       int32_t hd, int32_t kv_type, int32_t n_ctx,
-                                                       KvLayer kv) {
+__device__ __forceinline__ void v_append_body(int bx, int by, const QkvSrc& src, int32_t n,
+                                              int32_t start, int32_t Hq, int32_t Hkv, int32_t hd,
+                                              int32_t kv_type, int32_t n_ctx, const KvLayer& kv) {
   __shared__ uint16_t sv[64][VT + 2];
   __shared__ int8_t sq[64][VT + 4];
   __shared__ uint16_t sd[2][VT];
-  const int t0 = blockIdx.x * VT;
-  const int g = blockIdx.y / (hd / 64);
-  const int d0 = (blockIdx.y % (hd / 64)) * 64;
+  const int t0 = bx * VT;
+  const int g = by / (hd / 64);
+  const int d0 = (by % (hd / 64)) * 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t Nqkv = (int64_t)(Hq + 2 * Hkv) * hd;
   const int64_t vcol = (int64_t)(Hq + Hkv + g) * hd + d0;
   for (int tl = wave; tl < VT; tl += 4) {
     const int t = t0 + tl;
-    const float v = t < n ? qkv[(int64_t)t * Nqkv + vcol + lane] : 0.0f;
+    const float v = t < n ? qkv_load1(src, (int64_t)t * Nqkv + vcol + lane) : 0.0f;
     if (kv_type == CP_KV_F16) {
       sv[lane][tl] = float_to_half_bits(v);
     } else {
@@ -316,12 +349,60 @@ __global__ __launch_bounds__(256) void v_append_kernel(const float* __restrict__
   }
 }
 
+__global__ __launch_bounds__(256) void v_append_kernel(QkvSrc src, int32_t n, int32_t start,
+                                                       int32_t Hq, int32_t Hkv, int32_t hd,
+                                                       int32_t kv_type, int32_t n_ctx, KvLayer kv) {
+  v_append_body(blockIdx.x, blockIdx.y, src, n, start, Hq, Hkv, hd, kv_type, n_ctx, kv);
+}
+
 hipError_t launch_v_append(const float* qkv, int32_t n, int32_t start, int32_t n_head,
                            int32_t n_kv_head, int32_t head_dim, int32_t kv_type, int32_t n_ctx,
                            KvLayer kv, hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  QkvSrc src;
+  src.qkv = qkv;
   hipLaunchKernelGGL(v_append_kernel, dim3((unsigned)ceil_div(n, VT), n_kv_head * (head_dim / 64)),
-                     dim3(256), 0, s, qkv, n, start, n_head, n_kv_head, head_dim, kv_type, n_ctx, kv);
+                     dim3(256), 0, s, src, n, start, n_head, n_kv_head, head_dim, kv_type, n_ctx, kv);
+  return hipGetLastError();
+}
+
+// Both in one launch, for chunks of a few tokens: the first workgroups run RoPE and the K
+// append, the rest the V append, straight from the QKV output or its split planes (one
+// launch instead of the split-K reduction, RoPE and the V append).
+__global__ __launch_bounds__(256) void qkv_post_kernel(QkvSrc src, const float* __restrict__ cos_t,
+                                                       const float* __restrict__ sin_t, int32_t n,
+                                                       int32_t start, int32_t Hq, int32_t Hkv,
+                                                       int32_t hd, int32_t kv_type, int32_t n_ctx,
+                                                       _Float16* __restrict__ q_out, KvLayer kv,
+                                                       int32_t rope_blocks) {
+  const int b = blockIdx.x;
+  if (b < rope_blocks) {
+    rope_qk_body(b, src, cos_t, sin_t, n, start, Hq, Hkv, hd, kv_type, n_ctx, q_out, kv);
+    return;
+  }
+  const int vb = b - rope_blocks, nby = Hkv * (hd / 64);
+  v_append_body(vb / nby, vb % nby, src, n, start, Hq, Hkv, hd, kv_type, n_ctx, kv);
+}
+
+hipError_t launch_qkv_post(const float* qkv, const PendingSum& ps, const float* cos_t,
+                           const float* sin_t, int32_t n, int32_t start, int32_t n_head,
+                           int32_t n_kv_head, int32_t head_dim, int32_t kv_type, int32_t n_ctx,
+                           _Float16* q_out, KvLayer kv, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t Nqkv = (int64_t)(n_head + 2 * n_kv_head) * head_dim;
+  QkvSrc src;
+  src.qkv = qkv;
+  if (ps.partial) {
+    // the planes must be the whole QKV output of these rows, unsummed
+    if (ps.M != n || ps.n0 != 0 || ps.N != Nqkv || ps.add || ps.splits < 1) return hipErrorInvalidValue;
+    src.partial = ps.partial;
+    src.splits = ps.splits;
+    src.plane = (int64_t)n * Nqkv;
+  }
+  const int64_t rb = rope_qk_blocks(n, n_head, n_kv_head, head_dim);
+  const int64_t vb = ceil_div(n, VT) * n_kv_head * (head_dim / 64);
+  hipLaunchKernelGGL(qkv_post_kernel, dim3((unsigned)(rb + vb)), dim3(256), 0, s, src, cos_t, sin_t,
+                     n, start, n_head, n_kv_head, head_dim, kv_type, n_ctx, q_out, kv, (int32_t)rb);
   return hipGetLastError();
 }
 

@@ -277,6 +277,18 @@ def cp_test_rope_kv_append(qkv, cos_t, sin_t, n, start, n_head, n_kv_head, head_
         raise PrefillError(rc, "cp_test_rope_kv_append failed")
 
 
+def cp_test_rope_kv_append_planes(partial, splits, cos_t, sin_t, n, start, n_head, n_kv_head,
+                                  head_dim, kv_type, n_ctx, q_out, kv):
+    """RoPE + K/V append from the QKV GEMM's split planes, as prefill_chunk runs it."""
+    work = torch.empty(n * (n_head + 2 * n_kv_head) * head_dim, dtype=torch.float32,
+                       device=partial.device)
+    rc = lib().cp_test_rope_kv_append_planes(ptr(partial), splits, ptr(cos_t), ptr(sin_t), n, start,
+                                             n_head, n_kv_head, head_dim, kv_type, n_ctx,
+                                             ptr(q_out), ptr(kv), ptr(work), stream_ptr())
+    if rc != CP_OK:
+        raise PrefillError(rc, "cp_test_rope_kv_append_planes failed")
+
+
 def cp_test_kv_rows(kv, n_tokens, n_kv_head, head_dim, kv_type, n_ctx, out):
     rc = lib().cp_test_kv_rows(ptr(kv), n_tokens, n_kv_head, head_dim, kv_type, n_ctx, ptr(out),
                                stream_ptr())

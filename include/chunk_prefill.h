@@ -338,6 +338,17 @@ int cp_test_rope_kv_append(const float* qkv, const float* cos_t, const float* si
                            int32_t head_dim, int32_t kv_type, int32_t n_ctx, void* q_out,
                            void* kv, void* hip_stream);
 
+/* The same from the split planes of the QKV GEMM, as prefill_chunk runs it: the values
+ * are partial[0] + partial[1] + ... + partial[splits-1] (float32, added in split order),
+ * partial: float32 [splits][n][(n_head + 2*n_kv_head)*head_dim].  Chunks of up to four
+ * tokens take the one-launch RoPE + append that reads the planes directly; larger ones
+ * sum them first (into work: float32 [n][(n_head + 2*n_kv_head)*head_dim], dev, unused
+ * otherwise but required).  CP_E_INVALID for splits < 1 and as cp_test_rope_kv_append. */
+int cp_test_rope_kv_append_planes(const float* partial, int32_t splits, const float* cos_t,
+                                  const float* sin_t, int32_t n, int32_t start, int32_t n_head,
+                                  int32_t n_kv_head, int32_t head_dim, int32_t kv_type, int32_t n_ctx,
+                                  void* q_out, void* kv, void* work, void* hip_stream);
+
 /* Copy rows [0, n_tokens) of a one-layer cache into the serialized row form (K rows then
  * V rows, token-major, as in the state blob).  out: dev bytes. */
 int cp_test_kv_rows(const void* kv, int32_t n_tokens, int32_t n_kv_head, int32_t head_dim,

@@ -92,6 +92,46 @@ def test_rope_kv_append_bit_exact(torch, cpa, kv, hd, Hq, Hkv, n, start):
     assert np.array_equal(rows[1], vref), "V rows differ"
 
 
+# The same from the QKV GEMM's split planes, as prefill_chunk runs it: chunks of up to four
+# tokens through the one-launch RoPE + append reading the planes, a larger one through the
+# split-K reduction first.  The planes' float32 sum in split order is formed on the host
+# and the result must match the oracle on it bit for bit, as above.
+@pytest.mark.parametrize("kv", ["f16", "q8_0"])
+@pytest.mark.parametrize("hd,Hq,Hkv,n,start,splits", [(128, 40, 8, 1, 17000, 7), (128, 40, 8, 3, 100, 3),
+                                                      (64, 4, 2, 4, 0, 1), (128, 8, 2, 2, 63, 16),
+                                                      (128, 40, 8, 5, 700, 3)])
+def test_rope_kv_append_from_split_planes_bit_exact(torch, cpa, kv, hd, Hq, Hkv, n, start, splits):
+    kv_code = 0 if kv == "f16" else 1
+    n_ctx = start + n + 3
+    W = (Hq + 2 * Hkv) * hd
+    log(f"rope_kv_append planes kv={kv} hd={hd} Hq={Hq} Hkv={Hkv} n={n} start={start} splits={splits}")
+    planes = synth.normal(synth.tensor_seed("qkv-planes", hd, Hq, n, splits), (splits, n, W), scale=0.5)
+    qkv = planes[0].copy()
+    for k in range(1, splits):
+        qkv = (qkv + planes[k]).astype(np.float32)
+    cos, sin = oracle.rope_table(n_ctx, hd, 1e6)
+    q_out = torch.empty((n, Hq, hd), dtype=torch.float16, device="cuda")
+    kvbuf = torch.zeros(cpa.cp_test_kv_layer_bytes(Hkv, hd, n_ctx, kv_code), dtype=torch.uint8,
+                        device="cuda")
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    cpa.cp_test_rope_kv_append_planes(T(planes), splits, T(cos), T(sin), n, start, Hq, Hkv, hd,
+                                      kv_code, n_ctx, q_out, kvbuf)
+    rb = (hd * 2) if kv == "f16" else (hd // 32) * 34
+    rows = torch.empty(2 * (start + n) * Hkv * rb, dtype=torch.uint8, device="cuda")
+    cpa.cp_test_kv_rows(kvbuf, start + n, Hkv, hd, kv_code, n_ctx, rows)
+    torch.cuda.synchronize()
+    rows = rows.cpu().numpy().reshape(2, start + n, Hkv, rb)[:, start:]
+    q = qkv[:, :Hq * hd].reshape(n, Hq, hd)
+    k = qkv[:, Hq * hd:(Hq + Hkv) * hd].reshape(n, Hkv, hd)
+    v = qkv[:, (Hq + Hkv) * hd:].reshape(n, Hkv, hd)
+    cs, sn = cos[start:start + n], sin[start:start + n]
+    q32 = oracle.rope_apply_f32(q, cs, sn)
+    k32 = oracle.rope_apply_f32(k, cs, sn)
+    assert np.array_equal(q_out.cpu().numpy().view(np.uint16), q32.astype(np.float16).view(np.uint16))
+    assert np.array_equal(rows[0], cache_row_bytes(oracle.cache_encode_rows(k32, kv), kv)), "K rows differ"
+    assert np.array_equal(rows[1], cache_row_bytes(oracle.cache_encode_rows(v, kv), kv)), "V rows differ"
+
+
 # --------------------------------------------------------------------------- GEMM
 def f16_round(a: np.ndarray) -> np.ndarray:
     return a.astype(np.float16).astype(np.float32)
