@@ -331,9 +331,11 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
   using I2 = std::integral_constant<int, 2>;
   if (jt0 < jt1) {
     const int last = jt1 - 1;
-    // Tile t lives in buffer (t - jt0) % NB.  The loop runs in groups of NB tiles; steps
-    // past the range still wait, synchronise and issue (a clamped repeat of the last tile)
-    // so every wave sees the same count of loads in flight, but skip the arithmetic.
+    // Tile t lives in buffer (t - jt0) % NB.  The loops run in unrolled groups of steps;
+    // loads past the range are clamped repeats of the last tile.  The f16 loop skips the
+    // steps past the range whole; the q8_0 loop's last pair may run one step past it, which
+    // waits, synchronises and issues like the others (every wave sees the same loads in
+    // flight) but skips the arithmetic.
     if constexpr (!Q8) {
       // NB = 3, software-pipelined across tiles.  Step t waits for tile t+1 (the only loads
       // in flight), synchronises (every wave is done with tile t-1), and refills the buffer
@@ -387,13 +389,15 @@ __global__ __launch_bounds__(AW * 64, 1) void attn_kernel(AttnArgs a) {
       __builtin_amdgcn_s_barrier();    // everyone's
       attn_cfence();
       if (wave_rows) qk(bufK(I0{}), sa);
+      // (the steps past the range are skipped whole, by every wave alike: their waits and
+      // barriers would only delay a short range, such as a decode-sized chunk's KV split)
       for (int t = jt0; t < jt1; t += 6) {
         step(I0{}, P0{}, t);
-        step(I1{}, P1{}, t + 1);
-        step(I2{}, P0{}, t + 2);
-        step(I0{}, P1{}, t + 3);
-        step(I1{}, P0{}, t + 4);
-        step(I2{}, P1{}, t + 5);
+        if (t + 1 < jt1) step(I1{}, P1{}, t + 1);
+        if (t + 2 < jt1) step(I2{}, P0{}, t + 2);
+        if (t + 3 < jt1) step(I0{}, P1{}, t + 3);
+        if (t + 4 < jt1) step(I1{}, P0{}, t + 4);
+        if (t + 5 < jt1) step(I2{}, P1{}, t + 5);
       }
       attn_wait_vm0();
     } else {
