@@ -204,7 +204,10 @@ GemmPlan plan_gemm_mt(int M, int N, int K, int mt, int force_splits) {
 // workgroup per 64 columns and K split S ways.  Measured on the 27B-class shapes, the
 // stream runs near the HBM rate once about 600-900 workgroups are in flight, and each
 // split costs a reduction launch (about 4 us plus the gap between launches), so S brings
-// the workgroup count near 768 and no further (at most one 4-stage share per split).
+// the workgroup count near 768 and no further (at most one 4-stage share per split).  A
+// single row does less arithmetic per weight byte, and there about 1536 workgroups did
+// best (the 16-layer share per one-token chunk: 1.94 ms against 1.99 at 768 and 1.97 at
+// 1100; with three rows 1536 was 6% slower than 768).
 GemmPlan plan_gemm_skinny(int M, int N, int K, int force_splits) {
   GemmPlan p;
   p.mt = 1;
@@ -212,7 +215,7 @@ GemmPlan plan_gemm_skinny(int M, int N, int K, int force_splits) {
   const int KQ = K / 128, P = N / 64;
   int S;
   if (force_splits > 0) S = std::min(force_splits, KQ);
-  else S = std::max(1, std::min((768 + P / 2) / P, std::max(1, KQ / 4)));
+  else S = std::max(1, std::min(((M == 1 ? 1536 : 768) + P / 2) / P, std::max(1, KQ / 4)));
   p.part[0] = {0, N, S};
   p.partial_bytes = S > 1 ? (size_t)S * M * N * 4 : 0;
   return p;
