@@ -187,8 +187,10 @@ def test_sweep_shapes_every_chunk_size_at_depth(torch):
     """Four layers of the dense shapes: 16,384 positions prefilled in 8192-token chunks
     (the first of them the depth-0 8192-token chunk), then, after truncation back to
     16,384 each time, one chunk of every sweep size (128 ... 8192) at that depth, in the
-    bench's launch plans.  One oracle layer-0 evaluation at sampled rows serves all of
-    them: the depth-0 chunk's rows, and for each size rows of [16,384, 16,384 + C)."""
+    bench's launch plans, and decode-sized chunks of 1 and 3 tokens there (the
+    weight-streaming GEMMs, the one-launch RoPE + append, split attention).  One oracle
+    layer-0 evaluation at sampled rows serves all of them: the depth-0 chunk's rows, and
+    for each size rows of [16,384, 16,384 + C)."""
     w = synth.WORKLOADS["dense27b_sweep"]
     D, sizes = w.depth_prefill, w.chunk_sweep
     Cmax = max(sizes)
@@ -202,7 +204,8 @@ def test_sweep_shapes_every_chunk_size_at_depth(torch):
     rows0 = sample_rows(0, Cmax, Cmax, seed=Cmax)
     got = {0: lo[0][torch.from_numpy(rows0).cuda()].cpu().numpy()}
     rows = {0: rows0}
-    for C in sizes:
+    decode = (1, 3)
+    for C in decode + tuple(sizes):     # the largest last: the state below holds it
         assert fr.ctx.kv_cache_truncate(D) == 0
         lo[:, D:].zero_()
         fr.run(xd, out, [(D, D + C)], lo, None, n)
@@ -217,7 +220,7 @@ def test_sweep_shapes_every_chunk_size_at_depth(torch):
     allrows = np.unique(np.concatenate(list(rows.values())))
     m = oracle.OracleModel(w.with_(n_layer=1), [ql0])
     ref, cache = m.layer_rows(0, x, allrows)
-    for C in [0] + list(sizes):
+    for C in [0] + list(decode) + list(sizes):
         sel = np.searchsorted(allrows, rows[C])
         e = rel_err(got[C], ref[sel])
         log(f"  {'depth-0 chunk of ' + str(Cmax) if C == 0 else f'chunk {C} at depth {D}'}: "

@@ -206,7 +206,8 @@ def test_gemm_q8_0_row_tiles(torch, cpa, M, N, K, splits, mode, row_tile):
 # uneven split and one stage per workgroup (idle waves), in the three epilogues.  Two calls must agree bit for bit (fixed summation order).
 @pytest.mark.parametrize("M,N,K,splits", [(1, 64, 128, 0), (2, 5120, 640, 0), (3, 6144, 5120, 0),
                                           (4, 5120, 17408, 0), (1, 34816, 5120, 0), (3, 1024, 5120, 1),
-                                          (4, 512, 2048, 3), (2, 256, 1024, 8), (2, 768, 1664, 1)])
+                                          (4, 512, 2048, 3), (2, 256, 1024, 8), (2, 768, 1664, 1),
+                                          (1, 5120, 17408, 0)])
 @pytest.mark.parametrize("mode", [0, 1, 2])
 def test_gemm_skinny(torch, cpa, M, N, K, splits, mode):
     log(f"gemm skinny M={M} N={N} K={K} splits={splits} mode={mode}")
