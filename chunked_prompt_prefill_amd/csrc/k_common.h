@@ -92,4 +92,39 @@ __device__ __forceinline__ float warp_max32(float v) {   // max over aligned gro
 // g < about -88, and then the reciprocal gives 0 and silu gives -0.
 __device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
+// The split-K sum of `splits` planes at p, p + plane, ... in plane order, p0 + p1 + p2 + ...
+// in float32 (the fixed order every reader of split partial sums uses).  The loads are
+// issued four at a time, so that they are in flight together instead of one per add.
+__device__ __forceinline__ float4 split_sum4(const float* p, int64_t plane, int splits) {
+  float4 acc = *reinterpret_cast<const float4*>(p);
+  int s = 1;
+  for (; s + 3 < splits; s += 4) {
+    float4 a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const float4*>(p + (s + j) * plane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc.x += a[j].x; acc.y += a[j].y; acc.z += a[j].z; acc.w += a[j].w;
+    }
+  }
+  for (; s < splits; ++s) {
+    const float4 a = *reinterpret_cast<const float4*>(p + s * plane);
+    acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
+  }
+  return acc;
+}
+__device__ __forceinline__ float split_sum1(const float* p, int64_t plane, int splits) {
+  float acc = p[0];
+  int s = 1;
+  for (; s + 3 < splits; s += 4) {
+    float a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = p[(s + j) * plane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc += a[j];
+  }
+  for (; s < splits; ++s) acc += p[s * plane];
+  return acc;
+}
+
 }  // namespace cp

@@ -115,12 +115,7 @@ __device__ __forceinline__ float4 pend_load4(const float* base, int64_t ld, cons
   const float4 b = *reinterpret_cast<const float4*>(base + row * ld + col);
   if (!ps.partial || col < ps.n0) return b;
   const int64_t pn = ps.N - ps.n0, plane = (int64_t)ps.M * pn;
-  const float* p = ps.partial + row * pn + (col - ps.n0);
-  float4 acc = *reinterpret_cast<const float4*>(p);
-  for (int sp = 1; sp < ps.splits; ++sp) {
-    const float4 a = *reinterpret_cast<const float4*>(p + sp * plane);
-    acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
-  }
+  float4 acc = split_sum4(ps.partial + row * pn + (col - ps.n0), plane, ps.splits);
   if (ps.add) { acc.x = b.x + acc.x; acc.y = b.y + acc.y; acc.z = b.z + acc.z; acc.w = b.w + acc.w; }
   return acc;
 }
@@ -202,18 +197,11 @@ KvLayer kv_layer_at(void* base, int32_t Hkv, int32_t hd, int32_t n_ctx, int32_t 
 // order exactly as the split-K reduction adds them (p0 + p1 + ... in float32).
 __device__ __forceinline__ float4 qkv_load4(const QkvSrc& src, int64_t off) {
   if (src.splits == 0) return *reinterpret_cast<const float4*>(src.qkv + off);
-  float4 acc = *reinterpret_cast<const float4*>(src.partial + off);
-  for (int k = 1; k < src.splits; ++k) {
-    const float4 a = *reinterpret_cast<const float4*>(src.partial + k * src.plane + off);
-    acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
-  }
-  return acc;
+  return split_sum4(src.partial + off, src.plane, src.splits);
 }
 __device__ __forceinline__ float qkv_load1(const QkvSrc& src, int64_t off) {
   if (src.splits == 0) return src.qkv[off];
-  float acc = src.partial[off];
-  for (int k = 1; k < src.splits; ++k) acc += src.partial[k * src.plane + off];
-  return acc;
+  return split_sum1(src.partial + off, src.plane, src.splits);
 }
 
 // RoPE on q and k (rotate-half pairs (i, i+hd/2)), then q -> f16 output and k -> cache.

@@ -264,14 +264,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int64_t plane = (int64_t)M * pn;
   if (mode == GM_SWIGLU) {
     const int64_t gc = (c4 / 32) * 64 + (c4 % 32);
-    float4 gs = *reinterpret_cast<const float4*>(partial + row * pn + gc);
-    float4 us = *reinterpret_cast<const float4*>(partial + row * pn + gc + 32);
-    for (int s = 1; s < splits; ++s) {
-      const float4 a = *reinterpret_cast<const float4*>(partial + s * plane + row * pn + gc);
-      const float4 b = *reinterpret_cast<const float4*>(partial + s * plane + row * pn + gc + 32);
-      gs.x += a.x; gs.y += a.y; gs.z += a.z; gs.w += a.w;
-      us.x += b.x; us.y += b.y; us.z += b.z; us.w += b.w;
-    }
+    const float4 gs = split_sum4(partial + row * pn + gc, plane, splits);
+    const float4 us = split_sum4(partial + row * pn + gc + 32, plane, splits);
     _Float16* o = reinterpret_cast<_Float16*>(out) + row * ldo + n0 / 2 + c4;
     o[0] = f16_sat(silu(gs.x) * us.x);
     o[1] = f16_sat(silu(gs.y) * us.y);
@@ -279,11 +273,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     o[3] = f16_sat(silu(gs.w) * us.w);
     return;
   }
-  float4 acc = *reinterpret_cast<const float4*>(partial + row * pn + c4);
-  for (int s = 1; s < splits; ++s) {
-    const float4 a = *reinterpret_cast<const float4*>(partial + s * plane + row * pn + c4);
-    acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
-  }
+  float4 acc = split_sum4(partial + row * pn + c4, plane, splits);
   float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + row * ldo + n0 + c4);
   if (mode == GM_F32_ADD) {
     const float4 x = *o;
