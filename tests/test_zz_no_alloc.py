@@ -66,9 +66,10 @@ def run_pair(torch, w, chunks, n_chunk_max, n_ctx):
 
 def test_static_chunk_equals_prefill_chunk_dense(torch):
     """Two layers of the 27B-class dense shapes (split-K GEMMs, deferred partial sums):
-    512 rows, then 200."""
+    512 rows, then 200, then decode-sized chunks of 3 and 1 (weight-streaming GEMMs, the
+    one-launch RoPE + append)."""
     w = synth.WORKLOADS["dense27b_sweep"].with_(n_layer=2)
-    run_pair(torch, w, [512, 200], n_chunk_max=512, n_ctx=1024)
+    run_pair(torch, w, [512, 200, 3, 1], n_chunk_max=512, n_ctx=1024)
 
 
 def test_static_chunk_equals_prefill_chunk_q8_0_cache_and_routed_experts(torch):
