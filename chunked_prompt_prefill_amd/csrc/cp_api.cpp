@@ -541,26 +541,23 @@ hipError_t timed(cp_ctx* c, const char* cls, F&& launch) {
 
 // defer (optional): a split launch covering the last column range leaves its partial
 // sums pending and describes them there (PendingSum) for the kernel that reads the
-// result, instead of running the reduction pass; *defer is cleared otherwise.  Only for
-// chunks of kDeferMinRows rows or more: the reading kernel (RMSNorm, one workgroup per
-// row) then has rows enough to spread the partial reads over the chip.
-constexpr int kDeferMinRows = 64;
+// result, instead of running the reduction pass; *defer is cleared otherwise.  This holds
+// for chunks of any size: at a few rows the reading kernel (RMSNorm, one workgroup per
+// row) has few workgroups for the partial reads, but it still costs less than the launch
+// of the reduction pass it replaces.
 // chunks of up to this many tokens run RoPE and the K/V append as one launch, reading the
 // QKV GEMM's split planes directly
 constexpr int kQkvPostMaxRows = kSkinnyMaxRows;
 hipError_t gemm(cp_ctx* c, const char* cls, const _Float16* A, int lda, int M, const QMat& W,
-                int mode, void* out, int ldo, PendingSum* defer = nullptr, bool defer_few = false) {
-  // (split sums are deferred only for a non-SwiGLU launch of kDeferMinRows rows or more, or
-  // with defer_few for any row count: the QKV sums of a few rows, which the one-launch
-  // RoPE + append takes)
-  const bool deferrable = defer && mode != GM_SWIGLU && M >= kDeferMinRows;
+                int mode, void* out, int ldo, PendingSum* defer = nullptr) {
+  // (split sums are deferred only for a non-SwiGLU launch)
+  const bool deferrable = defer && mode != GM_SWIGLU;
   const GemmPlan p = plan_gemm(M, W.N, W.K, 0, 0,
                                !c->plan_shared ? kPlanSingle : deferrable ? kPlanSharedDeferred : kPlanShared);
   if (defer) *defer = PendingSum();
   return timed(c, cls, [&] {
     for (int i = 0; i < p.nparts; ++i) {
-      const bool leave = defer && p.part[i].splits > 1 && i == p.nparts - 1 && mode != GM_SWIGLU &&
-                         (M >= kDeferMinRows || defer_few);
+      const bool leave = deferrable && p.part[i].splits > 1 && i == p.nparts - 1;
       GemmArgs g;
       g.A = A; g.lda = lda; g.M = M; g.N = p.part[i].n1; g.K = W.K; g.n0 = p.part[i].n0;
       g.wq = W.q; g.wd = W.d; g.mode = mode; g.out = out; g.ldo = ldo;
@@ -608,7 +605,7 @@ int run_layer(cp_ctx* c, int li, const float* x_res_in, float* x, int n, int sta
   // append instead, which saves two launches per layer.)
   const bool few = n <= kQkvPostMaxRows;
   PendingSum pq;
-  CP_HIP(c, gemm(c, "gemm_qkv", xn, D.d, n, L.qkv, GM_F32, qkv, D.Nqkv, few ? &pq : nullptr, few), "gemm_qkv");
+  CP_HIP(c, gemm(c, "gemm_qkv", xn, D.d, n, L.qkv, GM_F32, qkv, D.Nqkv, few ? &pq : nullptr), "gemm_qkv");
   CP_HIP(c, timed(c, "rope_kv_append", [&] {
     if (few)
       return launch_qkv_post(qkv, pq, cos_t, sin_t, n, start, D.Hq, D.Hkv, D.hd, D.kv_type, D.n_ctx, q, L.kv, s);

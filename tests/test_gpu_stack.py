@@ -112,19 +112,26 @@ def test_tiny_dense_workload_chunk_sizes(torch):
         assert rel_err(outs[c], outs[128]) < TOL
 
 
-def test_deferred_split_sums_bitwise_equal_reduction_pass(torch):
-    """Chunks of 64+ rows leave the split-K sums of the output and down projections to the
-    RMSNorm that reads them (the down sums cross into the next layer).  The traced entry
-    point adds each layer's down sums in the reduction pass instead; the arithmetic and
-    its order are the same, so outputs and cache state must agree bit for bit."""
+# a wide FFN (K = 2048 in the down projection) so that chunks of 1-4 rows split it as well
+WIDE_FFN = synth.Workload("gpu_wide_ffn", 2, 256, 4, 2, 64, 2048, kv_type="f16", n_prompt=90, chunk=3)
+
+
+@pytest.mark.parametrize("wname,chunks", [("tiny_dense", (37, 128, 512)), ("wide_ffn", (1, 3, 37))])
+def test_deferred_split_sums_bitwise_equal_reduction_pass(torch, wname, chunks):
+    """Chunks of every size leave the split-K sums of the output and down projections to
+    the RMSNorm that reads them (the down sums cross into the next layer).  The traced
+    entry point adds each layer's down sums in the reduction pass instead; the arithmetic
+    and its order are the same, so outputs and cache state must agree bit for bit."""
     import chunked_prompt_prefill_amd as cpa
-    w = synth.WORKLOADS["tiny_dense"]
+    w = synth.WORKLOADS["tiny_dense"] if wname == "tiny_dense" else WIDE_FFN
     ql = q8_layers(w)
     x = torch.from_numpy(synth.prompt_inputs(w)).cuda()
     n = x.shape[0]
     dev = [cpa.to_device(l) for l in ql]
-    for chunk in (128, 512):
-        log(f"deferred sums tiny_dense chunk={chunk} plan(O)={cpa.cp_test_gemm_plan(chunk, w.d_model, w.n_head * w.head_dim)}")
+    for chunk in chunks:
+        plan = cpa.cp_test_gemm_plan(chunk, w.d_model, -(-w.ffn_dim // 128) * 128)
+        log(f"deferred sums {wname} chunk={chunk} plan(down)={plan}")
+        assert max(s for _, s in plan[1]) > 1          # the down projection is split
         a = cpa.PrefillContext(cpa.make_config(w, n, chunk), dev)
         b = cpa.PrefillContext(cpa.make_config(w, n, chunk), dev)
         ya, yb = torch.empty_like(x), torch.empty_like(x)
