@@ -278,8 +278,14 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_big_kernel(GemmArgs g) {
       if constexpr (decltype(ISS)::value && t < BNLOAD) issue_piece(JI, T, iks, wi);
       constexpr int mi = t % 8, st = t / 8;
       const f16x8 av = __builtin_bit_cast(f16x8, af[t % 4]);
-      acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, __builtin_bit_cast(f16x8, dq[0][st]), acc[mi][0], 0, 0, 0);
-      acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, __builtin_bit_cast(f16x8, dq[1][st]), acc[mi][1], 0, 0, 0);
+      const f16x8 b0 = __builtin_bit_cast(f16x8, dq[0][st]), b1 = __builtin_bit_cast(f16x8, dq[1][st]);
+      if constexpr (MODE == GM_SWIGLU) {   // transposed tile (see the epilogue)
+        acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, av, acc[mi][0], 0, 0, 0);
+        acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, av, acc[mi][1], 0, 0, 0);
+      } else {
+        acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, b0, acc[mi][0], 0, 0, 0);
+        acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, b1, acc[mi][1], 0, 0, 0);
+      }
       if constexpr (t + 3 < 16) af[(t + 3) % 4] = frag(J, kb, t + 3);
       else if constexpr (decltype(NEXTA)::value) af[(t + 3) % 4] = frag(J, kb + 1, t + 3 - 16);
       else af[(t + 3) % 4] = frag(std::integral_constant<int, (decltype(J)::value + 1) % NBUFA>(), 0, t + 3 - 16);
@@ -359,7 +365,12 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_big_kernel(GemmArgs g) {
 
   // Epilogue.  acc[mi][ni][e]: row mi*32 + 8*(e/4) + 4*h + e%4, column n_wave + 32*ni + l32.
   // A lane's rows are 4h plus constants, so each store address is a per-lane base plus a
-  // constant times the (uniform) row stride; whole tiles skip the row check.
+  // constant times the (uniform) row stride; whole tiles skip the row check.  The SwiGLU
+  // tile is held transposed instead (weights as the MFMA's first operand): acc[mi][ni][e]
+  // is row mi*32 + l32, column n_wave + 32*ni + 8*(e/4) + 4h + e%4, so a lane's four
+  // consecutive outputs of group e/4 leave in one 8-byte store (a quarter of the store
+  // instructions; the fp32 epilogues keep the row-contiguous form, whose stores fill
+  // whole 128-byte lines).
   const int pn = g.N - g.n0;
   const bool full = rows >= BMT;
   auto each = [&](auto&& st) __attribute__((always_inline)) {
@@ -373,10 +384,18 @@ __global__ __launch_bounds__(256, 1) void gemm_q8_big_kernel(GemmArgs g) {
   };
   if constexpr (MODE == GM_SWIGLU) {
     if (col_ok0) {
-      _Float16* ob = reinterpret_cast<_Float16*>(g.out) + (m0 + 4 * h) * (int64_t)g.ldo + (n_wave >> 1) + l32;
-      each([&](int mi, int e, int rc) {
-        ob[(int64_t)rc * g.ldo] = f16_sat(silu(acc[mi][0][e]) * acc[mi][1][e]);
-      });
+      _Float16* ob = reinterpret_cast<_Float16*>(g.out) + (m0 + l32) * (int64_t)g.ldo + (n_wave >> 1) + 4 * h;
+#pragma unroll
+      for (int mi = 0; mi < 8; ++mi)
+        if (full || mi * 32 + l32 < rows) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f16x4 v;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = f16_sat(silu(acc[mi][0][4 * q + c]) * acc[mi][1][4 * q + c]);
+            *reinterpret_cast<f16x4*>(ob + (int64_t)(mi * 32) * g.ldo + 8 * q) = v;
+          }
+        }
     }
   } else if constexpr (MODE == GM_PARTIAL) {
     float* pb = g.partial + ((int64_t)split * g.M + m0 + 4 * h) * pn + (n_wave - g.n0) + l32;
