@@ -962,14 +962,14 @@ __global__ __launch_bounds__(LMW * 64) void last_logits_stream_kernel(const floa
   uint8_t* slot = reinterpret_cast<uint8_t*>(sy + d) + wave * LL_SEGBYTES;
   const int nb = d / QK, nseg = (nb + LL_SEGB - 1) / LL_SEGB;
   const int64_t row_bytes = (int64_t)nb * 34;
-  const int64_t v0 = (int64_t)blockIdx.x * LMW + wave, vstep = (int64_t)gridDim.x * LMW;
-  const int64_t items = v0 < vocab ? ((vocab - 1 - v0) / vstep + 1) * nseg : 0;
+  // Items are (row, segment) pairs, segments fastest, walked incrementally: row v0, then
+  // every vstep-th row.  (Deriving the pair from a flat 64-bit item index took a 64-bit
+  // division per item, more scalar work than the item's own.)
+  const int v0 = blockIdx.x * LMW + wave, vstep = gridDim.x * LMW;
   auto seg_blocks = [&](int sg) { return min(LL_SEGB, nb - sg * LL_SEGB); };
-  auto load = [&](int64_t it, uint4 (&r)[LL_CHL]) {
-    const int64_t v = v0 + (it / nseg) * vstep;
-    const int sg = (int)(it % nseg);
+  auto load = [&](int v, int sg, uint4 (&r)[LL_CHL]) {
     const int nc = seg_blocks(sg) * 34 / 16;
-    const uint4* src = reinterpret_cast<const uint4*>(head + v * row_bytes + (int64_t)sg * LL_SEGBYTES);
+    const uint4* src = reinterpret_cast<const uint4*>(head + (int64_t)v * row_bytes + (int64_t)sg * LL_SEGBYTES);
 #pragma unroll
     for (int c = 0; c < LL_CHL; ++c) {
       const int ch = lane + 64 * c;
@@ -977,11 +977,12 @@ __global__ __launch_bounds__(LMW * 64) void last_logits_stream_kernel(const floa
     }
   };
   uint4 cur[LL_CHL], nxt[LL_CHL];
-  if (items > 0) load(0, cur);
+  if (v0 < vocab) load(v0, 0, cur);
   float part = 0.0f;
-  for (int64_t it = 0; it < items; ++it) {
-    if (it + 1 < items) load(it + 1, nxt);
-    const int sg = (int)(it % nseg);
+  for (int v = v0, sg = 0; v < vocab;) {
+    const int nsg = sg + 1 < nseg ? sg + 1 : 0;
+    const int nv = sg + 1 < nseg ? v : (v < vocab - vstep ? v + vstep : vocab);   // no int overflow
+    if (nv < vocab) load(nv, nsg, nxt);
     const int nbs = seg_blocks(sg), nc = nbs * 34 / 16;
     // The slot belongs to this wave alone, and a wave's LDS operations take effect in
     // program order: the reads below see these writes, and the next item's writes come
@@ -1024,11 +1025,13 @@ __global__ __launch_bounds__(LMW * 64) void last_logits_stream_kernel(const floa
     if (sg == nseg - 1) {
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
-      if (lane == 0) logits[v0 + (it / nseg) * vstep] = part;
+      if (lane == 0) logits[v] = part;
       part = 0.0f;
     }
 #pragma unroll
     for (int c = 0; c < LL_CHL; ++c) cur[c] = nxt[c];
+    v = nv;
+    sg = nsg;
   }
 }
 
