@@ -3,6 +3,8 @@
 // unpermute.  Every kernel that decides stored bytes or integers (q8_0 codes, cache rows,
 // expert indices) uses one float32 rounding per operation (explicit _rn intrinsics; the
 // library is also built without floating-point contraction).
+#include <mutex>
+
 #include "cp_internal.h"
 #include "k_common.h"
 
@@ -1035,21 +1037,155 @@ __global__ __launch_bounds__(LMW * 64) void last_logits_stream_kernel(const floa
   }
 }
 
+// Row-pair form for heads whose two rows fit a wave's LDS slot (d % 256 == 0, d <= 5120):
+// an item is two consecutive rows (contiguous bytes, whole 16-byte chunks), so a wave's
+// lanes run over 2*d/32 blocks with none idle at the row's end, and the per-item work
+// (loads, staging, the cross-lane sums) is shared by two rows.  y is staged with a
+// 36-float stride per block: 16 lanes on consecutive blocks reading 16 bytes each then
+// hit 16 distinct 4-bank groups, and the eight reads of a block take immediate offsets.
+constexpr int LLP_CH = 11;                                // 16-byte chunks per lane per item
+constexpr int LLP_SLOT = LLP_CH * 64 * 16;                // 11,264 bytes: two rows at d = 5120
+constexpr int LLP_YS = 36;                                // floats per staged y block
+
+__global__ __launch_bounds__(LMW * 64) void last_logits_pair_kernel(const float* __restrict__ x,
+                                                                    const float* __restrict__ gamma,
+                                                                    const uint8_t* __restrict__ head,
+                                                                    int32_t vocab, int32_t d, float eps,
+                                                                    float* __restrict__ logits) {
+  extern __shared__ float sy[];                   // y (nb blocks of LLP_YS floats), then LMW slots
+  __shared__ float red[LMW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float ss = 0.0f;
+  for (int i = tid; i < d; i += LMW * 64) ss += x[i] * x[i];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < LMW; ++w) tot += red[w];
+  const float scale = 1.0f / sqrtf(tot / (float)d + eps);
+  for (int i = tid; i < d; i += LMW * 64) sy[(i / QK) * LLP_YS + i % QK] = x[i] * scale * gamma[i];
+  __syncthreads();
+
+  const int nb = d / QK;
+  uint8_t* slot = reinterpret_cast<uint8_t*>(sy + nb * LLP_YS) + wave * LLP_SLOT;
+  const int row_bytes = nb * 34;
+  const int npair = (vocab + 1) / 2;
+  const int p0 = blockIdx.x * LMW + wave, pstep = gridDim.x * LMW;
+  auto load = [&](int p, uint4 (&r)[LLP_CH]) {
+    const int nc = min(2, vocab - 2 * p) * row_bytes / 16;
+    const uint4* src = reinterpret_cast<const uint4*>(head + (int64_t)(2 * p) * row_bytes);
+#pragma unroll
+    for (int c = 0; c < LLP_CH; ++c) {
+      const int ch = lane + 64 * c;
+      r[c] = ch < nc ? src[ch] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 cur[LLP_CH], nxt[LLP_CH];
+  if (p0 < npair) load(p0, cur);
+  for (int p = p0; p < npair;) {
+    const int np = p < npair - pstep ? p + pstep : npair;   // no int overflow
+    if (np < npair) load(np, nxt);
+    const int rows = min(2, vocab - 2 * p);
+    const int nc = rows * row_bytes / 16;
+    // The slot belongs to this wave alone, and a wave's LDS operations take effect in
+    // program order: the reads below see these writes, and the next item's writes come
+    // after these reads.
+#pragma unroll
+    for (int c = 0; c < LLP_CH; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nc) reinterpret_cast<uint4*>(slot)[ch] = cur[c];
+    }
+    __builtin_amdgcn_wave_barrier();
+    float part0 = 0.0f, part1 = 0.0f;
+    for (int b = lane; b < rows * nb; b += 64) {
+      // block b of the item starts at byte 34b (0 or 2 past a word boundary); nine aligned
+      // words and byte shifts give its 34 bytes
+      const int a = (34 * b) >> 2, r = (34 * b) & 3;
+      const uint32_t* sw = reinterpret_cast<const uint32_t*>(slot) + a;
+      uint32_t u[9];
+#pragma unroll
+      for (int i = 0; i < 9; ++i) u[i] = sw[i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) u[i] = __builtin_amdgcn_alignbyte(u[i + 1], u[i], r);
+      u[8] = __builtin_amdgcn_alignbyte(0u, u[8], r);
+      const float db = half_bits_to_float(u[0] & 0xFFFFu);
+      const bool second = b >= nb;
+      const int blk = second ? b - nb : b;
+      const float4* ys = reinterpret_cast<const float4*>(sy + blk * LLP_YS);
+      float q = 0.0f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const float4 yv = ys[g];
+        const float yy[4] = {yv.x, yv.y, yv.z, yv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 4 * g + e, byte = j + 2;        // q_j is byte j + 2 of the block
+          const int qv = __builtin_amdgcn_sbfe((int)u[byte >> 2], 8 * (byte & 3), 8);
+          q = fmaf((float)qv, yy[e], q);
+        }
+      }
+      if (second) part1 = fmaf(db, q, part1);
+      else part0 = fmaf(db, q, part0);
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      part0 += __shfl_xor(part0, o, 64);
+      part1 += __shfl_xor(part1, o, 64);
+    }
+    if (lane == 0) {
+      logits[2 * p] = part0;
+      if (rows == 2) logits[2 * p + 1] = part1;
+    }
+#pragma unroll
+    for (int c = 0; c < LLP_CH; ++c) cur[c] = nxt[c];
+    p = np;
+  }
+}
+
+// The largest dynamic LDS each last-logits kernel has been allowed on each device: the
+// attribute is set only when a launch needs more (a call per launch costs host time of the
+// order of the kernel's own).
+hipError_t allow_dyn_lds(const void* fn, int which, size_t bytes) {
+  static std::mutex mu;
+  static size_t allowed[3][64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  std::lock_guard<std::mutex> lk(mu);
+  if (allowed[which][dev] >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) allowed[which][dev] = bytes;
+  return e;
+}
+
 hipError_t launch_last_logits(const float* x, const float* gamma, const void* head, int32_t vocab,
                               int32_t d, float eps, float* logits, hipStream_t s) {
+  if (d % 256 == 0 && (uintptr_t)head % 16 == 0 && 2 * (d / QK) * 34 <= LLP_SLOT) {
+    // two workgroups per CU (the LDS allows two) that stay resident and walk every
+    // 2048th row pair: fewer, longer-lived waves streamed faster than more of them
+    const unsigned pgrid = (unsigned)std::min<int64_t>(ceil_div(ceil_div(vocab, 2), LMW), 512);
+    const size_t lds = (size_t)(d / QK) * LLP_YS * sizeof(float) + (size_t)LMW * LLP_SLOT;
+    hipError_t e = allow_dyn_lds((const void*)last_logits_pair_kernel, 0, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(last_logits_pair_kernel, dim3(pgrid), dim3(LMW * 64), lds, s, x, gamma,
+                       (const uint8_t*)head, vocab, d, eps, logits);
+    return hipGetLastError();
+  }
   const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(vocab, LMW), 2048);
   if (d % 256 == 0 && (uintptr_t)head % 16 == 0) {
     const size_t lds = (size_t)d * sizeof(float) + (size_t)LMW * LL_SEGBYTES;
-    hipError_t e = hipFuncSetAttribute((const void*)last_logits_stream_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = allow_dyn_lds((const void*)last_logits_stream_kernel, 1, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(last_logits_stream_kernel, dim3(grid), dim3(LMW * 64), lds, s, x, gamma,
                        (const uint8_t*)head, vocab, d, eps, logits);
     return hipGetLastError();
   }
   const size_t lds = (size_t)(d + d / QK) * sizeof(float);
-  hipError_t e = hipFuncSetAttribute((const void*)last_logits_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = allow_dyn_lds((const void*)last_logits_kernel, 2, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(last_logits_kernel, dim3(grid), dim3(LMW * 64), lds, s,
                      x, gamma, (const uint8_t*)head, vocab, d, eps, logits);

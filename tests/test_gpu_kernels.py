@@ -381,11 +381,13 @@ def test_router_bit_exact(torch, cpa, n, d, E, k):
 
 
 # --------------------------------------------------------------------------- last logits
-# d % 256 == 0 with an aligned head takes the streaming kernel (one partial segment, one
-# and a half, four and eight segments of 128 blocks); d = 2080 and a head at an odd
-# halfword offset take the per-block kernel.
-@pytest.mark.parametrize("vocab,d,offset", [(4096, 5120, 0), (1000, 256, 0), (33, 2048, 0), (77, 2080, 0),
-                                            (129, 16384, 0), (40, 32768, 0), (300, 5120, 2)])
+# d % 256 == 0 with an aligned head: up to d = 5120 the row-pair kernel (an odd vocabulary
+# ends on a single row), above it the streaming kernel (one and a half, four and eight
+# segments of 128 blocks); d = 2080 and a head at an odd halfword offset take the
+# per-block kernel.
+@pytest.mark.parametrize("vocab,d,offset", [(4096, 5120, 0), (1000, 256, 0), (33, 2048, 0), (4097, 5120, 0),
+                                            (77, 2080, 0), (65, 6144, 0), (129, 16384, 0), (40, 32768, 0),
+                                            (300, 5120, 2)])
 def test_last_logits_matches_oracle(torch, cpa, vocab, d, offset):
     """RMSNorm + q8_0 LM head on one row: float32 accumulation against the float64
     definition, to 1e-4 of the largest logit."""
