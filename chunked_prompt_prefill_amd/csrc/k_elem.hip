@@ -545,12 +545,15 @@ __device__ __forceinline__ float router_block_dot(const float* qf, const float4*
   return P;
 }
 
-__device__ __forceinline__ void router_block_weights(const int8_t* rq_blk, float* qf) {
-  const uint4* qp = reinterpret_cast<const uint4*>(rq_blk);
-  const uint4 qa = qp[0], qb = qp[1];
+__device__ __forceinline__ void router_raw_weights(uint4 qa, uint4 qb, float* qf) {
   const uint32_t w[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
 #pragma unroll
   for (int j = 0; j < QK; ++j) qf[j] = (float)(int8_t)((w[j >> 2] >> (8 * (j & 3))) & 0xFF);
+}
+
+__device__ __forceinline__ void router_block_weights(const int8_t* rq_blk, float* qf) {
+  const uint4* qp = reinterpret_cast<const uint4*>(rq_blk);
+  router_raw_weights(qp[0], qp[1], qf);
 }
 
 // Router logits in the fixed float32 order (per block: products and sums ascending,
@@ -559,7 +562,10 @@ __device__ __forceinline__ void router_block_weights(const int8_t* rq_blk, float
 // of the workgroup's 8 tokens, otherwise one group of 256 takes 4 (small workgroups: many
 // of them in flight, since each thread's sums are serial chains).  Each thread converts a
 // block's 32 weights to float once and applies them to its 4 tokens; y is staged 256
-// columns at a time and read from LDS as a broadcast.
+// columns at a time and read from LDS as a broadcast.  With few waves per SIMD nothing
+// hides a load's latency but the kernel's own prefetch: a thread's next q8_0 block is
+// loaded while the current one is applied, and the y columns of step s+1 are loaded into
+// registers during step s - 1 and stored into the other LDS buffer at the end of step s.
 constexpr int RT = 8;        // tokens per workgroup, at most
 constexpr int RTT = 4;       // tokens per thread
 __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ y,
@@ -569,7 +575,7 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ y
                                                      float* __restrict__ logits,
                                                      int32_t* __restrict__ idx,
                                                      float* __restrict__ wout) {
-  __shared__ float4 sy4[RT][64];
+  __shared__ float4 sy4[2][RT][64];
   __shared__ float slog[RT][256];
   const int tid = threadIdx.x;
   const int groups = E <= 128 ? 2 : 1;
@@ -577,36 +583,93 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ y
   const int e = tid % EP, grp = tid / EP;
   const int RTW = RTT * groups;
   const int t0 = blockIdx.x * RTW;
+  const int nb = d / QK;
+  const int nsteps = (d + 255) / 256;
+  const bool has_e = e < E;
+  const uint4* wrow = reinterpret_cast<const uint4*>(rq + (int64_t)(has_e ? e : 0) * d);
+  const uint16_t* drow = rd + (int64_t)(has_e ? e : 0) * nb;
+
+  // y of one 256-column step: RTW x 64 float4, at most two per thread
+  float4 yv[2];
+  auto load_y = [&](int c0) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int u = tid + 256 * r;
+      const int tt = u / 64, j4 = u % 64;
+      const int t = t0 + tt, col = c0 + 4 * j4;
+      yv[r] = (u < RTW * 64 && t < n && col < d)
+                  ? *reinterpret_cast<const float4*>(y + (int64_t)t * d + col)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store_y = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int u = tid + 256 * r;
+      if (u < RTW * 64) sy4[buf][u / 64][u % 64] = yv[r];
+    }
+  };
+  load_y(0);
+  store_y(0);
+  if (nsteps > 1) load_y(256);
+  uint4 qa = make_uint4(0, 0, 0, 0), qb = qa;
+  uint16_t dbits = 0;
+  if (has_e) { qa = wrow[0]; qb = wrow[1]; dbits = drow[0]; }
+  __syncthreads();
+
   float acc[RTT];
 #pragma unroll
   for (int tt = 0; tt < RTT; ++tt) acc[tt] = 0.0f;
-  for (int c0 = 0; c0 < d; c0 += 256) {
-    __syncthreads();
-    for (int u = tid; u < RTW * 64; u += 256) {
-      const int tt = u / 64, j4 = u % 64;
-      const int t = t0 + tt, col = c0 + 4 * j4;
-      sy4[tt][j4] = (t < n && col < d) ? *reinterpret_cast<const float4*>(y + (int64_t)t * d + col)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    __syncthreads();
-    if (e < E) {
-      for (int b = 0; b < 8; ++b) {
-        const int col = c0 + b * QK;
-        if (col >= d) break;
-        const int blk = col / QK;
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    if (has_e) {
+      const int blk0 = s * (256 / QK);
+      const int nbs = min(256 / QK, nb - blk0);
+      for (int b = 0; b < nbs; ++b) {
+        const int blk = blk0 + b;
         float qf[QK];
-        router_block_weights(rq + (int64_t)e * d + col, qf);
-        const float ds = half_bits_to_float(rd[(int64_t)e * (d / QK) + blk]);
+        router_raw_weights(qa, qb, qf);
+        const float ds = half_bits_to_float(dbits);
+        if (blk + 1 < nb) {
+          qa = wrow[2 * (blk + 1)];
+          qb = wrow[2 * (blk + 1) + 1];
+          dbits = drow[blk + 1];
+        }
+        // the RTT tokens' sums are independent chains: advance them together, one
+        // product and one add per token and weight, in the same per-token order
+        float P[RTT];
+#pragma unroll
+        for (int j4 = 0; j4 < QK / 4; ++j4) {
+          float4 yq[RTT];
+#pragma unroll
+          for (int tt = 0; tt < RTT; ++tt) yq[tt] = sy4[buf][grp * RTT + tt][b * (QK / 4) + j4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+#pragma unroll
+            for (int tt = 0; tt < RTT; ++tt) {
+              const float yc = c == 0 ? yq[tt].x : c == 1 ? yq[tt].y : c == 2 ? yq[tt].z : yq[tt].w;
+              const float prod = __fmul_rn(qf[4 * j4 + c], yc);
+              P[tt] = (j4 == 0 && c == 0) ? prod : __fadd_rn(P[tt], prod);
+            }
+          }
+        }
 #pragma unroll
         for (int tt = 0; tt < RTT; ++tt) {
-          const float term = __fmul_rn(ds, router_block_dot(qf, &sy4[grp * RTT + tt][b * (QK / 4)]));
+          const float term = __fmul_rn(ds, P[tt]);
           acc[tt] = (blk == 0) ? term : __fadd_rn(acc[tt], term);
         }
       }
     }
+    if (s + 1 < nsteps) {
+      // buffer buf ^ 1 was last read in step s - 1, which every thread finished before
+      // the barrier that opened step s
+      store_y(buf ^ 1);
+      if (s + 2 < nsteps) load_y((s + 2) * 256);
+      __syncthreads();
+    }
   }
   __syncthreads();
-  if (e < E) {
+  if (has_e) {
 #pragma unroll
     for (int tt = 0; tt < RTT; ++tt) {
       const int tw = grp * RTT + tt;
