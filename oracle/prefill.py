@@ -15,7 +15,9 @@ large prompts.
 
 Pinned by: chunked == layer-major, and equality across chunk sizes; the
 per-layer functions' own pins (see layer.py); the prefix property (outputs of
-a prefix do not change when tokens are appended).
+a prefix do not change when tokens are appended); closed-form stacks: with
+W_q = 0 and W_down = 0 every layer is the residual plus the causal prefix mean
+of the cached V rows through W_o, evaluated independently in numpy.
 """
 from __future__ import annotations
 
