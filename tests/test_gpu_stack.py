@@ -295,3 +295,22 @@ def test_last_position_logits_chunked_and_unchunked(torch):
         assert e < TOL
     for c in (1, 7, 512):
         assert rel_err(outs[c], outs[128]) < TOL
+
+
+@pytest.mark.parametrize("base", [GPU_DENSE, GPU_MOE])
+@pytest.mark.parametrize("chunk", [3, 37])
+def test_stack_with_zero_queries_matches_the_closed_form(torch, base, chunk):
+    """W_q = 0 and W_down = 0: every layer is the residual plus the causal prefix mean of
+    the cached V rows through W_o (see test_oracle_closed_form), a form evaluated here in
+    numpy, not by the oracle."""
+    from test_oracle_closed_form import closed_form, zero_q_and_down
+    w = base.with_(kv_type="f16")
+    log(f"closed-form stack {w.name} chunk={chunk}")
+    ql = zero_q_and_down(q8_layers(w))
+    x = synth.prompt_inputs(w)
+    out, ctx = run_prefill(torch, w, ql, x, chunk)[:2]
+    assert ctx.n_past == w.n_prompt
+    ref = closed_form(w, ql, x)
+    e = float(np.max(np.abs(out - ref)) / np.max(np.abs(ref - x)))
+    log(f"  max|d| / max|attention term| = {e:.3e}")
+    assert e < TOL
