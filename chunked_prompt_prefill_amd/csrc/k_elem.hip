@@ -896,7 +896,8 @@ hipError_t launch_moe_permute(const MoeBuffers& b, int32_t n, int32_t E, int32_t
 }
 
 // Unpermute: x_out[t] = x_res[t] + sum_{rank} w[t][rank] * y_perm[pos(t, rank)], summed in
-// rank order.  One thread per 4 columns of a token.
+// rank order.  One thread per 4 columns of a token; the rows of eight ranks are loaded
+// before any of them is added, so their loads are in flight together.
 __global__ __launch_bounds__(256) void moe_unpermute_kernel(const float* __restrict__ y_perm,
                                                             const int32_t* __restrict__ inv,
                                                             const float* __restrict__ w, int32_t n,
@@ -907,7 +908,21 @@ __global__ __launch_bounds__(256) void moe_unpermute_kernel(const float* __restr
   if (q >= (int64_t)n * quads) return;
   const int64_t t = q / quads, c = (q % quads) * 4;
   float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int r = 0; r < k; ++r) {
+  int r = 0;
+  for (; r + 8 <= k; r += 8) {
+    float wr[8];
+    float4 yv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      wr[j] = w[t * k + r + j];
+      yv[j] = *reinterpret_cast<const float4*>(y_perm + (int64_t)inv[t * k + r + j] * d + c);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      m.x += wr[j] * yv[j].x; m.y += wr[j] * yv[j].y; m.z += wr[j] * yv[j].z; m.w += wr[j] * yv[j].w;
+    }
+  }
+  for (; r < k; ++r) {
     const float wr = w[t * k + r];
     const float4 yv = *reinterpret_cast<const float4*>(y_perm + (int64_t)inv[t * k + r] * d + c);
     m.x += wr * yv.x; m.y += wr * yv.y; m.z += wr * yv.z; m.w += wr * yv.w;
